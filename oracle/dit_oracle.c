@@ -1,0 +1,301 @@
+/*
+ * dit_oracle.c -- plain fp64 CPU oracle for the fused non-GEMM operator chain
+ * of a video+audio DiT denoising block.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load or call this library.  It shares no
+ * code, header, table or helper with the HIP kernels, and the product path
+ * never links it.
+ *
+ * What is computed, and why this is the reference:
+ *   - The SGLang benchmark summary "8xH200 上的 MiniMax-H3: 无损加速 1.95 倍 ..."
+ *     (xhh.club), section Q&A (the question on which operations the fused
+ *     kernels cover), names the four fused operations: AdaLN modulation, gated
+ *     residual, SwiGLU activation, and per-head QK RMSNorm fused with 3D RoPE.
+ *   - "SGLang acelera video do MiniMax-H3 em ate 6,2x em GPUs H200"
+ *     (stamatios.com), section "Resultado principal", states that the fused
+ *     kernels cut memory traffic, intermediates and launches while leaving the
+ *     arithmetic unchanged, and that video and audio tokens share one packed
+ *     DiT stack.
+ *   So each function below is the plain, unfused definition of its operation,
+ *   evaluated in double precision with no blocking or reordering.  Inputs are
+ *   raw bf16 bit patterns (decoded exactly to double); outputs are unrounded
+ *   doubles.  Formulas the pages only name are the standard definitions of
+ *   those operations; every reading taken where the pages are silent is listed
+ *   in the project's design notes and repeated at the function it affects.
+ *
+ * Reductions are the textbook two-pass mean-then-variance in serial order.
+ * Build with a plain C compiler, -O2, no -ffast-math, -ffp-contract=off.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORACLE_OK 0
+#define ORACLE_BAD_ARG (-1)
+
+/* bf16 is the upper half of an IEEE binary32; widening is exact. */
+static double bf16_to_double(uint16_t bits)
+{
+    uint32_t word = (uint32_t)bits << 16;
+    float f;
+    memcpy(&f, &word, sizeof f);
+    return (double)f;
+}
+
+/* Exported so tests can check the decoding against known bit patterns. */
+double dit_oracle_bf16_decode(uint16_t bits) { return bf16_to_double(bits); }
+
+/*
+ * Packed token positions.
+ * Cited: "SGLang acelera video do MiniMax-H3 ..." (stamatios.com), section
+ * "Resultado principal": video and audio tokens run through one packed DiT
+ * stack.  "3D RoPE" in the xhh.club Q&A means each video token carries its
+ * (t, h, w) latent-grid coordinate.
+ * Readings: the video grid is enumerated in row-major (t, h, w) order with
+ * integer coordinates from 0; the n_extra tokens appended after it carry a
+ * temporal-only coordinate equal to their own index a = 0 .. n_extra-1, with
+ * h = w = 0.
+ * pos is [T*Hg*Wg + n_extra][3] int32.  Returns the token count written.
+ */
+int64_t dit_oracle_packed_positions(int32_t *pos, int64_t T, int64_t Hg,
+                                    int64_t Wg, int64_t n_extra)
+{
+    if (!pos || T < 0 || Hg < 0 || Wg < 0 || n_extra < 0)
+        return ORACLE_BAD_ARG;
+    int64_t n = 0;
+    for (int64_t t = 0; t < T; ++t)
+        for (int64_t h = 0; h < Hg; ++h)
+            for (int64_t w = 0; w < Wg; ++w) {
+                pos[3 * n + 0] = (int32_t)t;
+                pos[3 * n + 1] = (int32_t)h;
+                pos[3 * n + 2] = (int32_t)w;
+                ++n;
+            }
+    for (int64_t a = 0; a < n_extra; ++a) {
+        pos[3 * n + 0] = (int32_t)a;
+        pos[3 * n + 1] = 0;
+        pos[3 * n + 2] = 0;
+        ++n;
+    }
+    return n;
+}
+
+/*
+ * AdaLN modulation.
+ * Cited: xhh.club Q&A (fused-kernel answer) names "AdaLN modulation".
+ * Definition: LayerNorm over the hidden dimension with no affine parameters,
+ * then y = LN(x) * (1 + scale) + shift.
+ * Readings: biased variance (divide by D); eps added to the variance inside
+ * the square root; shift/scale are per sample, [B][D], broadcast over all N
+ * tokens of that sample (extra tokens included).
+ * x, y: [B][N][D]; shift, scale: [B][D].
+ */
+int dit_oracle_adaln_modulate(const uint16_t *x, const uint16_t *shift,
+                              const uint16_t *scale, double *y, int64_t B,
+                              int64_t N, int64_t D, double eps)
+{
+    if (!x || !shift || !scale || !y || B < 0 || N < 0 || D <= 0 || !(eps > 0))
+        return ORACLE_BAD_ARG;
+    for (int64_t b = 0; b < B; ++b) {
+        const uint16_t *sh = shift + b * D;
+        const uint16_t *sc = scale + b * D;
+        for (int64_t n = 0; n < N; ++n) {
+            const uint16_t *xr = x + (b * N + n) * D;
+            double *yr = y + (b * N + n) * D;
+
+            double sum = 0.0;
+            for (int64_t i = 0; i < D; ++i)
+                sum += bf16_to_double(xr[i]);
+            double mean = sum / (double)D;
+
+            double sq = 0.0;
+            for (int64_t i = 0; i < D; ++i) {
+                double d = bf16_to_double(xr[i]) - mean;
+                sq += d * d;
+            }
+            double var = sq / (double)D;
+            double denom = sqrt(var + eps);
+
+            for (int64_t i = 0; i < D; ++i) {
+                double ln = (bf16_to_double(xr[i]) - mean) / denom;
+                yr[i] = ln * (1.0 + bf16_to_double(sc[i])) + bf16_to_double(sh[i]);
+            }
+        }
+    }
+    return ORACLE_OK;
+}
+
+/*
+ * Gated residual.
+ * Cited: xhh.club Q&A (fused-kernel answer) names the gated residual.
+ * Definition: out = x + gate * y, elementwise, with gate per sample [B][D]
+ * broadcast over the N tokens.  Reading: the gate is used raw (no sigmoid or
+ * tanh).
+ * x, y, out: [B][N][D]; gate: [B][D].
+ */
+int dit_oracle_gated_residual(const uint16_t *x, const uint16_t *y,
+                              const uint16_t *gate, double *out, int64_t B,
+                              int64_t N, int64_t D)
+{
+    if (!x || !y || !gate || !out || B < 0 || N < 0 || D <= 0)
+        return ORACLE_BAD_ARG;
+    for (int64_t b = 0; b < B; ++b) {
+        const uint16_t *g = gate + b * D;
+        for (int64_t n = 0; n < N; ++n) {
+            int64_t base = (b * N + n) * D;
+            for (int64_t i = 0; i < D; ++i)
+                out[base + i] = bf16_to_double(x[base + i]) +
+                                bf16_to_double(g[i]) * bf16_to_double(y[base + i]);
+        }
+    }
+    return ORACLE_OK;
+}
+
+/* Logistic function 1/(1+e^-a), evaluated without overflow for either sign. */
+static double logistic(double a)
+{
+    if (a >= 0.0)
+        return 1.0 / (1.0 + exp(-a));
+    double e = exp(a);
+    return e / (1.0 + e);
+}
+
+/*
+ * SwiGLU activation.
+ * Cited: xhh.club Q&A (fused-kernel answer) and stamatios.com "De onde vem
+ * os ganhos" both list SwiGLU among the fused kernels.
+ * Definition: out = silu(a) * b with silu(a) = a * logistic(a) (beta = 1).
+ * Reading: each input row of width 2F is two contiguous halves [a | b]; the
+ * first half is the one passed through silu.
+ * in: [M][2F]; out: [M][F].
+ */
+int dit_oracle_swiglu(const uint16_t *in, double *out, int64_t M, int64_t F)
+{
+    if (!in || !out || M < 0 || F <= 0)
+        return ORACLE_BAD_ARG;
+    for (int64_t r = 0; r < M; ++r) {
+        const uint16_t *a = in + r * 2 * F;
+        const uint16_t *bh = a + F;
+        for (int64_t j = 0; j < F; ++j) {
+            double av = bf16_to_double(a[j]);
+            out[r * F + j] = av * logistic(av) * bf16_to_double(bh[j]);
+        }
+    }
+    return ORACLE_OK;
+}
+
+/*
+ * RMSNorm of one head vector: u = v / sqrt(mean(v^2) + eps) * w.
+ * Cited: xhh.club Q&A names "QK RMSNorm" (per head, fused with 3D RoPE).
+ * Reading: the mean runs over the head's Dh channels; w is a [Dh] weight.
+ */
+int dit_oracle_rmsnorm(const double *v, const double *w, double *u, int64_t n,
+                       double eps)
+{
+    if (!v || !w || !u || n <= 0 || !(eps > 0))
+        return ORACLE_BAD_ARG;
+    double sq = 0.0;
+    for (int64_t i = 0; i < n; ++i)
+        sq += v[i] * v[i];
+    double denom = sqrt(sq / (double)n + eps);
+    for (int64_t i = 0; i < n; ++i)
+        u[i] = v[i] / denom * w[i];
+    return ORACLE_OK;
+}
+
+/*
+ * 3D rotary embedding of one head vector, in place.
+ * Cited: xhh.club Q&A ("QK RMSNorm fused with 3D RoPE").
+ * Readings: the Dh channels are three contiguous bands in the order t, h, w
+ * with widths d_t, d_h, d_w (each even, summing to Dh).  Inside a band of
+ * width d driven by integer coordinate p, the channel pair (2j, 2j+1),
+ * j = 0 .. d/2-1, is rotated by the angle p * theta^(-2j/d) (exponent
+ * normalised by the band's own width), counter-clockwise:
+ *   (u0, u1) -> (u0 cos f - u1 sin f, u0 sin f + u1 cos f).
+ */
+int dit_oracle_rope3d(double *u, int64_t Dh, int32_t d_t, int32_t d_h,
+                      int32_t d_w, int32_t p_t, int32_t p_h, int32_t p_w,
+                      double theta)
+{
+    if (!u || d_t < 0 || d_h < 0 || d_w < 0 || (d_t | d_h | d_w) & 1 ||
+        (int64_t)d_t + d_h + d_w != Dh || !(theta > 0))
+        return ORACLE_BAD_ARG;
+    const int32_t width[3] = {d_t, d_h, d_w};
+    const int32_t coord[3] = {p_t, p_h, p_w};
+    int64_t start = 0;
+    for (int band = 0; band < 3; ++band) {
+        int32_t d = width[band];
+        for (int32_t j = 0; j < d / 2; ++j) {
+            double angle = (double)coord[band] * pow(theta, -2.0 * j / (double)d);
+            double c = cos(angle), s = sin(angle);
+            double u0 = u[start + 2 * j], u1 = u[start + 2 * j + 1];
+            u[start + 2 * j] = u0 * c - u1 * s;
+            u[start + 2 * j + 1] = u0 * s + u1 * c;
+        }
+        start += d;
+    }
+    return ORACLE_OK;
+}
+
+/*
+ * QK RMSNorm followed by 3D RoPE, for every (sample, token, head) of q and of
+ * k separately (q uses wq, k uses wk).  Order: normalise, multiply by the
+ * weight, rotate.
+ * q, k, q_out, k_out: [B][N][H][Dh]; wq, wk: [Dh]; pos: [N][3] shared by all
+ * samples of the batch.
+ */
+int dit_oracle_qk_rmsnorm_rope3d(const uint16_t *q, const uint16_t *k,
+                                 const uint16_t *wq, const uint16_t *wk,
+                                 const int32_t *pos, double *q_out,
+                                 double *k_out, int64_t B, int64_t N, int64_t H,
+                                 int64_t Dh, int32_t d_t, int32_t d_h,
+                                 int32_t d_w, double theta, double eps)
+{
+    if (!q || !k || !wq || !wk || !pos || !q_out || !k_out || B < 0 || N < 0 ||
+        H <= 0 || Dh <= 0 || !(eps > 0) || !(theta > 0))
+        return ORACLE_BAD_ARG;
+    if ((d_t | d_h | d_w) & 1 || d_t < 0 || d_h < 0 || d_w < 0 ||
+        (int64_t)d_t + d_h + d_w != Dh)
+        return ORACLE_BAD_ARG;
+
+    double *w_q = malloc(sizeof(double) * (size_t)Dh);
+    double *w_k = malloc(sizeof(double) * (size_t)Dh);
+    double *v = malloc(sizeof(double) * (size_t)Dh);
+    double *u = malloc(sizeof(double) * (size_t)Dh);
+    if (!w_q || !w_k || !v || !u) {
+        free(w_q); free(w_k); free(v); free(u);
+        return ORACLE_BAD_ARG;
+    }
+    for (int64_t i = 0; i < Dh; ++i) {
+        w_q[i] = bf16_to_double(wq[i]);
+        w_k[i] = bf16_to_double(wk[i]);
+    }
+
+    int status = ORACLE_OK;
+    for (int64_t b = 0; b < B && status == ORACLE_OK; ++b)
+        for (int64_t n = 0; n < N && status == ORACLE_OK; ++n) {
+            const int32_t *p = pos + 3 * n;
+            for (int64_t h = 0; h < H && status == ORACLE_OK; ++h) {
+                int64_t base = ((b * N + n) * H + h) * Dh;
+                for (int which = 0; which < 2; ++which) {
+                    const uint16_t *src = which == 0 ? q : k;
+                    double *dst = which == 0 ? q_out : k_out;
+                    const double *w = which == 0 ? w_q : w_k;
+                    for (int64_t i = 0; i < Dh; ++i)
+                        v[i] = bf16_to_double(src[base + i]);
+                    status = dit_oracle_rmsnorm(v, w, u, Dh, eps);
+                    if (status == ORACLE_OK)
+                        status = dit_oracle_rope3d(u, Dh, d_t, d_h, d_w, p[0],
+                                                   p[1], p[2], theta);
+                    if (status != ORACLE_OK)
+                        break;
+                    for (int64_t i = 0; i < Dh; ++i)
+                        dst[base + i] = u[i];
+                }
+            }
+        }
+    free(w_q); free(w_k); free(v); free(u);
+    return status;
+}

@@ -1,0 +1,94 @@
+"""Planted-mistake check of the oracle's pins (CPU only).
+
+Each case below copies oracle/dit_oracle.c, plants one plausible mistake by a
+textual edit (a dropped term, a wrong sign or index, a swapped operand, a wrong
+normalisation), builds the copy with the same compiler flags into a temporary
+directory, and runs every pin of tests/test_oracle_pins.py against it.  The
+case passes when at least one pin fails.  The real oracle is never modified.
+"""
+import os
+import subprocess
+
+import pytest
+
+import oracle
+import test_oracle_pins as pins
+
+MUTANTS = {
+    # AdaLN
+    "adaln_unbiased_variance": ("double var = sq / (double)D;", "double var = sq / (double)(D - 1);"),
+    "adaln_eps_outside_root": ("double denom = sqrt(var + eps);", "double denom = sqrt(var) + eps;"),
+    "adaln_scale_without_one": ("ln * (1.0 + bf16_to_double(sc[i]))", "ln * bf16_to_double(sc[i])"),
+    "adaln_shift_scale_swapped": ("const uint16_t *sh = shift + b * D;\n        const uint16_t *sc = scale + b * D;",
+                                  "const uint16_t *sh = scale + b * D;\n        const uint16_t *sc = shift + b * D;"),
+    "adaln_variance_not_centred": ("double d = bf16_to_double(xr[i]) - mean;", "double d = bf16_to_double(xr[i]);"),
+    "adaln_sample_zero_vectors": ("const uint16_t *sh = shift + b * D;", "const uint16_t *sh = shift;"),
+    "adaln_mean_not_subtracted": ("double ln = (bf16_to_double(xr[i]) - mean) / denom;",
+                                  "double ln = bf16_to_double(xr[i]) / denom;"),
+    # gated residual
+    "residual_gate_on_x": ("bf16_to_double(x[base + i]) +\n                                bf16_to_double(g[i]) * bf16_to_double(y[base + i]);",
+                           "bf16_to_double(g[i]) * bf16_to_double(x[base + i]) +\n                                bf16_to_double(y[base + i]);"),
+    "residual_gate_sample_zero": ("const uint16_t *g = gate + b * D;", "const uint16_t *g = gate;"),
+    "residual_minus": ("bf16_to_double(x[base + i]) +\n", "bf16_to_double(x[base + i]) -\n"),
+    # SwiGLU
+    "swiglu_halves_swapped": ("out[r * F + j] = av * logistic(av) * bf16_to_double(bh[j]);",
+                              "out[r * F + j] = bf16_to_double(bh[j]) * logistic(bf16_to_double(bh[j])) * av;"),
+    "swiglu_sigmoid_sign": ("return 1.0 / (1.0 + exp(-a));", "return 1.0 / (1.0 + exp(a));"),
+    "swiglu_drops_a_factor": ("out[r * F + j] = av * logistic(av) * bf16_to_double(bh[j]);",
+                              "out[r * F + j] = logistic(av) * bf16_to_double(bh[j]);"),
+    "swiglu_negative_branch": ("return e / (1.0 + e);", "return 1.0 / (1.0 + e);"),
+    "swiglu_second_half_offset": ("const uint16_t *bh = a + F;", "const uint16_t *bh = a + F - 1;"),
+    # RMSNorm
+    "rmsnorm_sum_not_mean": ("double denom = sqrt(sq / (double)n + eps);", "double denom = sqrt(sq + eps);"),
+    "rmsnorm_no_weight": ("u[i] = v[i] / denom * w[i];", "u[i] = v[i] / denom;"),
+    "rmsnorm_eps_outside_root": ("double denom = sqrt(sq / (double)n + eps);", "double denom = sqrt(sq / (double)n) + eps;"),
+    # RoPE
+    "rope_sin_sign": ("u[start + 2 * j] = u0 * c - u1 * s;", "u[start + 2 * j] = u0 * c + u1 * s;"),
+    "rope_exponent_over_dh": ("pow(theta, -2.0 * j / (double)d)", "pow(theta, -2.0 * j / (double)Dh)"),
+    "rope_exponent_j_not_2j": ("pow(theta, -2.0 * j / (double)d)", "pow(theta, -1.0 * j / (double)d)"),
+    "rope_t_h_swapped": ("const int32_t coord[3] = {p_t, p_h, p_w};", "const int32_t coord[3] = {p_h, p_t, p_w};"),
+    "rope_rotate_half_pairing": ("double u0 = u[start + 2 * j], u1 = u[start + 2 * j + 1];\n"
+                                 "            u[start + 2 * j] = u0 * c - u1 * s;\n"
+                                 "            u[start + 2 * j + 1] = u0 * s + u1 * c;",
+                                 "double u0 = u[start + j], u1 = u[start + j + d / 2];\n"
+                                 "            u[start + j] = u0 * c - u1 * s;\n"
+                                 "            u[start + j + d / 2] = u0 * s + u1 * c;"),
+    "rope_band_start_not_advanced": ("        start += d;\n    }\n    return ORACLE_OK;", "    }\n    return ORACLE_OK;"),
+    # QK composition
+    "qk_k_uses_wq": ("const double *w = which == 0 ? w_q : w_k;", "const double *w = w_q;"),
+    "qk_position_of_first_token": ("const int32_t *p = pos + 3 * n;", "const int32_t *p = pos;"),
+    "qk_rotate_before_norm_weight": ("status = dit_oracle_rmsnorm(v, w, u, Dh, eps);",
+                                     "status = dit_oracle_rmsnorm(v, w, u, Dh, eps);\n"
+                                     "                    for (int64_t i = 0; i < Dh; ++i) u[i] /= w[i];"),
+    # positions
+    "positions_h_w_swapped": ("pos[3 * n + 1] = (int32_t)h;\n                pos[3 * n + 2] = (int32_t)w;",
+                              "pos[3 * n + 1] = (int32_t)w;\n                pos[3 * n + 2] = (int32_t)h;"),
+    "positions_extra_at_zero": ("pos[3 * n + 0] = (int32_t)a;", "pos[3 * n + 0] = 0;"),
+    # bf16 decode
+    "decode_wrong_shift": ("uint32_t word = (uint32_t)bits << 16;", "uint32_t word = (uint32_t)bits << 15;"),
+}
+
+
+@pytest.fixture(scope="module")
+def source():
+    with open(oracle.SOURCE, encoding="utf-8") as fh:
+        return fh.read()
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_planted_mistake_is_caught(source, tmp_path, name):
+    old, new = MUTANTS[name]
+    assert source.count(old) == 1, f"mutation site for {name} not found exactly once"
+    src = tmp_path / f"{name}.c"
+    src.write_text(source.replace(old, new), encoding="utf-8")
+    lib_path = str(tmp_path / f"lib{name}.so")
+    subprocess.run(["gcc", *oracle.CFLAGS, "-o", lib_path, str(src), "-lm"], check=True)
+    lib = oracle.load(lib_path)
+    failed = []
+    for pin_name, pin in pins.PINS.items():
+        try:
+            pin(lib)
+        except Exception:  # any failure of a pin counts as catching the mistake
+            failed.append(pin_name)
+    assert failed, f"planted mistake {name} passed every pin"
+    os.remove(lib_path)
