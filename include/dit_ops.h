@@ -1,0 +1,181 @@
+/*
+ * dit_ops.h -- C ABI of the fused non-GEMM operator chain of a video+audio
+ * diffusion-transformer (DiT) denoising block, for AMD Instinct MI355X (gfx950).
+ *
+ * Where the operations come from:
+ *   "8×H200 上的 MiniMax-H3:无损加速 1.95 倍,SSIM 0.76–0.91 下最高 6.24 倍"
+ *   (xhh.club), section Q&A, the answer on which operations the fused kernels
+ *   optimise: AdaLN modulation, gated residual, SwiGLU activation, and QK
+ *   RMSNorm fused with 3D RoPE.
+ *   "SGLang acelera vídeo do MiniMax-H3 em até 6,2x em GPUs H200"
+ *   (stamatios.com), section "Resultado principal": the fused kernels remove
+ *   memory traffic, intermediate tensors and launches without changing the
+ *   arithmetic; video and audio tokens form one packed DiT sequence.
+ *   "Sol-H3: Recursive Self-Improvement for MiniMax-H3 Inference Acceleration
+ *   on Sol-Engine across Cloud and Edge", abstract: operator work is a search
+ *   over kernel fusions and memory layouts judged by latency together with
+ *   numerical agreement.
+ * The pages name these operations but print no formulas; each entry point
+ * states the standard definition it computes and the readings it takes.
+ *
+ * Conventions shared by every entry point:
+ *   - Tensors are bf16 (raw bit patterns, dit_bf16), row-major and contiguous,
+ *     last dimension unit-stride, batch-major [B][N][...].  Arithmetic is fp32
+ *     with a single round-to-nearest-even to bf16 at each output element.
+ *   - Every pointer is a DEVICE pointer on the current HIP device.  The caller
+ *     owns all buffers; the library allocates nothing, keeps no state between
+ *     calls, and never synchronises.  Work is enqueued on `stream` (a
+ *     hipStream_t cast to void*; NULL = the default stream) and completes
+ *     asynchronously, in stream order.
+ *   - Arguments are validated on the host BEFORE any HIP call or write; a
+ *     rejected call touches no memory and enqueues nothing:
+ *       DIT_ERR_NULL   a required pointer is NULL
+ *       DIT_ERR_SHAPE  a width is not a multiple of 8, exceeds a stated limit,
+ *                      or RoPE bands are odd or do not sum to the head width
+ *       DIT_ERR_ALIGN  a bf16 pointer is not 16-byte aligned (int32 pointers:
+ *                      4-byte)
+ *       DIT_ERR_ARG    a negative size, eps <= 0 or not finite, theta <= 1 or
+ *                      not finite, more than 2^24 - 1 rows (tokens) in one
+ *                      call, or outputs that overlap inputs in a way the entry
+ *                      point forbids
+ *       DIT_ERR_HIP    the kernel launch itself failed (hipGetLastError)
+ *     A call with zero rows is a no-op returning DIT_OK (its pointers are not
+ *     examined).  Faults inside a
+ *     kernel (for example a pointer that is not device memory) surface at the
+ *     caller's next synchronisation, as for any HIP work.  The library never
+ *     aborts and never prints.
+ */
+#ifndef DIT_OPS_H
+#define DIT_OPS_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef uint16_t dit_bf16; /* raw bfloat16 bits */
+
+typedef enum {
+    DIT_OK = 0,
+    DIT_ERR_NULL = 1,
+    DIT_ERR_SHAPE = 2,
+    DIT_ERR_ALIGN = 3,
+    DIT_ERR_ARG = 4,
+    DIT_ERR_HIP = 5
+} dit_status;
+
+#define DIT_ABI_VERSION 1
+
+/* Human-readable name of a status code; never NULL. */
+const char *dit_status_str(int status);
+
+/* DIT_ABI_VERSION of the built library. */
+int dit_abi_version(void);
+
+/*
+ * AdaLN modulation: y = LayerNorm(x) * (1 + scale[b]) + shift[b].
+ * Cited: xhh.club summary, Q&A (fused-kernel answer), "AdaLN modulation".
+ * LayerNorm runs over the D channels of each token with no affine parameters:
+ * mean, biased variance (divide by D), y_i = (x_i - mean) / sqrt(var + eps).
+ * shift and scale are per sample and apply to all N tokens of that sample.
+ *   x      [B][N][D]  input
+ *   shift  [B][D]
+ *   scale  [B][D]
+ *   y      [B][N][D]  output; y == x (in place) is allowed, any other overlap
+ *                     with x, shift or scale is rejected (DIT_ERR_ARG)
+ *   D      multiple of 8, 8 <= D <= 8192
+ *   eps    > 0 (1e-6 in the shipped workloads)
+ */
+dit_status dit_adaln_modulate(const dit_bf16 *x, const dit_bf16 *shift,
+                              const dit_bf16 *scale, dit_bf16 *y, int64_t B,
+                              int64_t N, int64_t D, float eps, void *stream);
+
+/*
+ * Gated residual: out = x + gate[b] * y.
+ * Cited: xhh.club summary, Q&A (fused-kernel answer), "gated residual".
+ * The gate is used as given (no sigmoid or tanh); it is per sample and
+ * applies to all N tokens of that sample.
+ *   x, y   [B][N][D]
+ *   gate   [B][D]
+ *   out    [B][N][D]; out == x or out == y (in place) is allowed, any other
+ *          overlap with an input is rejected (DIT_ERR_ARG)
+ *   D      multiple of 8, D >= 8
+ */
+dit_status dit_gated_residual(const dit_bf16 *x, const dit_bf16 *y,
+                              const dit_bf16 *gate, dit_bf16 *out, int64_t B,
+                              int64_t N, int64_t D, void *stream);
+
+/*
+ * SwiGLU activation: out[r][j] = silu(in[r][j]) * in[r][F + j],
+ * silu(a) = a / (1 + exp(-a)).
+ * Cited: xhh.club summary, Q&A (fused-kernel answer), and the stamatios.com
+ * summary, "De onde vêm os ganhos", both listing SwiGLU.
+ * Each input row is the two halves [a | b] of width F each, as an up
+ * projection of width 2F emits them; the first half is gated.
+ *   in     [M][2F]
+ *   out    [M][F]; must not overlap `in` (DIT_ERR_ARG)
+ *   F      multiple of 8, F >= 8
+ * Finite inputs give finite outputs: silu saturates to a for large a and to
+ * (-)0 for very negative a.
+ */
+dit_status dit_swiglu(const dit_bf16 *in, dit_bf16 *out, int64_t M, int64_t F,
+                      void *stream);
+
+/*
+ * Per-head QK RMSNorm fused with 3D rotary embedding, for q and k.
+ * Cited: xhh.club summary, Q&A (fused-kernel answer), "QK RMSNorm fused with
+ * 3D RoPE".
+ * For every sample b, token n and head h, separately for q (weight wq) and
+ * k (weight wk), over the Dh channels v of that head:
+ *   u_i = v_i / sqrt(mean(v^2) + eps) * w_i
+ * then the head's channels are split into three contiguous bands t, h, w of
+ * widths d_t, d_h, d_w; in a band of width d driven by the token's integer
+ * coordinate p (pos[n][0], pos[n][1] or pos[n][2]), the adjacent pair
+ * (2j, 2j+1), j < d/2, is rotated counter-clockwise by p * theta^(-2j/d):
+ *   (u0, u1) -> (u0 cos f - u1 sin f, u0 sin f + u1 cos f).
+ *   q, k          [B][N][H][Dh] inputs
+ *   q_out, k_out  [B][N][H][Dh] outputs; q_out == q and k_out == k are
+ *                 allowed, any other overlap is rejected (DIT_ERR_ARG)
+ *   wq, wk        [Dh] RMSNorm weights shared by all heads
+ *   pos           [N][3] int32 (t, h, w) coordinates, shared by all B samples;
+ *                 entries must lie in [0, 2^24) so they convert to fp32 exactly
+ *   Dh            one of 8, 16, 32, 64, 128, 256
+ *   d_t, d_h, d_w even, >= 0, d_t + d_h + d_w == Dh
+ *   theta > 1 (1e4 in the shipped workloads), eps > 0
+ */
+dit_status dit_qk_rmsnorm_rope3d(const dit_bf16 *q, const dit_bf16 *k,
+                                 dit_bf16 *q_out, dit_bf16 *k_out,
+                                 const dit_bf16 *wq, const dit_bf16 *wk,
+                                 const int32_t *pos, int64_t B, int64_t N,
+                                 int64_t H, int64_t Dh, int32_t d_t,
+                                 int32_t d_h, int32_t d_w, float theta,
+                                 float eps, void *stream);
+
+/*
+ * Packed token coordinates for the 3D rotary embedding.
+ * Cited: stamatios.com summary, "Resultado principal" (video and audio tokens
+ * in one packed DiT sequence); xhh.club Q&A ("3D RoPE").
+ * Writes pos[N][3] int32 for N = T*Hg*Wg + n_extra tokens: video token
+ * n < T*Hg*Wg gets its row-major latent-grid coordinate
+ * (n / (Hg*Wg), (n / Wg) % Hg, n % Wg); the n_extra tokens that follow get the
+ * temporal-only coordinate (a, 0, 0), a = 0 .. n_extra-1.
+ *   pos    [N][3] device buffer, 4-byte aligned
+ *   T, Hg, Wg, n_extra >= 0; N = T*Hg*Wg + n_extra at most 2^24 - 1
+ */
+dit_status dit_packed_positions(int32_t *pos, int64_t T, int64_t Hg, int64_t Wg,
+                                int64_t n_extra, void *stream);
+
+/*
+ * Plain 16-byte-vector device copy, dst = src, `bytes` a multiple of 16.
+ * Not an operator of the chain: it is the streaming-bandwidth ceiling the
+ * chain's kernels are measured against, and the known-size workload used to
+ * calibrate hardware byte counters.  src and dst must not overlap.
+ */
+dit_status dit_copy16(const void *src, void *dst, int64_t bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DIT_OPS_H */

@@ -1,0 +1,172 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+The library must load, export every entry point include/dit_ops.h declares,
+and reject invalid arguments with the documented status codes.  Every call
+here fails validation (or is a zero-row no-op), so no HIP call is made and no
+pointer is dereferenced; the pointers are fake aligned addresses.
+"""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import video_diffusion_transformer_dit_amd as dit
+from video_diffusion_transformer_dit_amd import (DIT_ERR_ALIGN, DIT_ERR_ARG, DIT_ERR_NULL, DIT_ERR_SHAPE, DIT_OK)
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dit_ops.h")
+
+P = 0x100000  # fake 16-byte-aligned device addresses, never dereferenced
+Q = 0x200000
+R = 0x300000
+S = 0x400000
+T = 0x500000
+U = 0x600000
+V = 0x700000
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(dit.LIB_PATH):
+        from video_diffusion_transformer_dit_amd import build
+
+        build.build()
+    return dit.load_library()
+
+
+def declared_functions():
+    with open(HEADER, encoding="utf-8") as fh:
+        text = fh.read()
+    return set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(dit_\w+)\s*\(", text, flags=re.M))
+
+
+def test_header_and_binding_agree():
+    names = declared_functions()
+    assert names == set(dit.SIGNATURES), names ^ set(dit.SIGNATURES)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
+
+
+def test_abi_version_matches_header(lib):
+    with open(HEADER, encoding="utf-8") as fh:
+        version = int(re.search(r"#define DIT_ABI_VERSION (\d+)", fh.read()).group(1))
+    assert dit.dit_abi_version() == version
+
+
+def test_status_strings(lib):
+    for code in range(6):
+        assert dit.dit_status_str(code).startswith(("DIT_OK", "DIT_ERR_"))
+    assert dit.dit_status_str(99) == "unknown dit_status"
+
+
+def adaln(lib, x=P, sh=Q, sc=R, y=S, B=1, N=4, D=4096, eps=1e-6):
+    return lib.dit_adaln_modulate(x, sh, sc, y, B, N, D, eps, None)
+
+
+def test_adaln_validation(lib):
+    assert adaln(lib, B=-1) == DIT_ERR_ARG
+    assert adaln(lib, B=1 << 40, N=1 << 40) == DIT_ERR_ARG
+    assert adaln(lib, N=(1 << 24) + 1) == DIT_ERR_ARG
+    assert adaln(lib, D=12) == DIT_ERR_SHAPE
+    assert adaln(lib, D=0) == DIT_ERR_SHAPE
+    assert adaln(lib, D=8200) == DIT_ERR_SHAPE
+    assert adaln(lib, eps=0.0) == DIT_ERR_ARG
+    assert adaln(lib, eps=math.nan) == DIT_ERR_ARG
+    assert adaln(lib, eps=math.inf) == DIT_ERR_ARG
+    assert adaln(lib, x=0) == DIT_ERR_NULL
+    assert adaln(lib, y=0) == DIT_ERR_NULL
+    assert adaln(lib, x=P + 2) == DIT_ERR_ALIGN
+    assert adaln(lib, sc=R + 8) == DIT_ERR_ALIGN
+    assert adaln(lib, y=P + 16) == DIT_ERR_ARG  # partial overlap with x
+    assert adaln(lib, y=Q) == DIT_ERR_ARG  # output over the shift vector
+    assert adaln(lib, x=0, sh=0, sc=0, y=0, N=0) == DIT_OK  # zero rows: no-op
+    assert adaln(lib, N=0, D=12) == DIT_ERR_SHAPE  # shapes still checked
+
+
+def test_gated_residual_validation(lib):
+    f = lib.dit_gated_residual
+    assert f(P, Q, R, S, 1, -3, 4096, None) == DIT_ERR_ARG
+    assert f(P, Q, R, S, 1, 3, 4100, None) == DIT_ERR_SHAPE
+    assert f(P, 0, R, S, 1, 3, 4096, None) == DIT_ERR_NULL
+    assert f(P, Q, R + 4, S, 1, 3, 4096, None) == DIT_ERR_ALIGN
+    assert f(P, Q, R, Q + 32, 1, 3, 4096, None) == DIT_ERR_ARG  # partial overlap with y
+    assert f(P, Q, R, R, 1, 3, 4096, None) == DIT_ERR_ARG  # output over the gate
+    assert f(0, 0, 0, 0, 0, 3, 4096, None) == DIT_OK
+
+
+def test_swiglu_validation(lib):
+    f = lib.dit_swiglu
+    assert f(P, Q, -1, 16384, None) == DIT_ERR_ARG
+    assert f(P, Q, (1 << 24) + 1, 16384, None) == DIT_ERR_ARG
+    assert f(P, Q, 4, 0, None) == DIT_ERR_SHAPE
+    assert f(P, Q, 4, 1001, None) == DIT_ERR_SHAPE
+    assert f(0, Q, 4, 16384, None) == DIT_ERR_NULL
+    assert f(P, Q + 2, 4, 16384, None) == DIT_ERR_ALIGN
+    assert f(P, P + 4 * 16384, 4, 16384, None) == DIT_ERR_ARG  # output inside the input
+    assert f(0, 0, 0, 16384, None) == DIT_OK
+
+
+def qk(lib, q=P, k=Q, qo=R, ko=S, wq=T, wk=U, pos=V, B=1, N=8, H=32, Dh=128, bands=(16, 56, 56),
+       theta=1e4, eps=1e-6):
+    return lib.dit_qk_rmsnorm_rope3d(q, k, qo, ko, wq, wk, pos, B, N, H, Dh, *bands, theta, eps, None)
+
+
+def test_qk_validation(lib):
+    assert qk(lib, N=-1) == DIT_ERR_ARG
+    assert qk(lib, Dh=96, bands=(32, 32, 32)) == DIT_ERR_SHAPE
+    assert qk(lib, Dh=512, bands=(128, 192, 192)) == DIT_ERR_SHAPE
+    assert qk(lib, H=0) == DIT_ERR_SHAPE
+    assert qk(lib, H=1024) == DIT_ERR_SHAPE  # H*Dh beyond 65536
+    assert qk(lib, bands=(15, 57, 56)) == DIT_ERR_SHAPE
+    assert qk(lib, bands=(16, 56, 58)) == DIT_ERR_SHAPE
+    assert qk(lib, bands=(-2, 74, 56)) == DIT_ERR_SHAPE
+    assert qk(lib, theta=1.0) == DIT_ERR_ARG
+    assert qk(lib, theta=math.inf) == DIT_ERR_ARG
+    assert qk(lib, eps=-1e-6) == DIT_ERR_ARG
+    assert qk(lib, pos=0) == DIT_ERR_NULL
+    assert qk(lib, wk=0) == DIT_ERR_NULL
+    assert qk(lib, pos=V + 2) == DIT_ERR_ALIGN
+    assert qk(lib, wq=T + 8) == DIT_ERR_ALIGN
+    assert qk(lib, qo=P + 64) == DIT_ERR_ARG  # partial overlap with q
+    assert qk(lib, qo=Q) == DIT_ERR_ARG  # q output over k
+    assert qk(lib, ko=R) == DIT_ERR_ARG  # both outputs in one buffer
+    assert qk(lib, ko=V) == DIT_ERR_ARG  # k output over the positions
+    assert qk(lib, q=0, k=0, qo=0, ko=0, wq=0, wk=0, pos=0, B=0) == DIT_OK
+
+
+def test_positions_validation(lib):
+    f = lib.dit_packed_positions
+    assert f(P, -1, 4, 4, 0, None) == DIT_ERR_ARG
+    assert f(P, 2, 4, 4, -1, None) == DIT_ERR_ARG
+    assert f(P, 1 << 12, 1 << 12, 2, 0, None) == DIT_ERR_ARG  # 2^25 tokens
+    assert f(P, 1 << 40, 1 << 40, 1 << 40, 0, None) == DIT_ERR_ARG  # overflow
+    assert f(0, 2, 4, 4, 0, None) == DIT_ERR_NULL
+    assert f(P + 2, 2, 4, 4, 0, None) == DIT_ERR_ALIGN
+    assert f(0, 0, 4, 4, 0, None) == DIT_OK
+
+
+def test_copy_validation(lib):
+    f = lib.dit_copy16
+    assert f(P, Q, -16, None) == DIT_ERR_ARG
+    assert f(P, Q, 17, None) == DIT_ERR_SHAPE
+    assert f(0, Q, 16, None) == DIT_ERR_NULL
+    assert f(P + 8, Q, 16, None) == DIT_ERR_ALIGN
+    assert f(P, P + 16, 64, None) == DIT_ERR_ARG
+    assert f(0, 0, 0, None) == DIT_OK
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+
+    x = torch.zeros((1, 2, 8), dtype=torch.bfloat16)
+    v = torch.zeros((1, 8), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        dit.dit_adaln_modulate(x, v, v)
+    with pytest.raises(TypeError):
+        dit.dit_adaln_modulate(x.float(), v, v)

@@ -1,0 +1,35 @@
+"""Fused non-GEMM operator chain of a video+audio DiT block, for MI355X (gfx950).
+
+The package is a thin Python face over ``libdit_ops.so``, a C-ABI library of
+hand-written HIP kernels (``csrc/``; declarations in ``include/dit_ops.h``):
+
+  dit_adaln_modulate      y = LayerNorm(x) * (1 + scale) + shift
+  dit_gated_residual      out = x + gate * y
+  dit_swiglu              out = silu(a) * b over [a | b] rows
+  dit_qk_rmsnorm_rope3d   per-head RMSNorm of q and k, then 3D (t, h, w) RoPE
+  dit_packed_positions    (t, h, w) coordinates of a packed token sequence
+  dit_copy16              plain 16-byte-vector copy (bandwidth ceiling)
+
+PyTorch supplies device memory and streams only.  Build the library with
+``python -m video_diffusion_transformer_dit_amd.build``.
+"""
+from ._binding import (  # noqa: F401
+    DIT_ERR_ALIGN,
+    DIT_ERR_ARG,
+    DIT_ERR_HIP,
+    DIT_ERR_NULL,
+    DIT_ERR_SHAPE,
+    DIT_OK,
+    LIB_PATH,
+    SIGNATURES,
+    DitError,
+    dit_abi_version,
+    dit_adaln_modulate,
+    dit_copy16,
+    dit_gated_residual,
+    dit_packed_positions,
+    dit_qk_rmsnorm_rope3d,
+    dit_status_str,
+    dit_swiglu,
+    load_library,
+)

@@ -1,0 +1,202 @@
+// abi.hip -- the library's C entry points (declared in include/dit_ops.h).
+//
+// Each entry point validates its arguments on the host, in a fixed order,
+// before any HIP call:
+//   1. sizes negative or beyond the limits     -> DIT_ERR_ARG
+//   2. widths, head size or RoPE bands invalid  -> DIT_ERR_SHAPE
+//   3. eps / theta out of range                 -> DIT_ERR_ARG
+//   4. zero rows                                -> DIT_OK (nothing enqueued;
+//                                                  pointers not examined)
+//   5. NULL pointers                            -> DIT_ERR_NULL
+//   6. misaligned pointers                      -> DIT_ERR_ALIGN
+//   7. forbidden overlaps                       -> DIT_ERR_ARG
+// and only then launches on the caller's stream; a failed launch returns
+// DIT_ERR_HIP.  Nothing is allocated, cached or synchronised.
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "dit_ops.h"
+#include "launch.hpp"
+
+namespace {
+
+// Largest row (token) count accepted by one call: below 2^24 rows every grid
+// dimension stays within the 32-bit work-item count of a dispatch (a
+// workgroup per row spans up to 256 work-items) and every row index fits in
+// 32 bits.
+constexpr int64_t kMaxRows = (int64_t(1) << 24) - 1;
+constexpr int64_t kMaxAdaLNWidth = 8192; // row held in registers: 128 fp32 per lane
+constexpr int64_t kMaxWidth = int64_t(1) << 24;
+constexpr int64_t kMaxHeadRow = 65536; // H * Dh
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// Byte ranges [a, a+na) and [b, b+nb) intersect.
+bool overlap(const void *a, int64_t na, const void *b, int64_t nb)
+{
+    const uintptr_t pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
+    return pa < pb + (uintptr_t)nb && pb < pa + (uintptr_t)na;
+}
+
+// Overlap that is not the exact in-place case (same start, same extent).
+bool bad_alias(const void *out, const void *in, int64_t n) { return out != in && overlap(out, n, in, n); }
+
+// rows = a * b without overflow, or -1 when either is negative or the product
+// exceeds kMaxRows.
+int64_t row_count(int64_t a, int64_t b)
+{
+    if (a < 0 || b < 0)
+        return -1;
+    if (a != 0 && b > kMaxRows / a)
+        return -1;
+    const int64_t r = a * b;
+    return r > kMaxRows ? -1 : r;
+}
+
+dit_status launched(hipError_t e) { return e == hipSuccess ? DIT_OK : DIT_ERR_HIP; }
+
+} // namespace
+
+extern "C" {
+
+const char *dit_status_str(int status)
+{
+    switch (status) {
+    case DIT_OK: return "DIT_OK";
+    case DIT_ERR_NULL: return "DIT_ERR_NULL: a required pointer is NULL";
+    case DIT_ERR_SHAPE: return "DIT_ERR_SHAPE: unsupported width, head size or RoPE bands";
+    case DIT_ERR_ALIGN: return "DIT_ERR_ALIGN: pointer not aligned (bf16 tensors need 16 bytes)";
+    case DIT_ERR_ARG: return "DIT_ERR_ARG: size, eps, theta or buffer overlap out of range";
+    case DIT_ERR_HIP: return "DIT_ERR_HIP: kernel launch failed";
+    default: return "unknown dit_status";
+    }
+}
+
+int dit_abi_version(void) { return DIT_ABI_VERSION; }
+
+dit_status dit_adaln_modulate(const dit_bf16 *x, const dit_bf16 *shift, const dit_bf16 *scale, dit_bf16 *y,
+                              int64_t B, int64_t N, int64_t D, float eps, void *stream)
+{
+    const int64_t rows = row_count(B, N);
+    if (rows < 0 || D < 0)
+        return DIT_ERR_ARG;
+    if (D < 8 || D % 8 != 0 || D > kMaxAdaLNWidth)
+        return DIT_ERR_SHAPE;
+    if (!(eps > 0.f) || !isfinite(eps))
+        return DIT_ERR_ARG;
+    if (rows == 0)
+        return DIT_OK;
+    if (!x || !shift || !scale || !y)
+        return DIT_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(shift, 16) || !aligned(scale, 16) || !aligned(y, 16))
+        return DIT_ERR_ALIGN;
+    const int64_t nx = rows * D * 2, nv = B * D * 2;
+    if (bad_alias(y, x, nx) || overlap(y, nx, shift, nv) || overlap(y, nx, scale, nv))
+        return DIT_ERR_ARG;
+    return launched(dit::launch_adaln_modulate(x, shift, scale, y, rows, N, D, eps, (hipStream_t)stream));
+}
+
+dit_status dit_gated_residual(const dit_bf16 *x, const dit_bf16 *y, const dit_bf16 *gate, dit_bf16 *out, int64_t B,
+                              int64_t N, int64_t D, void *stream)
+{
+    const int64_t rows = row_count(B, N);
+    if (rows < 0 || D < 0)
+        return DIT_ERR_ARG;
+    if (D < 8 || D % 8 != 0 || D > kMaxWidth)
+        return DIT_ERR_SHAPE;
+    if (rows == 0)
+        return DIT_OK;
+    if (!x || !y || !gate || !out)
+        return DIT_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(y, 16) || !aligned(gate, 16) || !aligned(out, 16))
+        return DIT_ERR_ALIGN;
+    const int64_t nx = rows * D * 2, ng = B * D * 2;
+    if (bad_alias(out, x, nx) || bad_alias(out, y, nx) || overlap(out, nx, gate, ng))
+        return DIT_ERR_ARG;
+    return launched(dit::launch_gated_residual(x, y, gate, out, rows, N, D, (hipStream_t)stream));
+}
+
+dit_status dit_swiglu(const dit_bf16 *in, dit_bf16 *out, int64_t M, int64_t F, void *stream)
+{
+    if (M < 0 || M > kMaxRows || F < 0)
+        return DIT_ERR_ARG;
+    if (F < 8 || F % 8 != 0 || F > kMaxWidth)
+        return DIT_ERR_SHAPE;
+    if (M == 0)
+        return DIT_OK;
+    if (!in || !out)
+        return DIT_ERR_NULL;
+    if (!aligned(in, 16) || !aligned(out, 16))
+        return DIT_ERR_ALIGN;
+    if (overlap(out, M * F * 2, in, M * F * 4))
+        return DIT_ERR_ARG;
+    return launched(dit::launch_swiglu(in, out, M, F, (hipStream_t)stream));
+}
+
+dit_status dit_qk_rmsnorm_rope3d(const dit_bf16 *q, const dit_bf16 *k, dit_bf16 *q_out, dit_bf16 *k_out,
+                                 const dit_bf16 *wq, const dit_bf16 *wk, const int32_t *pos, int64_t B, int64_t N,
+                                 int64_t H, int64_t Dh, int32_t d_t, int32_t d_h, int32_t d_w, float theta, float eps,
+                                 void *stream)
+{
+    const int64_t rows = row_count(B, N);
+    if (rows < 0 || H < 0 || Dh < 0)
+        return DIT_ERR_ARG;
+    const bool dh_ok = Dh == 8 || Dh == 16 || Dh == 32 || Dh == 64 || Dh == 128 || Dh == 256;
+    if (!dh_ok || H < 1 || H * Dh > kMaxHeadRow || d_t < 0 || d_h < 0 || d_w < 0 || (d_t | d_h | d_w) & 1 ||
+        (int64_t)d_t + d_h + d_w != Dh)
+        return DIT_ERR_SHAPE;
+    if (!(eps > 0.f) || !isfinite(eps) || !(theta > 1.f) || !isfinite(theta))
+        return DIT_ERR_ARG;
+    if (rows == 0)
+        return DIT_OK;
+    if (!q || !k || !q_out || !k_out || !wq || !wk || !pos)
+        return DIT_ERR_NULL;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(q_out, 16) || !aligned(k_out, 16) || !aligned(wq, 16) ||
+        !aligned(wk, 16) || !aligned(pos, 4))
+        return DIT_ERR_ALIGN;
+    const int64_t nt = rows * H * Dh * 2, nw = Dh * 2, np = N * 12;
+    if (bad_alias(q_out, q, nt) || overlap(q_out, nt, k, nt) || overlap(q_out, nt, wq, nw) ||
+        overlap(q_out, nt, wk, nw) || overlap(q_out, nt, pos, np) || bad_alias(k_out, k, nt) ||
+        overlap(k_out, nt, q, nt) || overlap(k_out, nt, wq, nw) || overlap(k_out, nt, wk, nw) ||
+        overlap(k_out, nt, pos, np) || overlap(k_out, nt, q_out, nt))
+        return DIT_ERR_ARG;
+    return launched(dit::launch_qk_rmsnorm_rope3d(q, k, q_out, k_out, wq, wk, pos, rows, N, H, Dh, d_t, d_h, d_w,
+                                                  theta, eps, (hipStream_t)stream));
+}
+
+dit_status dit_packed_positions(int32_t *pos, int64_t T, int64_t Hg, int64_t Wg, int64_t n_extra, void *stream)
+{
+    if (T < 0 || Hg < 0 || Wg < 0 || n_extra < 0 || n_extra > kMaxRows)
+        return DIT_ERR_ARG;
+    const int64_t hw = row_count(Hg, Wg);
+    const int64_t video = hw < 0 ? -1 : row_count(T, hw);
+    if (video < 0 || video + n_extra > kMaxRows)
+        return DIT_ERR_ARG;
+    if (video + n_extra == 0)
+        return DIT_OK;
+    if (!pos)
+        return DIT_ERR_NULL;
+    if (!aligned(pos, 4))
+        return DIT_ERR_ALIGN;
+    return launched(dit::launch_packed_positions(pos, T, Hg, Wg, n_extra, (hipStream_t)stream));
+}
+
+dit_status dit_copy16(const void *src, void *dst, int64_t bytes, void *stream)
+{
+    if (bytes < 0)
+        return DIT_ERR_ARG;
+    if (bytes % 16 != 0)
+        return DIT_ERR_SHAPE;
+    if (bytes == 0)
+        return DIT_OK;
+    if (!src || !dst)
+        return DIT_ERR_NULL;
+    if (!aligned(src, 16) || !aligned(dst, 16))
+        return DIT_ERR_ALIGN;
+    if (overlap(src, bytes, dst, bytes))
+        return DIT_ERR_ARG;
+    return launched(dit::launch_copy16(src, dst, bytes, (hipStream_t)stream));
+}
+
+} // extern "C"

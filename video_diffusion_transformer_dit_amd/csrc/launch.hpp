@@ -1,0 +1,36 @@
+// launch.hpp -- host-side launchers of the chain's kernels.  Each assumes its
+// arguments were validated by the C entry points in abi.hip (sizes in range,
+// pointers 16-byte aligned) and enqueues on `stream` without synchronising.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dit {
+
+// y = LN(x) * (1 + scale[b]) + shift[b]; rows = B*N, D % 8 == 0, D <= 8192.
+hipError_t launch_adaln_modulate(const void *x, const void *shift, const void *scale, void *y,
+                                 int64_t rows, int64_t N, int64_t D, float eps, hipStream_t stream);
+
+// out = x + gate[b] * y; rows = B*N, D % 8 == 0.
+hipError_t launch_gated_residual(const void *x, const void *y, const void *gate, void *out,
+                                 int64_t rows, int64_t N, int64_t D, hipStream_t stream);
+
+// out[r][j] = silu(in[r][j]) * in[r][F+j]; F % 8 == 0.
+hipError_t launch_swiglu(const void *in, void *out, int64_t M, int64_t F, hipStream_t stream);
+
+// Per-head RMSNorm + 3D RoPE of q and k; Dh in {8,...,256} (power of two).
+hipError_t launch_qk_rmsnorm_rope3d(const void *q, const void *k, void *q_out, void *k_out,
+                                    const void *wq, const void *wk, const int32_t *pos,
+                                    int64_t rows, int64_t N, int64_t H, int64_t Dh,
+                                    int d_t, int d_h, int d_w, float theta, float eps,
+                                    hipStream_t stream);
+
+// Packed (t, h, w) coordinates of T*Hg*Wg video tokens then n_extra tokens.
+hipError_t launch_packed_positions(int32_t *pos, int64_t T, int64_t Hg, int64_t Wg, int64_t n_extra,
+                                   hipStream_t stream);
+
+// dst = src, bytes % 16 == 0.
+hipError_t launch_copy16(const void *src, void *dst, int64_t bytes, hipStream_t stream);
+
+} // namespace dit
