@@ -130,7 +130,8 @@ def test_adaln_in_place_and_deterministic():
 
 # --------------------------------------------------------------------------- gated residual
 
-RESIDUAL_SHAPES = [(1, 33, 4096), (2, 1953, 4096), (1, 7, 8), (3, 5, 264), (2, 3, 1000), (1, 2, 65536), (1, 9, 24)]
+RESIDUAL_SHAPES = [(1, 33, 4096), (2, 1953, 4096), (1, 7, 8), (3, 5, 264), (2, 3, 1000), (1, 2, 65536), (1, 9, 24),
+                   (2, 5, 12288)]
 
 
 @pytest.mark.parametrize("B,N,D", RESIDUAL_SHAPES)
@@ -160,7 +161,7 @@ def test_gated_residual_zero_gate_in_place_deterministic():
 
 # --------------------------------------------------------------------------- SwiGLU
 
-SWIGLU_SHAPES = [(33, 16384), (7, 8), (5, 1000), (3, 16392), (64, 2048), (1, 8), (1953, 512), (2, 24)]
+SWIGLU_SHAPES = [(33, 16384), (7, 8), (5, 1000), (3, 16392), (64, 2048), (1, 8), (1953, 512), (2, 24), (5, 6144)]
 
 
 @pytest.mark.parametrize("M,F", SWIGLU_SHAPES)

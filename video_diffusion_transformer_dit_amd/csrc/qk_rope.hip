@@ -6,34 +6,32 @@
 // u = v / sqrt(mean(v^2) + eps) * w, then the head's channels form three
 // contiguous bands (t, h, w); in a band of width d at coordinate p the
 // adjacent pair (2j, 2j+1) turns counter-clockwise by p * theta^(-2j/d).
-// Fused, q and k are read once and written once (8 bytes per channel pair of
-// q and k together), and no cos/sin table is read: the angles come from the
-// token's integer coordinate in registers.
+// Fused, q and k are read once and written once (8 bytes per channel of q
+// and k together), and no cos/sin table is read from memory: the angles come
+// from the token's integer coordinate.
 //
-// Mapping (gfx950): one 64-lane wavefront per token at a time, four waves per
-// 256-thread workgroup, waves striding over the tokens.  A head of Dh channels is Dh/8 lanes holding 8 channels (16 bytes)
-// each, so a wave instruction covers 64*8 channels = 512/Dh heads and lane l
-// always holds channels 8*(l mod Dh/8) .. +7 of some head.  Hence:
-//   - the head's sum of squares is a DPP sum over Dh/8 adjacent lanes;
-//   - a lane's 4 channel pairs, their bands and frequencies are fixed for the
-//     whole kernel (computed once, in fp64, as turns per unit coordinate);
-//   - per token a lane evaluates 4 (cos, sin) pairs, reused for every head of
-//     q and of k.
-// The angle is reduced to [-1/2, 1/2] turn in fp64 before the hardware sine
-// and cosine (v_sin_f32 / v_cos_f32 take turns), so coordinates in the
-// hundreds lose no accuracy.
+// Mapping (gfx950): each thread handles one 16-byte vector (8 channels of one
+// head); a 256-thread workgroup covers 256 vectors of one token's q or k row,
+// i.e. 256*8/Dh heads.  The grid is 2-D: x = token, y = part, where parts
+// 0 .. P-1 cover q and P .. 2P-1 cover k.  The dispatcher runs x fastest, so
+// each part streams token after token: at any time the workgroups in flight
+// read one input stream and write one output stream, which the MI355X
+// memory system serves faster than interleaving q, k and both outputs.
+//   - A head is Dh/8 adjacent lanes, so its sum of squares is a DPP sum over
+//     those lanes (no LDS).
+//   - The token's Dh/2 (cos, sin) pairs are computed once per workgroup by
+//     its first Dh/2 threads into LDS and read by all: the angle in turns is
+//     coordinate * theta^(-2i/d) / (2 pi), formed and reduced to [-1/2, 1/2]
+//     in fp64, then fed to the hardware v_cos_f32 / v_sin_f32 (which take
+//     turns), so coordinates in the hundreds lose no accuracy.
 #include "device_common.hpp"
 #include "launch.hpp"
 
 namespace dit {
 namespace {
 
-constexpr int kTokensPerBlock = 256 / kWave;
-constexpr int kGroup = 8; // vectors per lane per tensor loaded together
-// Waves loop over tokens; the grid is capped so each wave amortises its
-// per-lane constants over several tokens while still oversubscribing the
-// 256 CUs many times.
-constexpr int kMaxBlocks = 2048;
+constexpr int kQKThreads = 256;
+constexpr double kInv2Pi = 0.15915494309189535;
 
 template <int LPH>
 __device__ __forceinline__ u32x4 norm_rotate(u32x4 raw, const float w[8], const float cs[4], const float sn[4],
@@ -58,85 +56,58 @@ __device__ __forceinline__ u32x4 norm_rotate(u32x4 raw, const float w[8], const 
     return pack8(o);
 }
 
+// LPH = Dh/8 lanes per head.  half_parts = workgroups per q (or k) row.
 template <int LPH>
-__global__ __launch_bounds__(256) void qk_rmsnorm_rope3d_kernel(const u32x4 *q, const u32x4 *k, u32x4 *q_out,
-                                                                u32x4 *k_out, const u32x4 *__restrict__ wq,
-                                                                const u32x4 *__restrict__ wk,
-                                                                const int32_t *__restrict__ pos, int rows, int N,
-                                                                int VPR, int d_t, int d_h, int d_w, double log2_theta,
-                                                                float inv_dh, float eps)
+__global__ __launch_bounds__(kQKThreads) void qk_rmsnorm_rope3d_kernel(
+    const u32x4 *q, const u32x4 *k, u32x4 *q_out, u32x4 *k_out, const u32x4 *__restrict__ wq,
+    const u32x4 *__restrict__ wk, const int32_t *__restrict__ pos, int N, int B, int VPR, int half_parts, int d_t,
+    int d_h, int d_w, double log2_theta, float inv_dh, float eps)
 {
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wave = blockIdx.x * kTokensPerBlock + (threadIdx.x / kWave);
-    const int nwaves = gridDim.x * kTokensPerBlock;
+    __shared__ float2 rot[4 * LPH]; // (cos, sin) of each channel pair of a head
+    const int tid = threadIdx.x;
+    const unsigned row = blockIdx.x;
+    const int which = (int)blockIdx.y >= half_parts; // 0: q, 1: k
+    const int c = ((int)blockIdx.y - which * half_parts) * kQKThreads + tid;
+    const size_t at = (size_t)row * VPR + c;
+    const bool valid = c < VPR;
 
-    // Lane constants, fixed for every token this wave visits: the lane's slot
-    // inside a head, its 8 weights of q and of k, and for each of its 4
-    // channel pairs the band axis and theta^(-2i/d) / (2 pi) turns per unit
-    // coordinate (2i = the pair's first channel relative to its band start).
-    const int slot = lane % LPH;
-    float wqf[8], wkf[8];
-    unpack8(load_cached(wq + slot), wqf);
-    unpack8(load_cached(wk + slot), wkf);
-    int axis[4];
-    double turns_per_unit[4];
+    // Issue the row load first; it overlaps the angle computation below.
+    u32x4 raw = u32x4{0u, 0u, 0u, 0u};
+    if (valid)
+        raw = load_stream((which ? k : q) + at);
+
+    if (tid < 4 * LPH) {
+        const int ch = 2 * tid; // first channel of pair `tid`
+        int axis, lo, width;
+        if (ch < d_t) {
+            axis = 0, lo = 0, width = d_t;
+        } else if (ch < d_t + d_h) {
+            axis = 1, lo = d_t, width = d_h;
+        } else {
+            axis = 2, lo = d_t + d_h, width = d_w;
+        }
+        const int n = B == 1 ? (int)row : (int)(row % (unsigned)N);
+        const double turns_per_unit = exp2(-(double)(ch - lo) / (double)width * log2_theta) * kInv2Pi;
+        const double turns = (double)pos[3 * (size_t)n + axis] * turns_per_unit;
+        const float r = (float)(turns - rint(turns));
+        rot[tid] = make_float2(__builtin_amdgcn_cosf(r), __builtin_amdgcn_sinf(r));
+    }
+    const int slot = tid % LPH; // the lane's 8 channels are 8*slot .. 8*slot+7 of its head
+    float w[8];
+    unpack8(load_cached((which ? wk : wq) + slot), w);
+    __syncthreads();
+    float cs[4], sn[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        const int ch = slot * 8 + 2 * j;
-        int lo, width;
-        if (ch < d_t) {
-            axis[j] = 0, lo = 0, width = d_t;
-        } else if (ch < d_t + d_h) {
-            axis[j] = 1, lo = d_t, width = d_h;
-        } else {
-            axis[j] = 2, lo = d_t + d_h, width = d_w;
-        }
-        turns_per_unit[j] = exp2(-(double)(ch - lo) / (double)width * log2_theta) * 0.15915494309189535;
+        const float2 t = rot[4 * slot + j];
+        cs[j] = t.x;
+        sn[j] = t.y;
     }
-
-    for (int row = wave; row < rows; row += nwaves) { // wave-uniform loop
-        const int n = row % N;
-        const int32_t *p = pos + 3 * (size_t)n;
-        const int coord[3] = {p[0], p[1], p[2]};
-        float cs[4], sn[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const double turns = (double)coord[axis[j]] * turns_per_unit[j];
-            const float r = (float)(turns - rint(turns)); // [-1/2, 1/2] turn
-            cs[j] = __builtin_amdgcn_cosf(r);
-            sn[j] = __builtin_amdgcn_sinf(r);
-        }
-
-        const size_t base = (size_t)row * VPR;
-        for (int g0 = 0; g0 < VPR; g0 += kGroup * kWave) {
-            u32x4 qv[kGroup], kv[kGroup];
-#pragma unroll
-            for (int i = 0; i < kGroup; ++i) {
-                const int c = g0 + lane + kWave * i;
-                qv[i] = kv[i] = u32x4{0u, 0u, 0u, 0u};
-                if (c < VPR) {
-                    qv[i] = load_stream(q + base + c);
-                    kv[i] = load_stream(k + base + c);
-                }
-            }
-            // Lanes past the last head hold zeros; whole heads are either in or
-            // out (VPR is a multiple of LPH), so the group sums stay per head.
-#pragma unroll
-            for (int i = 0; i < kGroup; ++i) {
-                const int c = g0 + lane + kWave * i;
-                const u32x4 r = norm_rotate<LPH>(qv[i], wqf, cs, sn, inv_dh, eps);
-                if (c < VPR)
-                    store_stream(q_out + base + c, r);
-            }
-#pragma unroll
-            for (int i = 0; i < kGroup; ++i) {
-                const int c = g0 + lane + kWave * i;
-                const u32x4 r = norm_rotate<LPH>(kv[i], wkf, cs, sn, inv_dh, eps);
-                if (c < VPR)
-                    store_stream(k_out + base + c, r);
-            }
-        }
-    }
+    // Threads past the last head hold zeros; heads are LPH-aligned and VPR is
+    // a multiple of LPH, so every DPP group is wholly in or wholly out.
+    const u32x4 o = norm_rotate<LPH>(raw, w, cs, sn, inv_dh, eps);
+    if (valid)
+        store_stream((which ? k_out : q_out) + at, o);
 }
 
 template <int LPH>
@@ -144,10 +115,10 @@ hipError_t launch_lph(const u32x4 *q, const u32x4 *k, u32x4 *qo, u32x4 *ko, cons
                       const int32_t *pos, int rows, int N, int VPR, int d_t, int d_h, int d_w, double log2_theta,
                       float inv_dh, float eps, hipStream_t stream)
 {
-    const int blocks = (rows + kTokensPerBlock - 1) / kTokensPerBlock;
-    const dim3 grid(blocks < kMaxBlocks ? blocks : kMaxBlocks), block(256);
-    hipLaunchKernelGGL((qk_rmsnorm_rope3d_kernel<LPH>), grid, block, 0, stream, q, k, qo, ko, wq, wk, pos, rows, N,
-                       VPR, d_t, d_h, d_w, log2_theta, inv_dh, eps);
+    const int half_parts = (VPR + kQKThreads - 1) / kQKThreads;
+    const dim3 grid((unsigned)rows, (unsigned)(2 * half_parts)), block(kQKThreads);
+    hipLaunchKernelGGL((qk_rmsnorm_rope3d_kernel<LPH>), grid, block, 0, stream, q, k, qo, ko, wq, wk, pos, N,
+                       rows / N, VPR, half_parts, d_t, d_h, d_w, log2_theta, inv_dh, eps);
     return hipGetLastError();
 }
 

@@ -5,53 +5,41 @@
 // per-sample vector applied raw.  One pass: x and y are read once, out is
 // written once (6 bytes per element).
 //
-// Mapping (gfx950): the grid is (row, segment); a workgroup of up to 256
-// threads covers one segment of one row, each thread U 16-byte vectors spaced
-// one workgroup-width apart, so each wave instruction touches 1 KiB of
-// contiguous memory and every thread has 2U loads in flight.  The sample index
-// of a row is one scalar division per workgroup; the gate vector (8 KiB per
-// sample) is re-read from cache, never from HBM more than once per XCD.
+// Mapping (gfx950): each thread handles one 16-byte vector; a 512-thread
+// workgroup covers one segment of 512 vectors (a whole 4096-wide row).  The
+// grid is 1-D over (row, segment) tiles in row-major order, one tile per
+// workgroup, so consecutive workgroups stream consecutive memory.  The gate
+// vector (8 KiB per sample) is re-read from cache.  With a single sample the
+// sample index is 0 and no division is needed.
 #include "device_common.hpp"
 #include "launch.hpp"
 
 namespace dit {
 namespace {
 
-constexpr int kResidualU = 2;
+constexpr int kResidualThreads = 512;
 
-template <int U>
-__global__ __launch_bounds__(256) void gated_residual_kernel(const u32x4 *x, const u32x4 *y,
-                                                             const u32x4 *__restrict__ gate, u32x4 *out, int N,
-                                                             int C)
+template <bool POW2>
+__global__ __launch_bounds__(kResidualThreads) void gated_residual_kernel(const u32x4 *x, const u32x4 *y,
+                                                                          const u32x4 *__restrict__ gate, u32x4 *out,
+                                                                          int N, int B, int C, unsigned segs,
+                                                                          unsigned seg_shift, unsigned tiles)
 {
-    const int row = blockIdx.x;
-    const int b = row / N;
-    const size_t base = (size_t)row * C;
-    const u32x4 *g = gate + (size_t)b * C;
-    const int c0 = blockIdx.y * blockDim.x * U + threadIdx.x;
-
-    u32x4 xv[U], yv[U];
-#pragma unroll
-    for (int k = 0; k < U; ++k) {
-        const int c = c0 + k * blockDim.x;
+    for (unsigned tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
+        const unsigned row = POW2 ? tile >> seg_shift : tile / segs;
+        const int c = (int)(tile - row * segs) * kResidualThreads + threadIdx.x;
         if (c < C) {
-            xv[k] = load_stream(x + base + c);
-            yv[k] = load_stream(y + base + c);
-        }
-    }
-#pragma unroll
-    for (int k = 0; k < U; ++k) {
-        const int c = c0 + k * blockDim.x;
-        if (c < C) {
-            const u32x4 gv = load_cached(g + c);
+            const int b = B == 1 ? 0 : (int)row / N;
+            const size_t at = (size_t)row * C + c;
+            const u32x4 xv = load_stream(x + at);
+            const u32x4 yv = load_stream(y + at);
+            const u32x4 gv = load_cached(gate + (size_t)b * C + c);
             u32x4 o;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float lo = fmaf(bf16_lo(gv[i]), bf16_lo(yv[k][i]), bf16_lo(xv[k][i]));
-                const float hi = fmaf(bf16_hi(gv[i]), bf16_hi(yv[k][i]), bf16_hi(xv[k][i]));
-                o[i] = pack_bf16x2(lo, hi);
-            }
-            store_stream(out + base + c, o);
+            for (int i = 0; i < 4; ++i)
+                o[i] = pack_bf16x2(fmaf(bf16_lo(gv[i]), bf16_lo(yv[i]), bf16_lo(xv[i])),
+                                   fmaf(bf16_hi(gv[i]), bf16_hi(yv[i]), bf16_hi(xv[i])));
+            store_stream(out + at, o);
         }
     }
 }
@@ -62,16 +50,24 @@ hipError_t launch_gated_residual(const void *x, const void *y, const void *gate,
                                  int64_t D, hipStream_t stream)
 {
     const int C = (int)(D / 8);
-    int threads = 256;
-    while (threads > kWave && threads / 2 * kResidualU >= C)
-        threads /= 2;
-    const int per_block = threads * kResidualU;
-    const int segs = (C + per_block - 1) / per_block;
-    if (segs > 65535)
+    const unsigned segs = (unsigned)((C + kResidualThreads - 1) / kResidualThreads);
+    const uint64_t tiles = (uint64_t)rows * segs;
+    if (tiles > 0xffffffffull)
         return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((gated_residual_kernel<kResidualU>), dim3((unsigned)rows, (unsigned)segs), dim3(threads), 0,
-                       stream, static_cast<const u32x4 *>(x), static_cast<const u32x4 *>(y),
-                       static_cast<const u32x4 *>(gate), static_cast<u32x4 *>(out), (int)N, C);
+    const unsigned grid = tiles < (1u << 23) - 1 ? (unsigned)tiles : (1u << 23) - 1; // < 2^32 work-items
+    const int B = (int)(rows / N);
+    const auto *xv = static_cast<const u32x4 *>(x);
+    const auto *yv = static_cast<const u32x4 *>(y);
+    const auto *gv = static_cast<const u32x4 *>(gate);
+    auto *ov = static_cast<u32x4 *>(out);
+    if ((segs & (segs - 1)) == 0) {
+        const unsigned shift = (unsigned)__builtin_ctz(segs);
+        hipLaunchKernelGGL((gated_residual_kernel<true>), dim3(grid), dim3(kResidualThreads), 0, stream, xv, yv, gv,
+                           ov, (int)N, B, C, segs, shift, (unsigned)tiles);
+    } else {
+        hipLaunchKernelGGL((gated_residual_kernel<false>), dim3(grid), dim3(kResidualThreads), 0, stream, xv, yv, gv,
+                           ov, (int)N, B, C, segs, 0u, (unsigned)tiles);
+    }
     return hipGetLastError();
 }
 

@@ -13,16 +13,21 @@
 // a the exponential overflows to +inf and the reciprocal gives 0, so the
 // result saturates to (-)0 rather than NaN; for large a it is a * b.
 //
-// Mapping (gfx950): grid (row, segment), each thread U 16-byte vectors of a
-// and of b in flight, spaced one workgroup-width apart (1 KiB contiguous per
-// wave instruction).
+// Mapping (gfx950): each thread handles one 16-byte vector (8 outputs); a
+// 256-thread workgroup covers one 4 KiB segment of an output row.  The grid
+// is 1-D over (row, segment) tiles in row-major order, so consecutive
+// workgroups -- which the dispatcher spreads round-robin over the 8 XCDs --
+// walk consecutive memory in all three streams (a, b, out).  One tile per
+// workgroup and a full grid: measured on MI355X, many short-lived workgroups
+// keep more requests in flight than fewer workgroups looping over tiles or
+// threads holding several vectors.
 #include "device_common.hpp"
 #include "launch.hpp"
 
 namespace dit {
 namespace {
 
-constexpr int kSwigluU = 4;
+constexpr int kSwigluThreads = 256;
 constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ float silu_mul(float a, float b)
@@ -31,34 +36,25 @@ __device__ __forceinline__ float silu_mul(float a, float b)
     return a * __builtin_amdgcn_rcpf(1.f + e) * b;
 }
 
-template <int U>
-__global__ __launch_bounds__(256) void swiglu_kernel(const u32x4 *__restrict__ in, u32x4 *__restrict__ out, int C)
+// segs is the number of segments per row; when it is a power of two the row
+// index is a shift (seg_shift), otherwise a scalar division.
+template <bool POW2>
+__global__ __launch_bounds__(kSwigluThreads) void swiglu_kernel(const u32x4 *__restrict__ in, u32x4 *__restrict__ out,
+                                                                int C, unsigned segs, unsigned seg_shift,
+                                                                unsigned tiles)
 {
-    const size_t row = blockIdx.x;
-    const u32x4 *a = in + row * 2 * C;
-    const u32x4 *bh = a + C;
-    u32x4 *o = out + row * C;
-    const int c0 = blockIdx.y * blockDim.x * U + threadIdx.x;
-
-    u32x4 av[U], bv[U];
-#pragma unroll
-    for (int k = 0; k < U; ++k) {
-        const int c = c0 + k * blockDim.x;
+    for (unsigned tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
+        const unsigned row = POW2 ? tile >> seg_shift : tile / segs;
+        const int c = (int)(tile - row * segs) * kSwigluThreads + threadIdx.x;
         if (c < C) {
-            av[k] = load_stream(a + c);
-            bv[k] = load_stream(bh + c);
-        }
-    }
-#pragma unroll
-    for (int k = 0; k < U; ++k) {
-        const int c = c0 + k * blockDim.x;
-        if (c < C) {
+            const u32x4 *a = in + (size_t)row * 2 * C;
+            const u32x4 av = load_stream(a + c);
+            const u32x4 bv = load_stream(a + C + c);
             u32x4 r;
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                r[i] = pack_bf16x2(silu_mul(bf16_lo(av[k][i]), bf16_lo(bv[k][i])),
-                                   silu_mul(bf16_hi(av[k][i]), bf16_hi(bv[k][i])));
-            store_stream(o + c, r);
+                r[i] = pack_bf16x2(silu_mul(bf16_lo(av[i]), bf16_lo(bv[i])), silu_mul(bf16_hi(av[i]), bf16_hi(bv[i])));
+            store_stream(out + (size_t)row * C + c, r);
         }
     }
 }
@@ -68,15 +64,23 @@ __global__ __launch_bounds__(256) void swiglu_kernel(const u32x4 *__restrict__ i
 hipError_t launch_swiglu(const void *in, void *out, int64_t M, int64_t F, hipStream_t stream)
 {
     const int C = (int)(F / 8);
-    int threads = 256;
-    while (threads > kWave && threads / 2 * kSwigluU >= C)
-        threads /= 2;
-    const int per_block = threads * kSwigluU;
-    const int segs = (C + per_block - 1) / per_block;
-    if (segs > 65535)
+    const unsigned segs = (unsigned)((C + kSwigluThreads - 1) / kSwigluThreads);
+    const uint64_t tiles = (uint64_t)M * segs;
+    if (tiles > 0xffffffffull)
         return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((swiglu_kernel<kSwigluU>), dim3((unsigned)M, (unsigned)segs), dim3(threads), 0, stream,
-                       static_cast<const u32x4 *>(in), static_cast<u32x4 *>(out), C);
+    // A dispatch holds fewer than 2^32 work-items: beyond 2^24-1 workgroups the
+    // grid stays at that size and workgroups loop over tiles.
+    const unsigned grid = tiles < (1u << 24) - 1 ? (unsigned)tiles : (1u << 24) - 1;
+    const auto *src = static_cast<const u32x4 *>(in);
+    auto *dst = static_cast<u32x4 *>(out);
+    if ((segs & (segs - 1)) == 0) {
+        const unsigned shift = (unsigned)__builtin_ctz(segs);
+        hipLaunchKernelGGL((swiglu_kernel<true>), dim3(grid), dim3(kSwigluThreads), 0, stream, src, dst, C, segs,
+                           shift, (unsigned)tiles);
+    } else {
+        hipLaunchKernelGGL((swiglu_kernel<false>), dim3(grid), dim3(kSwigluThreads), 0, stream, src, dst, C, segs,
+                           0u, (unsigned)tiles);
+    }
     return hipGetLastError();
 }
 
