@@ -97,12 +97,17 @@ def parse_args(argv=None):
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="target oracle time for the CPU baseline")
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle leg (profiling runs)")
     p.add_argument("--copy-calibration", action="store_true",
-                   help="also run one 1 GiB dit_copy16 per timed step's warm-up (counter calibration runs)")
+                   help="run three 1 GiB dit_copy16 calls after warm-up (known-size work for counter calibration)")
+    p.add_argument("--summarize-rocprof", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
+                   help="write profiles/ summaries from rocprofv3 CSV output of a kernel-trace run and of "
+                        "FETCH_SIZE and WRITE_SIZE counter runs of this benchmark, then exit")
     return p.parse_args(argv)
 
 
 def main(argv=None) -> int:
     args = parse_args(argv)
+    if args.summarize_rocprof:
+        return summarize_rocprof(*args.summarize_rocprof, workload=args.workload)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures the chain on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
@@ -256,7 +261,7 @@ def cpu_baseline(wl, ins, outs, target_s: float) -> dict:
 
     import oracle  # test infrastructure: used only by this leg of the benchmark
     from synthetic_inputs import bits
-    from tests.parity_util import worst
+    from tests.parity_util import worst_ratio
 
     threads = max(1, min(16, os.cpu_count() or 1))
     R, N, B = wl.R, wl.N, wl.B
@@ -305,32 +310,27 @@ def cpu_baseline(wl, ins, outs, target_s: float) -> dict:
         return res
 
     def check(res, gpu):
-        ex = -np.inf
+        """Largest |gpu - oracle| / bound over the chunk (<= 1 passes)."""
+        ratio = 0.0
         for key, parts in res.items():
             for sel, ref in parts:
-                ex = max(ex, worst(gpu[key][sel], ref)[0])
-        return ex
+                ratio = max(ratio, worst_ratio(gpu[key][sel], ref))
+        return ratio
 
-    # Calibrate on one small chunk, then size the sample for about target_s seconds.
-    chunk = 64
-    rows_all = np.linspace(0, R - 1, num=min(R, 1 << 20)).astype(np.int64)
-    probe = rows_all[:: max(1, len(rows_all) // chunk)][:chunk].tolist()
-    host, gpu = chunk_rows(probe)
-    t = time.perf_counter()
-    res = run_oracle(probe, host)
-    per_row = (time.perf_counter() - t) / len(probe)
-    max_excess = check(res, gpu)
-    total = min(R, max(chunk, int(target_s / max(per_row, 1e-9))))
-    sample = np.unique(np.linspace(0, R - 1, num=total).astype(np.int64))
-    elapsed, done = 0.0, 0
-    for c0 in range(0, len(sample), 512):
-        rows = sample[c0:c0 + 512].tolist()
+    # Seeded random tokens, in chunks, until about target_s seconds of oracle time.
+    order = np.random.default_rng(0).permutation(R)
+    chunk = 1024
+    elapsed, done, max_ratio = 0.0, 0, 0.0
+    for c0 in range(0, R, chunk):
+        rows = np.sort(order[c0:c0 + chunk]).tolist()
         host, gpu = chunk_rows(rows)
         t = time.perf_counter()
         res = run_oracle(rows, host)
         elapsed += time.perf_counter() - t
         done += len(rows)
-        max_excess = max(max_excess, check(res, gpu))
+        max_ratio = max(max_ratio, check(res, gpu))
+        if elapsed >= target_s:
+            break
     tokens_per_s = done / elapsed
     return {
         "value": round(tokens_per_s * per_token / 1e9, 4),
@@ -338,13 +338,148 @@ def cpu_baseline(wl, ins, outs, target_s: float) -> dict:
         "tokens_per_s": round(tokens_per_s, 1),
         "cores": threads,
         "kind": "oracle",
-        "sample": f"{done} of {R} tokens, evenly spaced over the sequence, of the {wl.name} workload; all four "
-                  f"ops in the fp64 C oracle on {threads} host threads; {elapsed:.1f} s of oracle time "
-                  f"(the same tokens' GPU outputs are checked against it)",
-        "parity_rows_checked": done + len(probe),
-        "parity_max_excess": max_excess,
-        "parity_ok": bool(max_excess <= 0.0),
+        "sample": f"{done} of {R} tokens (seeded uniform random rows) of the {wl.name} workload; all four ops "
+                  f"in the fp64 C oracle on {threads} host threads; {elapsed:.1f} s of oracle time (the same "
+                  f"tokens' GPU outputs are checked against it)",
+        "parity_rows_checked": done,
+        "parity_max_err_over_bound": round(max_ratio, 4),
+        "parity_ok": bool(max_ratio <= 1.0),
     }
+
+# --------------------------------------------------------------------------- rocprofv3 summaries
+
+KERNEL_OPS = {
+    "packed_positions_kernel": "positions",
+    "adaln_modulate_kernel": "adaln",
+    "gated_residual_kernel": "residual",
+    "swiglu_kernel": "swiglu",
+    "qk_rmsnorm_rope3d_kernel": "qk",
+    "copy16_kernel": "copy",
+}
+
+PROFILE_COMMANDS = """\
+cd /tmp && export TMPDIR=/tmp
+rocprofv3 --kernel-trace --stats --output-format csv -d $REPO/gpurun_out/prof_trace -o trace -- \\
+    python $REPO/bench.py --workload {wl} --steps 10 --warmup 2 --no-cpu-baseline
+rocprofv3 --pmc FETCH_SIZE --output-format csv -d $REPO/gpurun_out/prof_fetch -o fetch -- \\
+    python $REPO/bench.py --workload {wl} --steps 2 --warmup 1 --no-cpu-baseline --copy-calibration
+rocprofv3 --pmc WRITE_SIZE --output-format csv -d $REPO/gpurun_out/prof_write -o write -- \\
+    python $REPO/bench.py --workload {wl} --steps 2 --warmup 1 --no-cpu-baseline --copy-calibration
+cd $REPO && python bench.py --workload {wl} --summarize-rocprof gpurun_out/prof_trace gpurun_out/prof_fetch gpurun_out/prof_write"""
+
+
+def _kernel_op(name: str):
+    for key, op in KERNEL_OPS.items():
+        if key in name:
+            return op
+    return None
+
+
+def _csv_rows(directory: str, suffix: str):
+    import csv
+    import glob
+
+    files = sorted(glob.glob(os.path.join(directory, "**", f"*{suffix}"), recursive=True))
+    if not files:
+        raise FileNotFoundError(f"no *{suffix} under {directory}")
+    rows = []
+    for f in files:
+        with open(f, newline="", encoding="utf-8") as fh:
+            rows.extend(csv.DictReader(fh))
+    return rows
+
+
+def summarize_rocprof(trace_dir: str, fetch_dir: str, write_dir: str, workload: str = "full5s") -> int:
+    """Turn rocprofv3 CSV output into the short summaries kept under profiles/.
+
+    Counter calibration: every dit_copy16 dispatch in the counter runs moves a
+    known number of bytes (one 16-byte vector per work-item, read once and
+    written once), so FETCH_SIZE and WRITE_SIZE are each scaled by
+    known bytes / counter bytes summed over those dispatches.
+    """
+    import synthetic_inputs as si
+
+    wl = si.WORKLOADS[workload]
+    nbytes = op_bytes(wl)
+    out_dir = os.path.join(ROOT, "profiles")
+    os.makedirs(out_dir, exist_ok=True)
+    commands = PROFILE_COMMANDS.format(wl=workload)
+
+    stats = {}
+    for r in _csv_rows(trace_dir, "kernel_stats.csv"):
+        op = _kernel_op(r["Name"])
+        if op:
+            m = re.search(r"::(\w+(?:<[^()]*>)?)\(", r["Name"])
+            stats[op] = {"name": m.group(1) if m else r["Name"][:60], "calls": int(r["Calls"]), "avg_us": float(r["AverageNs"]) / 1e3,
+                         "min_us": float(r["MinNs"]) / 1e3, "max_us": float(r["MaxNs"]) / 1e3}
+
+    counters = {"FETCH_SIZE": {}, "WRITE_SIZE": {}}
+    calib = {"FETCH_SIZE": [0.0, 0.0], "WRITE_SIZE": [0.0, 0.0]}  # known bytes, counter bytes
+    for directory in (fetch_dir, write_dir):
+        for r in _csv_rows(directory, "counter_collection.csv"):
+            op = _kernel_op(r["Kernel_Name"])
+            name = r["Counter_Name"]
+            if op is None or name not in counters:
+                continue
+            kib = float(r["Counter_Value"])
+            if op == "copy":
+                calib[name][0] += 16.0 * int(r["Grid_Size"])
+                calib[name][1] += kib * 1024.0
+            else:
+                counters[name].setdefault(op, []).append(kib)
+    factor = {k: (v[0] / v[1] if v[1] else None) for k, v in calib.items()}
+
+    lines = [f"# Kernel durations: {wl.description}", "",
+             "rocprofv3 kernel trace of the benchmark step (10 timed + 2 warm-up steps, plus the copy-ceiling "
+             "copies). Bytes are the compulsory (algorithmic) HBM bytes of one launch; GB/s uses the average "
+             "duration.", "", "Commands (from the repository root on the GPU host, REPO=$PWD):", "", "```",
+             commands, "```", "",
+             "| kernel | calls | avg us | min us | max us | algorithmic bytes | GB/s at avg | % of 8 TB/s |",
+             "|---|---|---|---|---|---|---|---|"]
+    for op in ("positions", "adaln", "residual", "swiglu", "qk", "copy"):
+        if op not in stats:
+            continue
+        st = stats[op]
+        b = nbytes.get(op)
+        gbs = f"{b / (st['avg_us'] * 1e-6) / 1e9:.1f}" if b else "-"
+        pct = f"{100 * b / (st['avg_us'] * 1e-6) / 1e9 / HBM_PEAK_GBPS:.1f}" if b else "-"
+        lines.append(f"| `{st['name']}` | {st['calls']} | {st['avg_us']:.2f} | {st['min_us']:.2f} | {st['max_us']:.2f} "
+                     f"| {b if b else '-'} | {gbs} | {pct} |")
+    with open(os.path.join(out_dir, f"kernels_{workload}_trace.md"), "w", encoding="utf-8") as fh:
+        fh.write("\n".join(lines) + "\n")
+
+    for op in ("adaln", "residual", "swiglu", "qk"):
+        if op not in counters["FETCH_SIZE"] or op not in counters["WRITE_SIZE"]:
+            continue
+        f_kib = sum(counters["FETCH_SIZE"][op]) / len(counters["FETCH_SIZE"][op])
+        w_kib = sum(counters["WRITE_SIZE"][op]) / len(counters["WRITE_SIZE"][op])
+        hbm = f_kib * 1024 * factor["FETCH_SIZE"] + w_kib * 1024 * factor["WRITE_SIZE"]
+        body = [
+            f"# HBM traffic of `{op}` on {wl.description}", "",
+            "rocprofv3 counters, one counter per run (FETCH_SIZE, then WRITE_SIZE), KiB per dispatch averaged "
+            "over the timed and warm-up launches of the run; each scaled by the same counter's reading for "
+            "dit_copy16 calls of known size in the same run.", "",
+            "Commands (from the repository root on the GPU host, REPO=$PWD):", "", "```", commands, "```", "",
+            f"- dispatches: {len(counters['FETCH_SIZE'][op])} (FETCH_SIZE run), "
+            f"{len(counters['WRITE_SIZE'][op])} (WRITE_SIZE run)",
+            f"- FETCH_SIZE per launch: {f_kib:.1f} KiB (raw)",
+            f"- WRITE_SIZE per launch: {w_kib:.1f} KiB (raw)",
+            f"- copy calibration factor FETCH_SIZE: {factor['FETCH_SIZE']:.4f} "
+            f"({calib['FETCH_SIZE'][0]:.0f} known bytes read / {calib['FETCH_SIZE'][1]:.0f} counted)",
+            f"- copy calibration factor WRITE_SIZE: {factor['WRITE_SIZE']:.4f} "
+            f"({calib['WRITE_SIZE'][0]:.0f} known bytes written / {calib['WRITE_SIZE'][1]:.0f} counted)",
+            f"- HBM bytes per launch (calibrated): {hbm:.6e}",
+            f"- algorithmic bytes per launch: {nbytes[op]:.6e}",
+            f"- calibrated / algorithmic: {hbm / nbytes[op]:.4f}",
+            f"- kernel source sha256: {source_digest(op)}",
+        ]
+        if op in stats:
+            body.append(f"- kernel-trace average duration: {stats[op]['avg_us']:.2f} us "
+                        f"({nbytes[op] / (stats[op]['avg_us'] * 1e-6) / 1e9:.1f} GB/s algorithmic)")
+        with open(os.path.join(out_dir, f"{op}_{workload}_counters.md"), "w", encoding="utf-8") as fh:
+            fh.write("\n".join(body) + "\n")
+    print(f"wrote profiles/ summaries for {workload}; calibration factors {factor}")
+    return 0
 
 
 if __name__ == "__main__":

@@ -30,6 +30,16 @@ def worst(gpu: np.ndarray, ref: np.ndarray):
     return float(ex[i]), i, float(gpu[i]), float(ref[i])
 
 
+def worst_ratio(gpu, ref) -> float:
+    """Largest |gpu - ref| / (ATOL + RTOL |ref|); <= 1 means every element is within the bound."""
+    gpu = np.asarray(gpu, dtype=np.float64).ravel()
+    ref = np.asarray(ref, dtype=np.float64).ravel()
+    if gpu.size == 0:
+        return 0.0
+    r = np.abs(gpu - ref) / (ATOL + RTOL * np.abs(ref))
+    return float(np.inf) if np.isnan(r).any() else float(r.max())
+
+
 def assert_close(gpu, ref, what: str = ""):
     """Fail with the worst element if any element breaks the bound or is not finite."""
     g = to_f64(gpu) if isinstance(gpu, torch.Tensor) else np.asarray(gpu, dtype=np.float64)
