@@ -76,8 +76,14 @@ __device__ __forceinline__ float dpp_read(float v)
 // every lane of a group receives the group total.  Must be called with all 64
 // lanes active.  Groups of up to 16 lanes stay inside one DPP row: after the
 // two quad swaps each quad holds its sum, the half-row mirror pairs quad 0
-// with quad 1, and the row mirror pairs the two halves.  Wider groups swap
-// 16- and 32-lane halves through the cross-lane permute.
+// with quad 1, and the row mirror pairs the two halves.  Wider groups then add
+// the row totals read out of lanes 0, 16, 32 and 48 with v_readlane (scalar
+// registers, a few cycles) instead of a round trip through the LDS crossbar.
+__device__ __forceinline__ float lane_value(float v, int lane)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+
 template <int L>
 __device__ __forceinline__ float group_sum(float v)
 {
@@ -86,8 +92,13 @@ __device__ __forceinline__ float group_sum(float v)
     if constexpr (L >= 4) v += dpp_read<kDppQuadSwap2>(v);
     if constexpr (L >= 8) v += dpp_read<kDppRowHalfMirror>(v);
     if constexpr (L >= 16) v += dpp_read<kDppRowMirror>(v);
-    if constexpr (L >= 32) v += __shfl_xor(v, 16, kWave);
-    if constexpr (L >= 64) v += __shfl_xor(v, 32, kWave);
+    if constexpr (L == 32) {
+        const float lo = lane_value(v, 0) + lane_value(v, 16);
+        const float hi = lane_value(v, 32) + lane_value(v, 48);
+        v = (__lane_id() < 32) ? lo : hi;
+    }
+    if constexpr (L == 64)
+        v = (lane_value(v, 0) + lane_value(v, 16)) + (lane_value(v, 32) + lane_value(v, 48));
     return v;
 }
 

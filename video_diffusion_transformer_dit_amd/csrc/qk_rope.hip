@@ -23,7 +23,13 @@
 //     its first Dh/2 threads into LDS and read by all: the angle in turns is
 //     coordinate * theta^(-2i/d) / (2 pi), formed and reduced to [-1/2, 1/2]
 //     in fp64, then fed to the hardware v_cos_f32 / v_sin_f32 (which take
-//     turns), so coordinates in the hundreds lose no accuracy.
+//     turns), so coordinates in the hundreds lose no accuracy.  The per-pair
+//     factor theta^(-2i/d) / (2 pi) and band axis depend only on (Dh, bands,
+//     theta): the launcher computes them once in double and passes them in
+//     the kernel arguments, so no cos/sin table and no exponential is
+//     evaluated per token.
+#include <math.h>
+
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -31,7 +37,15 @@ namespace dit {
 namespace {
 
 constexpr int kQKThreads = 256;
-constexpr double kInv2Pi = 0.15915494309189535;
+constexpr int kMaxPairs = 128; // Dh / 2 for Dh <= 256
+
+// Per channel pair i of a head: theta^(-2i'/d) / (2 pi) turns per unit
+// coordinate (2i' = the pair's first channel relative to its band start, d =
+// the band width) and the coordinate axis (0 = t, 1 = h, 2 = w) of its band.
+struct RotaryPlan {
+    double turns_per_unit[kMaxPairs];
+    int32_t axis[kMaxPairs];
+};
 
 template <int LPH>
 __device__ __forceinline__ u32x4 norm_rotate(u32x4 raw, const float w[8], const float cs[4], const float sn[4],
@@ -60,8 +74,8 @@ __device__ __forceinline__ u32x4 norm_rotate(u32x4 raw, const float w[8], const 
 template <int LPH>
 __global__ __launch_bounds__(kQKThreads) void qk_rmsnorm_rope3d_kernel(
     const u32x4 *q, const u32x4 *k, u32x4 *q_out, u32x4 *k_out, const u32x4 *__restrict__ wq,
-    const u32x4 *__restrict__ wk, const int32_t *__restrict__ pos, int N, int B, int VPR, int half_parts, int d_t,
-    int d_h, int d_w, double log2_theta, float inv_dh, float eps)
+    const u32x4 *__restrict__ wk, const int32_t *__restrict__ pos, int N, int B, int VPR, int half_parts,
+    float inv_dh, float eps, const RotaryPlan plan)
 {
     __shared__ float2 rot[4 * LPH]; // (cos, sin) of each channel pair of a head
     const int tid = threadIdx.x;
@@ -71,30 +85,36 @@ __global__ __launch_bounds__(kQKThreads) void qk_rmsnorm_rope3d_kernel(
     const size_t at = (size_t)row * VPR + c;
     const bool valid = c < VPR;
 
-    // Issue the row load first; it overlaps the angle computation below.
-    u32x4 raw = u32x4{0u, 0u, 0u, 0u};
-    if (valid)
-        raw = load_stream((which ? k : q) + at);
-
+    // The lane's weights and the pair's rotary plan entry are read before the
+    // row, so that waiting for them leaves the row load in flight (vector
+    // loads complete in order).
+    const int slot = tid % LPH; // the lane's 8 channels are 8*slot .. 8*slot+7 of its head
+    const u32x4 wraw = load_cached((which ? wk : wq) + slot);
+    double turns_per_unit = 0.0;
+    int axis = 0;
     if (tid < 4 * LPH) {
-        const int ch = 2 * tid; // first channel of pair `tid`
-        int axis, lo, width;
-        if (ch < d_t) {
-            axis = 0, lo = 0, width = d_t;
-        } else if (ch < d_t + d_h) {
-            axis = 1, lo = d_t, width = d_h;
-        } else {
-            axis = 2, lo = d_t + d_h, width = d_w;
-        }
-        const int n = B == 1 ? (int)row : (int)(row % (unsigned)N);
-        const double turns_per_unit = exp2(-(double)(ch - lo) / (double)width * log2_theta) * kInv2Pi;
-        const double turns = (double)pos[3 * (size_t)n + axis] * turns_per_unit;
+        turns_per_unit = plan.turns_per_unit[tid];
+        axis = plan.axis[tid];
+    }
+    // Unconditional load (lanes past the row read the row's first vector and
+    // then zero it), so no branch forces a full wait on the plan load above.
+    u32x4 raw = load_stream((which ? k : q) + (valid ? at : (size_t)row * VPR));
+    if (!valid)
+        raw = u32x4{0u, 0u, 0u, 0u};
+
+    // The token's coordinates are the same for the whole workgroup: three
+    // scalar loads, then a per-lane select of the pair's axis.
+    const int n = B == 1 ? (int)row : (int)(row % (unsigned)N);
+    const int32_t *p = pos + 3 * (size_t)n;
+    const int p_t = p[0], p_h = p[1], p_w = p[2];
+    if (tid < 4 * LPH) {
+        const int coord = axis == 0 ? p_t : (axis == 1 ? p_h : p_w);
+        const double turns = (double)coord * turns_per_unit;
         const float r = (float)(turns - rint(turns));
         rot[tid] = make_float2(__builtin_amdgcn_cosf(r), __builtin_amdgcn_sinf(r));
     }
-    const int slot = tid % LPH; // the lane's 8 channels are 8*slot .. 8*slot+7 of its head
     float w[8];
-    unpack8(load_cached((which ? wk : wq) + slot), w);
+    unpack8(wraw, w);
     __syncthreads();
     float cs[4], sn[4];
 #pragma unroll
@@ -112,13 +132,13 @@ __global__ __launch_bounds__(kQKThreads) void qk_rmsnorm_rope3d_kernel(
 
 template <int LPH>
 hipError_t launch_lph(const u32x4 *q, const u32x4 *k, u32x4 *qo, u32x4 *ko, const u32x4 *wq, const u32x4 *wk,
-                      const int32_t *pos, int rows, int N, int VPR, int d_t, int d_h, int d_w, double log2_theta,
-                      float inv_dh, float eps, hipStream_t stream)
+                      const int32_t *pos, int rows, int N, int VPR, float inv_dh, float eps, const RotaryPlan &plan,
+                      hipStream_t stream)
 {
     const int half_parts = (VPR + kQKThreads - 1) / kQKThreads;
     const dim3 grid((unsigned)rows, (unsigned)(2 * half_parts)), block(kQKThreads);
     hipLaunchKernelGGL((qk_rmsnorm_rope3d_kernel<LPH>), grid, block, 0, stream, q, k, qo, ko, wq, wk, pos, N,
-                       rows / N, VPR, half_parts, d_t, d_h, d_w, log2_theta, inv_dh, eps);
+                       rows / N, VPR, half_parts, inv_dh, eps, plan);
     return hipGetLastError();
 }
 
@@ -135,16 +155,31 @@ hipError_t launch_qk_rmsnorm_rope3d(const void *q, const void *k, void *q_out, v
     const auto *wqv = static_cast<const u32x4 *>(wq);
     const auto *wkv = static_cast<const u32x4 *>(wk);
     const int VPR = (int)(H * Dh / 8);
-    const double log2_theta = log2((double)theta);
     const float inv_dh = 1.f / (float)Dh;
     const int r = (int)rows, n = (int)N;
+
+    RotaryPlan plan = {};
+    const double log2_theta = log2((double)theta);
+    for (int i = 0; i < (int)Dh / 2; ++i) {
+        const int ch = 2 * i;
+        int axis, lo, width;
+        if (ch < d_t) {
+            axis = 0, lo = 0, width = d_t;
+        } else if (ch < d_t + d_h) {
+            axis = 1, lo = d_t, width = d_h;
+        } else {
+            axis = 2, lo = d_t + d_h, width = d_w;
+        }
+        plan.axis[i] = axis;
+        plan.turns_per_unit[i] = exp2(-(double)(ch - lo) / (double)width * log2_theta) / (2.0 * M_PI);
+    }
     switch (Dh) {
-    case 8: return launch_lph<1>(qv, kv, qo, ko, wqv, wkv, pos, r, n, VPR, d_t, d_h, d_w, log2_theta, inv_dh, eps, stream);
-    case 16: return launch_lph<2>(qv, kv, qo, ko, wqv, wkv, pos, r, n, VPR, d_t, d_h, d_w, log2_theta, inv_dh, eps, stream);
-    case 32: return launch_lph<4>(qv, kv, qo, ko, wqv, wkv, pos, r, n, VPR, d_t, d_h, d_w, log2_theta, inv_dh, eps, stream);
-    case 64: return launch_lph<8>(qv, kv, qo, ko, wqv, wkv, pos, r, n, VPR, d_t, d_h, d_w, log2_theta, inv_dh, eps, stream);
-    case 128: return launch_lph<16>(qv, kv, qo, ko, wqv, wkv, pos, r, n, VPR, d_t, d_h, d_w, log2_theta, inv_dh, eps, stream);
-    case 256: return launch_lph<32>(qv, kv, qo, ko, wqv, wkv, pos, r, n, VPR, d_t, d_h, d_w, log2_theta, inv_dh, eps, stream);
+    case 8: return launch_lph<1>(qv, kv, qo, ko, wqv, wkv, pos, r, n, VPR, inv_dh, eps, plan, stream);
+    case 16: return launch_lph<2>(qv, kv, qo, ko, wqv, wkv, pos, r, n, VPR, inv_dh, eps, plan, stream);
+    case 32: return launch_lph<4>(qv, kv, qo, ko, wqv, wkv, pos, r, n, VPR, inv_dh, eps, plan, stream);
+    case 64: return launch_lph<8>(qv, kv, qo, ko, wqv, wkv, pos, r, n, VPR, inv_dh, eps, plan, stream);
+    case 128: return launch_lph<16>(qv, kv, qo, ko, wqv, wkv, pos, r, n, VPR, inv_dh, eps, plan, stream);
+    case 256: return launch_lph<32>(qv, kv, qo, ko, wqv, wkv, pos, r, n, VPR, inv_dh, eps, plan, stream);
     default: return hipErrorInvalidValue;
     }
 }
