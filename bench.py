@@ -17,6 +17,9 @@ The printed JSON line reports:
                  committed counter summary when it was taken on the current
                  kernel source, else null
   copy_ceiling   a plain 16-byte-vector copy on the same device
+  next_fused_residual_adaln
+                 the gated residual fused with the AdaLN that follows it,
+                 timed on its own after the chain (not part of `value`)
   cpu_baseline   the fp64 oracle on a bounded sample of the same workload,
                  on the host cores (and the GPU outputs of that sample checked
                  against it)
@@ -196,6 +199,26 @@ def main(argv=None) -> int:
                 "frac": round(achieved / HBM_PEAK_GBPS, 4),
                 "traffic": traffic, "algorithmic_bytes": nbytes[dominant]}
 
+    # The next fusion, measured on its own after the chain: gated residual ->
+    # AdaLN in one kernel (x and y read once, x_out and z written once).
+    fused_bytes = 4 * wl.R * wl.D * 2 + 3 * wl.B * wl.D * 2
+    fev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for i in range(args.warmup + args.steps):
+        if i >= args.warmup:
+            fev[i - args.warmup][0].record(stream)
+        dit.dit_gated_residual_adaln(ins["res_x"], ins["res_y"], ins["gate"], ins["shift"], ins["scale"], x_out=out,
+                                     z=y, eps=wl.eps, stream=stream)
+        if i >= args.warmup:
+            fev[i - args.warmup][1].record(stream)
+    torch.cuda.synchronize()
+    fused_ms = sum(a.elapsed_time(b) for a, b in fev) / args.steps
+    unfused_ms = ops["residual"]["avg_ms"] + ops["adaln"]["avg_ms"]
+    fused = {"op": "dit_gated_residual_adaln", "avg_ms": round(fused_ms, 5), "bytes": fused_bytes,
+             "GB_s": round(fused_bytes / (fused_ms * 1e-3) / 1e9, 1),
+             "pct_of_peak": round(100.0 * fused_bytes / (fused_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
+             "unfused_ms": round(unfused_ms, 5), "unfused_bytes": nbytes["residual"] + nbytes["adaln"],
+             "time_saved_pct": round(100.0 * (1.0 - fused_ms / unfused_ms), 1)}
+
     # A plain streaming copy on the same device: the practical ceiling.
     cbytes = 2 << 30
     src = torch.empty(cbytes, dtype=torch.uint8, device=dev)
@@ -218,6 +241,13 @@ def main(argv=None) -> int:
     mix_bytes = 2 * nbytes["adaln"] + nbytes["qk"] + 2 * nbytes["residual"] + nbytes["swiglu"]
     block_mix = {"ops": "2 adaln + qk + 2 residual + swiglu (kernel-time sum)", "ms": round(mix_ms, 4),
                  "GB_s": round(mix_bytes / (mix_ms * 1e-3) / 1e9, 1), "tokens_per_s": round(wl.R / (mix_ms * 1e-3))}
+
+    fused_mix_ms = ops["qk"]["avg_ms"] + 2 * fused_ms + ops["swiglu"]["avg_ms"]
+    fused_mix_bytes = nbytes["qk"] + 2 * fused_bytes + nbytes["swiglu"]
+    block_mix_fused = {"ops": "qk + 2 fused residual->adaln + swiglu (kernel-time sum; each residual feeds "
+                              "the next AdaLN)", "ms": round(fused_mix_ms, 4),
+                       "GB_s": round(fused_mix_bytes / (fused_mix_ms * 1e-3) / 1e9, 1),
+                       "tokens_per_s": round(wl.R / (fused_mix_ms * 1e-3))}
 
     value = chain_bytes / (ms_per_step * 1e-3) / 1e9
     result = {
@@ -246,6 +276,8 @@ def main(argv=None) -> int:
         "roofline": roofline,
         "copy_ceiling": copy_ceiling,
         "block_mix": block_mix,
+        "next_fused_residual_adaln": fused,
+        "block_mix_fused": block_mix_fused,
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, ins, {"y": y, "out": out, "sw": sw, "qo": qo, "ko": ko},

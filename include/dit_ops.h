@@ -153,6 +153,32 @@ dit_status dit_qk_rmsnorm_rope3d(const dit_bf16 *q, const dit_bf16 *k,
                                  float eps, void *stream);
 
 /*
+ * Gated residual fused with the AdaLN modulation that follows it:
+ *   x_out = x + gate[b] * y                       (rounded once to bf16)
+ *   z     = LayerNorm(x_out) * (1 + scale[b]) + shift[b]
+ * where LayerNorm (as in dit_adaln_modulate) runs over the bf16 values stored
+ * in x_out, so the result equals calling dit_gated_residual and then
+ * dit_adaln_modulate on its output.
+ * Cited: xhh.club summary, Q&A (fused-kernel answer) names both operations;
+ * the Sol-H3 abstract describes searching over such fusions; the
+ * stamatios.com summary, "Resultado principal", says fusion leaves the
+ * arithmetic unchanged.  Reads x and y once and writes x_out and z once:
+ * 8 bytes per element instead of 10 for the two separate calls.
+ *   x, y          [B][N][D] inputs
+ *   gate, shift, scale  [B][D]
+ *   x_out         [B][N][D]; x_out == x (in-place residual update) is allowed
+ *   z             [B][N][D]; z == y (reuse of the branch buffer) is allowed
+ *   any other overlap among the buffers is rejected (DIT_ERR_ARG)
+ *   D             multiple of 8, 8 <= D <= 8192
+ *   eps           > 0
+ */
+dit_status dit_gated_residual_adaln(const dit_bf16 *x, const dit_bf16 *y,
+                                    const dit_bf16 *gate, const dit_bf16 *shift,
+                                    const dit_bf16 *scale, dit_bf16 *x_out,
+                                    dit_bf16 *z, int64_t B, int64_t N,
+                                    int64_t D, float eps, void *stream);
+
+/*
  * Packed token coordinates for the 3D rotary embedding.
  * Cited: stamatios.com summary, "Resultado principal" (video and audio tokens
  * in one packed DiT sequence); xhh.club Q&A ("3D RoPE").

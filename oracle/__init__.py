@@ -51,6 +51,11 @@ def build(out_path: str = LIB_PATH, source: str = SOURCE, cc: str = "gcc") -> st
 def _bind(lib):
     lib.dit_oracle_bf16_decode.argtypes = [ctypes.c_uint16]
     lib.dit_oracle_bf16_decode.restype = _c_dbl
+    lib.dit_oracle_bf16_encode.argtypes = [_c_dbl]
+    lib.dit_oracle_bf16_encode.restype = ctypes.c_uint16
+    lib.dit_oracle_gated_residual_adaln.argtypes = [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p,
+                                                    _c_i64, _c_i64, _c_i64, _c_dbl]
+    lib.dit_oracle_gated_residual_adaln.restype = ctypes.c_int
     lib.dit_oracle_packed_positions.argtypes = [_c_p, _c_i64, _c_i64, _c_i64, _c_i64]
     lib.dit_oracle_packed_positions.restype = _c_i64
     lib.dit_oracle_adaln_modulate.argtypes = [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_dbl]
@@ -123,6 +128,11 @@ def bf16_decode(bits: int, lib=None) -> float:
     return (lib or load()).dit_oracle_bf16_decode(int(bits))
 
 
+def bf16_encode(value: float, lib=None) -> int:
+    """Bit pattern of the bf16 nearest to ``value`` (ties to even)."""
+    return int((lib or load()).dit_oracle_bf16_encode(float(value)))
+
+
 def packed_positions(T: int, Hg: int, Wg: int, n_extra: int = 0, lib=None) -> np.ndarray:
     """[N, 3] int32 token coordinates of a packed sequence (video grid, then extra tokens)."""
     lib = lib or load()
@@ -181,6 +191,36 @@ def gated_residual(x, y, gate, threads: int = 1, lib=None) -> np.ndarray:
             jobs.append(job)
     _run(jobs, threads)
     return out
+
+
+def gated_residual_adaln(x, y, gate, shift, scale, eps: float = 1e-6, threads: int = 1, lib=None):
+    """x, y [B,N,D], gate/shift/scale [B,D] (bf16 bits) -> (x_out, z) [B,N,D] float64.
+
+    x_out = x + gate*y (unrounded); z = AdaLN of x_out as stored in bf16.
+    """
+    lib = lib or load()
+    x, y, gate, shift, scale = _bits(x), _bits(y), _bits(gate), _bits(shift), _bits(scale)
+    B, N, D = x.shape
+    assert y.shape == x.shape and gate.shape == shift.shape == scale.shape == (B, D)
+    x_out = np.empty((B, N, D), dtype=np.float64)
+    z = np.empty((B, N, D), dtype=np.float64)
+    if threads <= 1:
+        _check(lib.dit_oracle_gated_residual_adaln(_ptr(x), _ptr(y), _ptr(gate), _ptr(shift), _ptr(scale),
+                                                   _ptr(x_out), _ptr(z), B, N, D, eps), "gated_residual_adaln")
+        return x_out, z
+    jobs = []
+    for b in range(B):
+        for lo, hi in _chunks(N, threads):
+            row0 = b * N + lo
+
+            def job(b=b, lo=lo, hi=hi, row0=row0):
+                _check(lib.dit_oracle_gated_residual_adaln(
+                    _ptr(x, row0 * D), _ptr(y, row0 * D), _ptr(gate, b * D), _ptr(shift, b * D),
+                    _ptr(scale, b * D), _ptr(x_out, row0 * D), _ptr(z, row0 * D), 1, hi - lo, D, eps),
+                    "gated_residual_adaln")
+            jobs.append(job)
+    _run(jobs, threads)
+    return x_out, z
 
 
 def swiglu(inp, threads: int = 1, lib=None) -> np.ndarray:

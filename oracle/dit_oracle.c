@@ -48,6 +48,34 @@ static double bf16_to_double(uint16_t bits)
 double dit_oracle_bf16_decode(uint16_t bits) { return bf16_to_double(bits); }
 
 /*
+ * Round a double to the nearest bf16 (8 significant bits, ties to even, the
+ * IEEE default), returning its bit pattern.  Used where an operation's
+ * definition stores an intermediate tensor in bf16.  Normal numbers keep 8
+ * bits below the leading one; below 2^-126 the spacing is fixed at 2^-133
+ * (bf16 subnormals); magnitudes that round past the largest finite bf16
+ * become infinity.  NaN maps to the canonical quiet NaN.
+ */
+uint16_t dit_oracle_bf16_encode(double v)
+{
+    if (isnan(v))
+        return 0x7FC0;
+    const double max_finite = ldexp(255.0, 120); /* (2 - 2^-7) * 2^127 */
+    double mag = fabs(v), q;
+    int e;
+    if (mag < ldexp(1.0, -126)) {
+        q = nearbyint(ldexp(mag, 133)) * ldexp(1.0, -133); /* ties to even */
+    } else {
+        double m = frexp(mag, &e); /* mag = m * 2^e, 0.5 <= m < 1 */
+        q = ldexp(nearbyint(ldexp(m, 8)), e - 8);
+    }
+    float f = q > max_finite ? INFINITY : (float)q; /* exact: q has <= 8 significant bits */
+    uint32_t word;
+    memcpy(&word, &f, sizeof word);
+    uint16_t bits = (uint16_t)(word >> 16);
+    return signbit(v) ? (uint16_t)(bits | 0x8000) : bits;
+}
+
+/*
  * Packed token positions.
  * Cited: "SGLang acelera video do MiniMax-H3 ..." (stamatios.com), section
  * "Resultado principal": video and audio tokens run through one packed DiT
@@ -299,3 +327,41 @@ int dit_oracle_qk_rmsnorm_rope3d(const uint16_t *q, const uint16_t *k,
     free(w_q); free(w_k); free(v); free(u);
     return status;
 }
+
+/*
+ * Gated residual fused with the AdaLN modulation that follows it.
+ * Cited: xhh.club Q&A (fused-kernel answer) names both operations, and the
+ * Sol-H3 abstract describes searching over such kernel fusions; the
+ * stamatios.com summary ("Resultado principal") says fusion leaves the
+ * arithmetic unchanged.  So this is the composition of the two unfused
+ * operations exactly as a pipeline would run them:
+ *   x_out = x + gate[b] * y                      (returned unrounded)
+ *   x_bf  = x_out stored as bf16 (round to nearest even)
+ *   z     = LN(x_bf) * (1 + scale[b]) + shift[b] (LN as in adaln_modulate)
+ * Reading: the normalisation sees the bf16-stored residual, as the unfused
+ * AdaLN reads it back from memory.
+ * x, y, x_out, z: [B][N][D]; gate, shift, scale: [B][D].
+ */
+int dit_oracle_gated_residual_adaln(const uint16_t *x, const uint16_t *y,
+                                    const uint16_t *gate, const uint16_t *shift,
+                                    const uint16_t *scale, double *x_out,
+                                    double *z, int64_t B, int64_t N, int64_t D,
+                                    double eps)
+{
+    if (!x || !y || !gate || !shift || !scale || !x_out || !z || B < 0 ||
+        N < 0 || D <= 0 || !(eps > 0))
+        return ORACLE_BAD_ARG;
+    int status = dit_oracle_gated_residual(x, y, gate, x_out, B, N, D);
+    if (status != ORACLE_OK)
+        return status;
+    size_t count = (size_t)(B * N * D);
+    uint16_t *stored = malloc(sizeof(uint16_t) * (count ? count : 1));
+    if (!stored)
+        return ORACLE_BAD_ARG;
+    for (size_t i = 0; i < count; ++i)
+        stored[i] = dit_oracle_bf16_encode(x_out[i]);
+    status = dit_oracle_adaln_modulate(stored, shift, scale, z, B, N, D, eps);
+    free(stored);
+    return status;
+}
+

@@ -100,6 +100,29 @@ def test_gated_residual_validation(lib):
     assert f(0, 0, 0, 0, 0, 3, 4096, None) == DIT_OK
 
 
+def test_gated_residual_adaln_validation(lib):
+    W = 0x800000
+    X = 0x900000
+
+    def f(x=P, y=Q, g=R, sh=S, sc=T, xo=U, z=V, B=1, N=3, D=4096, eps=1e-6):
+        return lib.dit_gated_residual_adaln(x, y, g, sh, sc, xo, z, B, N, D, eps, None)
+
+    assert f(N=-1) == DIT_ERR_ARG
+    assert f(D=8200) == DIT_ERR_SHAPE
+    assert f(D=20) == DIT_ERR_SHAPE
+    assert f(eps=0.0) == DIT_ERR_ARG
+    assert f(sh=0) == DIT_ERR_NULL
+    assert f(z=V + 4) == DIT_ERR_ALIGN
+    assert f(xo=P + 32) == DIT_ERR_ARG  # partial overlap with x
+    assert f(xo=Q) == DIT_ERR_ARG  # x_out over y
+    assert f(z=P) == DIT_ERR_ARG  # z over x
+    assert f(z=U) == DIT_ERR_ARG  # both outputs in one buffer
+    assert f(xo=R) == DIT_ERR_ARG  # x_out over the gate
+    assert f(z=T) == DIT_ERR_ARG  # z over scale
+    assert f(x=0, y=0, g=0, sh=0, sc=0, xo=0, z=0, B=0) == DIT_OK
+    assert f(xo=W, z=X, N=0) == DIT_OK
+
+
 def test_swiglu_validation(lib):
     f = lib.dit_swiglu
     assert f(P, Q, -1, 16384, None) == DIT_ERR_ARG

@@ -159,6 +159,67 @@ def test_gated_residual_zero_gate_in_place_deterministic():
     assert torch.equal(a, b) and torch.equal(a, xi) and torch.equal(a, yi)
 
 
+# --------------------------------------------------------------------------- fused gated residual + AdaLN
+
+FUSED_SHAPES = [(1, 33, 4096), (2, 1953, 4096), (3, 5, 264), (2, 17, 4104), (1, 3, 8192), (1, 7, 8), (2, 3, 1000)]
+
+
+def fused_inputs(B, N, D, seed):
+    return (randn_bf16((B, N, D), seed=seed), randn_bf16((B, N, D), seed=seed + 1),
+            randn_bf16((B, D), seed=seed + 2, scale=0.1), randn_bf16((B, D), seed=seed + 3, scale=0.1),
+            randn_bf16((B, D), seed=seed + 4, scale=0.1))
+
+
+@pytest.mark.parametrize("B,N,D", FUSED_SHAPES)
+def test_gated_residual_adaln_shapes(B, N, D):
+    x, y, g, sh, sc = fused_inputs(B, N, D, seed=B * 7 + N + D)
+    x_out, z = dit.dit_gated_residual_adaln(x, y, g, sh, sc)
+    sync()
+    xr, zr = oracle.gated_residual_adaln(bits(x), bits(y), bits(g), bits(sh), bits(sc), threads=8)
+    assert_close(x_out, xr, f"fused x_out {B}x{N}x{D}")
+    assert_close(z, zr, f"fused z {B}x{N}x{D}")
+
+
+@pytest.mark.parametrize("B,N,D", FUSED_SHAPES)
+def test_gated_residual_adaln_equals_the_two_calls(B, N, D):
+    """The fused kernel reproduces dit_gated_residual then dit_adaln_modulate bit for bit."""
+    x, y, g, sh, sc = fused_inputs(B, N, D, seed=B * 11 + N + D)
+    x_out, z = dit.dit_gated_residual_adaln(x, y, g, sh, sc)
+    x_ref = dit.dit_gated_residual(x, y, g)
+    z_ref = dit.dit_adaln_modulate(x_ref, sh, sc)
+    sync()
+    assert torch.equal(x_out, x_ref) and torch.equal(z, z_ref)
+
+
+def test_gated_residual_adaln_in_place_and_deterministic():
+    x, y, g, sh, sc = fused_inputs(2, 257, 4096, seed=101)
+    a = dit.dit_gated_residual_adaln(x, y, g, sh, sc)
+    b = dit.dit_gated_residual_adaln(x, y, g, sh, sc)
+    xi, yi = x.clone(), y.clone()
+    dit.dit_gated_residual_adaln(xi, yi, g, sh, sc, x_out=xi, z=yi)
+    sync()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+    assert torch.equal(a[0], xi) and torch.equal(a[1], yi)
+
+
+def test_gated_residual_adaln_rounding_ties():
+    """Rows whose residual lands exactly halfway between bf16 neighbours."""
+    D = 4096
+    x = torch.ones((1, 2, D), dtype=torch.bfloat16, device=DEV)
+    x[..., 1::2] = 3.0
+    y = torch.zeros_like(x)
+    y[0, 0, 0::2] = 2.0 ** -8        # 1 + 2^-8 -> 1 (tie to even)
+    y[0, 1, 0::2] = 3 * 2.0 ** -8    # 1 + 3*2^-8 -> 1 + 2^-6 (tie to even, up)
+    g = torch.ones((1, D), dtype=torch.bfloat16, device=DEV)
+    sh = torch.zeros_like(g)
+    sc = torch.zeros_like(g)
+    x_out, z = dit.dit_gated_residual_adaln(x, y, g, sh, sc)
+    sync()
+    assert torch.all(x_out[0, 0, 0::2] == 1.0) and torch.all(x_out[0, 1, 0::2] == 1.0 + 2.0 ** -6)
+    xr, zr = oracle.gated_residual_adaln(bits(x), bits(y), bits(g), bits(sh), bits(sc))
+    assert_close(z, zr, "fused z at rounding ties")
+
+
 # --------------------------------------------------------------------------- SwiGLU
 
 SWIGLU_SHAPES = [(33, 16384), (7, 8), (5, 1000), (3, 16392), (64, 2048), (1, 8), (1953, 512), (2, 24), (5, 6144)]
@@ -357,6 +418,21 @@ def test_full_workload_sampled(name):
                                     bits(row_of(ins["res_y"], r)).reshape(1, 1, -1), bits(ins["gate"][b:b + 1]))
         assert_close(row_of(out, r), ref.reshape(-1), f"{name} residual row {r}")
     del ins, out
+
+    # fused gated residual + AdaLN (residual inputs, AdaLN vectors)
+    ins = si.make_inputs(wl, device=DEV, names=("res_x", "res_y", "gate", "shift", "scale"))
+    x_out, z = dit.dit_gated_residual_adaln(ins["res_x"], ins["res_y"], ins["gate"], ins["shift"], ins["scale"],
+                                            eps=wl.eps)
+    sync()
+    assert torch.isfinite(x_out).all() and torch.isfinite(z).all()
+    for r in rows:
+        b = r // N
+        xr, zr = oracle.gated_residual_adaln(
+            bits(row_of(ins["res_x"], r)).reshape(1, 1, -1), bits(row_of(ins["res_y"], r)).reshape(1, 1, -1),
+            bits(ins["gate"][b:b + 1]), bits(ins["shift"][b:b + 1]), bits(ins["scale"][b:b + 1]), eps=wl.eps)
+        assert_close(row_of(x_out, r), xr.reshape(-1), f"{name} fused x_out row {r}")
+        assert_close(row_of(z, r), zr.reshape(-1), f"{name} fused z row {r}")
+    del ins, x_out, z
 
     # SwiGLU (the largest tensors: check runs of rows at once)
     ins = si.op_inputs(wl, "swiglu", device=DEV)

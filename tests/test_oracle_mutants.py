@@ -64,6 +64,16 @@ MUTANTS = {
     "positions_h_w_swapped": ("pos[3 * n + 1] = (int32_t)h;\n                pos[3 * n + 2] = (int32_t)w;",
                               "pos[3 * n + 1] = (int32_t)w;\n                pos[3 * n + 2] = (int32_t)h;"),
     "positions_extra_at_zero": ("pos[3 * n + 0] = (int32_t)a;", "pos[3 * n + 0] = 0;"),
+    # bf16 storage rounding
+    "encode_ties_away": ("q = ldexp(nearbyint(ldexp(m, 8)), e - 8);", "q = ldexp(round(ldexp(m, 8)), e - 8);"),
+    "encode_truncates": ("q = ldexp(nearbyint(ldexp(m, 8)), e - 8);", "q = ldexp(trunc(ldexp(m, 8)), e - 8);"),
+    "encode_seven_bits": ("q = ldexp(nearbyint(ldexp(m, 8)), e - 8);", "q = ldexp(nearbyint(ldexp(m, 7)), e - 7);"),
+    "encode_no_subnormal_ties": ("q = nearbyint(ldexp(mag, 133)) * ldexp(1.0, -133);",
+                                 "q = ceil(ldexp(mag, 133)) * ldexp(1.0, -133);"),
+    # fused gated residual + AdaLN
+    "fused_normalises_input_x": ("stored[i] = dit_oracle_bf16_encode(x_out[i]);", "stored[i] = x[i];"),
+    "fused_truncates_store": ("stored[i] = dit_oracle_bf16_encode(x_out[i]);",
+                              "{ float f = (float)x_out[i]; uint32_t w; memcpy(&w, &f, 4); stored[i] = (uint16_t)(w >> 16); }"),
     # bf16 decode
     "decode_wrong_shift": ("uint32_t word = (uint32_t)bits << 16;", "uint32_t word = (uint32_t)bits << 15;"),
 }

@@ -380,6 +380,65 @@ def pin_qk_matches_library_composition(lib):
     assert close(ko, ref(k, wk), rel=1e-11, abs_=1e-12)
 
 
+# --------------------------------------------------------------------------- bf16 storage rounding
+
+def pin_bf16_encode_hand_cases(lib):
+    for case in cases("bf16_round_hand.txt"):
+        value = evaluate(case["value"][0])
+        assert oracle.bf16_encode(value, lib=lib) == int(case["bits"][0], 16), case
+
+
+def pin_bf16_encode_matches_library_rounding(lib):
+    g = torch.Generator().manual_seed(81)
+    vals = torch.cat([torch.randn(2000, generator=g) * 3.0, torch.randn(500, generator=g) * 1e-30,
+                      torch.randn(500, generator=g) * 1e30])
+    ref = vals.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = np.array([oracle.bf16_encode(float(v), lib=lib) for v in vals.tolist()], dtype=np.uint16)
+    assert np.array_equal(got, ref)
+
+
+def pin_bf16_encode_round_trips(lib):
+    for bits in list(range(0, 0x7F80, 97)) + [0x7F7F, 0x0001, 0x8001, 0xC049]:
+        assert oracle.bf16_encode(oracle.bf16_decode(bits, lib=lib), lib=lib) == bits
+
+
+# --------------------------------------------------------------------------- fused gated residual + AdaLN
+
+def pin_residual_adaln_hand_cases(lib):
+    zeros = b16([0.0] * 4, (1, 4))
+    for case in cases("residual_adaln_hand.txt"):
+        x = b16([evaluate(v) for v in case["x"]], (1, 1, 4))
+        y = b16([evaluate(v) for v in case["y"]], (1, 1, 4))
+        g = b16([evaluate(v) for v in case["gate"]], (1, 4))
+        x_out, z = oracle.gated_residual_adaln(x, y, g, zeros, zeros, eps=1e-6, lib=lib)
+        assert close(x_out[0, 0], values(case["x_out"])), case
+        stored = b16(values(case["stored"]), (1, 1, 4))
+        assert close(z, oracle.adaln_modulate(stored, zeros, zeros, eps=1e-6, lib=lib)), case
+    x = b16([1, 2, 3, 4], (1, 1, 4))
+    y = b16([2 ** -8, 0, 0, 0], (1, 1, 4))
+    _, z = oracle.gated_residual_adaln(x, y, b16([1] * 4, (1, 4)), zeros, zeros, eps=1e-6, lib=lib)
+    assert close(z[0, 0], [v / math.sqrt(1.25 + 1e-6) for v in (-1.5, -0.5, 0.5, 1.5)])
+
+
+def pin_residual_adaln_is_the_pipeline(lib):
+    """Special cases reducing to the pinned unfused ops: gate = 0 and y = 0."""
+    B, N, D = 2, 5, 64
+    x = rand_bf16((B, N, D), seed=91)
+    y = rand_bf16((B, N, D), seed=92)
+    sh = rand_bf16((B, D), seed=93, scale=0.1)
+    sc = rand_bf16((B, D), seed=94, scale=0.1)
+    zero_g = torch.zeros((B, D), dtype=torch.bfloat16)
+    x_out, z = oracle.gated_residual_adaln(bits(x), bits(y), bits(zero_g), bits(sh), bits(sc), lib=lib)
+    assert np.array_equal(x_out, f64(x).numpy())
+    assert np.array_equal(z, oracle.adaln_modulate(bits(x), bits(sh), bits(sc), lib=lib))
+    g = rand_bf16((B, D), seed=95, scale=0.1)
+    zero_y = torch.zeros_like(y)
+    x_out, z = oracle.gated_residual_adaln(bits(x), bits(zero_y), bits(g), bits(sh), bits(sc), lib=lib)
+    assert np.array_equal(z, oracle.adaln_modulate(bits(x), bits(sh), bits(sc), lib=lib))
+    x_out, _ = oracle.gated_residual_adaln(bits(x), bits(y), bits(g), bits(sh), bits(sc), lib=lib)
+    assert np.array_equal(x_out, (f64(x) + f64(g)[:, None, :] * f64(y)).numpy())  # exact in fp64
+
+
 # --------------------------------------------------------------------------- argument checks and threading
 
 def pin_rope_rejects_bad_bands(lib):

@@ -5,6 +5,7 @@ hand-written HIP kernels (``csrc/``; declarations in ``include/dit_ops.h``):
 
   dit_adaln_modulate      y = LayerNorm(x) * (1 + scale) + shift
   dit_gated_residual      out = x + gate * y
+  dit_gated_residual_adaln  the two fused: x_out = x + gate * y, z = AdaLN(x_out)
   dit_swiglu              out = silu(a) * b over [a | b] rows
   dit_qk_rmsnorm_rope3d   per-head RMSNorm of q and k, then 3D (t, h, w) RoPE
   dit_packed_positions    (t, h, w) coordinates of a packed token sequence
@@ -27,6 +28,7 @@ from ._binding import (  # noqa: F401
     dit_adaln_modulate,
     dit_copy16,
     dit_gated_residual,
+    dit_gated_residual_adaln,
     dit_packed_positions,
     dit_qk_rmsnorm_rope3d,
     dit_status_str,

@@ -28,6 +28,7 @@ SIGNATURES = {
     "dit_swiglu": ([_P, _P, _I64, _I64, _P], ctypes.c_int),
     "dit_qk_rmsnorm_rope3d": ([_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I32, _I32, _I32, _F32, _F32, _P],
                               ctypes.c_int),
+    "dit_gated_residual_adaln": ([_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _F32, _P], ctypes.c_int),
     "dit_packed_positions": ([_P, _I64, _I64, _I64, _I64, _P], ctypes.c_int),
     "dit_copy16": ([_P, _P, _I64, _P], ctypes.c_int),
 }
@@ -133,6 +134,25 @@ def dit_gated_residual(x, y, gate, out=None, stream=None):
         _check("dit_gated_residual", load_library().dit_gated_residual(
             x.data_ptr(), y.data_ptr(), gate.data_ptr(), out.data_ptr(), B, N, D, _stream(stream, dev)))
     return out
+
+
+def dit_gated_residual_adaln(x, y, gate, shift, scale, x_out=None, z=None, eps: float = 1e-6, stream=None):
+    """x_out = x + gate[b]*y (bf16); z = LayerNorm(x_out)*(1+scale[b]) + shift[b]. Returns (x_out, z)."""
+    _tensor(x, "x", ndim=3)
+    B, N, D = x.shape
+    _shape(_tensor(y, "y"), "y", (B, N, D))
+    for t, name in ((gate, "gate"), (shift, "shift"), (scale, "scale")):
+        _shape(_tensor(t, name), name, (B, D))
+    x_out = torch.empty_like(x) if x_out is None else x_out
+    z = torch.empty_like(x) if z is None else z
+    _shape(_tensor(x_out, "x_out"), "x_out", (B, N, D))
+    _shape(_tensor(z, "z"), "z", (B, N, D))
+    dev = _same_device(x, y, gate, shift, scale, x_out, z)
+    with torch.cuda.device(dev):
+        _check("dit_gated_residual_adaln", load_library().dit_gated_residual_adaln(
+            x.data_ptr(), y.data_ptr(), gate.data_ptr(), shift.data_ptr(), scale.data_ptr(), x_out.data_ptr(),
+            z.data_ptr(), B, N, D, float(eps), _stream(stream, dev)))
+    return x_out, z
 
 
 def dit_swiglu(inp, out=None, stream=None):

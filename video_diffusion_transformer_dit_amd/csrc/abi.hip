@@ -165,6 +165,37 @@ dit_status dit_qk_rmsnorm_rope3d(const dit_bf16 *q, const dit_bf16 *k, dit_bf16 
                                                   theta, eps, (hipStream_t)stream));
 }
 
+dit_status dit_gated_residual_adaln(const dit_bf16 *x, const dit_bf16 *y, const dit_bf16 *gate, const dit_bf16 *shift,
+                                    const dit_bf16 *scale, dit_bf16 *x_out, dit_bf16 *z, int64_t B, int64_t N,
+                                    int64_t D, float eps, void *stream)
+{
+    const int64_t rows = row_count(B, N);
+    if (rows < 0 || D < 0)
+        return DIT_ERR_ARG;
+    if (D < 8 || D % 8 != 0 || D > kMaxAdaLNWidth)
+        return DIT_ERR_SHAPE;
+    if (!(eps > 0.f) || !isfinite(eps))
+        return DIT_ERR_ARG;
+    if (rows == 0)
+        return DIT_OK;
+    if (!x || !y || !gate || !shift || !scale || !x_out || !z)
+        return DIT_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(y, 16) || !aligned(gate, 16) || !aligned(shift, 16) || !aligned(scale, 16) ||
+        !aligned(x_out, 16) || !aligned(z, 16))
+        return DIT_ERR_ALIGN;
+    const int64_t nx = rows * D * 2, nv = B * D * 2;
+    // x_out may be x exactly and z may be y exactly; nothing else may overlap.
+    if (bad_alias(x_out, x, nx) || overlap(x_out, nx, y, nx) || bad_alias(z, y, nx) || overlap(z, nx, x, nx) ||
+        overlap(z, nx, x_out, nx))
+        return DIT_ERR_ARG;
+    const void *vecs[3] = {gate, shift, scale};
+    for (const void *v : vecs)
+        if (overlap(x_out, nx, v, nv) || overlap(z, nx, v, nv))
+            return DIT_ERR_ARG;
+    return launched(
+        dit::launch_gated_residual_adaln(x, y, gate, shift, scale, x_out, z, rows, N, D, eps, (hipStream_t)stream));
+}
+
 dit_status dit_packed_positions(int32_t *pos, int64_t T, int64_t Hg, int64_t Wg, int64_t n_extra, void *stream)
 {
     if (T < 0 || Hg < 0 || Wg < 0 || n_extra < 0 || n_extra > kMaxRows)

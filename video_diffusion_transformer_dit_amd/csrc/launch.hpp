@@ -26,6 +26,11 @@ hipError_t launch_qk_rmsnorm_rope3d(const void *q, const void *k, void *q_out, v
                                     int d_t, int d_h, int d_w, float theta, float eps,
                                     hipStream_t stream);
 
+// x_out = x + gate[b] * y (bf16), z = LN(x_out) * (1 + scale[b]) + shift[b]; D % 8 == 0, D <= 8192.
+hipError_t launch_gated_residual_adaln(const void *x, const void *y, const void *gate, const void *shift,
+                                       const void *scale, void *x_out, void *z, int64_t rows, int64_t N, int64_t D,
+                                       float eps, hipStream_t stream);
+
 // Packed (t, h, w) coordinates of T*Hg*Wg video tokens then n_extra tokens.
 hipError_t launch_packed_positions(int32_t *pos, int64_t T, int64_t Hg, int64_t Wg, int64_t n_extra,
                                    hipStream_t stream);
