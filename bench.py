@@ -20,6 +20,8 @@ The printed JSON line reports:
   next_fused_residual_adaln
                  the gated residual fused with the AdaLN that follows it,
                  timed on its own after the chain (not part of `value`)
+  next_qk_layout QK read from a fused QKV buffer, written head-major, timed
+                 on its own after the chain (not part of `value`)
   cpu_baseline   the fp64 oracle on a bounded sample of the same workload,
                  on the host cores (and the GPU outputs of that sample checked
                  against it)
@@ -219,6 +221,33 @@ def main(argv=None) -> int:
              "unfused_ms": round(unfused_ms, 5), "unfused_bytes": nbytes["residual"] + nbytes["adaln"],
              "time_saved_pct": round(100.0 * (1.0 - fused_ms / unfused_ms), 1)}
 
+    # QK with the layouts around attention: q and k read straight out of a fused
+    # [B, N, 3*H*Dh] projection buffer, q' and k' written head-major [B, H, N, Dh].
+    HD = wl.H * wl.Dh
+    qkv = torch.empty((wl.B, wl.N, 3 * HD), dtype=torch.bfloat16, device=dev)
+    qkv[..., :HD].copy_(ins["q"].reshape(wl.B, wl.N, HD))
+    qkv[..., HD:2 * HD].copy_(ins["k"].reshape(wl.B, wl.N, HD))
+    qkv[..., 2 * HD:].zero_()
+    qo_hm = qo.view(wl.B, wl.H, wl.N, wl.Dh)
+    ko_hm = ko.view(wl.B, wl.H, wl.N, wl.Dh)
+    lev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for i in range(args.warmup + args.steps):
+        if i >= args.warmup:
+            lev[i - args.warmup][0].record(stream)
+        dit.dit_qk_rmsnorm_rope3d_layout(qkv, wl.H, wl.Dh, ins["wq"], ins["wk"], pos, wl.bands, head_major=True,
+                                         q_out=qo_hm, k_out=ko_hm, theta=wl.theta, eps=wl.eps, stream=stream)
+        if i >= args.warmup:
+            lev[i - args.warmup][1].record(stream)
+    torch.cuda.synchronize()
+    del qkv
+    layout_ms = sum(a.elapsed_time(b) for a, b in lev) / args.steps
+    layout = {"op": "dit_qk_rmsnorm_rope3d_layout (fused QKV in, head-major out)", "avg_ms": round(layout_ms, 5),
+              "bytes": nbytes["qk"], "GB_s": round(nbytes["qk"] / (layout_ms * 1e-3) / 1e9, 1),
+              "pct_of_peak": round(100.0 * nbytes["qk"] / (layout_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
+              "token_major_ms": ops["qk"]["avg_ms"],
+              "passes_avoided": "splitting q, k out of the QKV buffer and transposing q', k' to head-major: "
+                                "each a further read and write of q and k (2 x 4.1 GB here)"}
+
     # A plain streaming copy on the same device: the practical ceiling.
     cbytes = 2 << 30
     src = torch.empty(cbytes, dtype=torch.uint8, device=dev)
@@ -277,6 +306,7 @@ def main(argv=None) -> int:
         "copy_ceiling": copy_ceiling,
         "block_mix": block_mix,
         "next_fused_residual_adaln": fused,
+        "next_qk_layout": layout,
         "block_mix_fused": block_mix_fused,
     }
     if not args.no_cpu_baseline:

@@ -152,6 +152,39 @@ dit_status dit_qk_rmsnorm_rope3d(const dit_bf16 *q, const dit_bf16 *k,
                                  int32_t d_h, int32_t d_w, float theta,
                                  float eps, void *stream);
 
+/* Output layouts of dit_qk_rmsnorm_rope3d_layout. */
+#define DIT_QK_TOKEN_MAJOR 0 /* [B][N][H][Dh] */
+#define DIT_QK_HEAD_MAJOR 1  /* [B][H][N][Dh] */
+
+/*
+ * dit_qk_rmsnorm_rope3d with the memory layouts around it made explicit:
+ * q and k are read with a token stride, so they can be the q and k parts of a
+ * fused QKV projection [B][N][3][H][Dh] (q = qkv, k = qkv + H*Dh, stride
+ * 3*H*Dh) with no split pass, and q_out, k_out can be written head-major
+ * [B][H][N][Dh], the layout an attention kernel reads, with no transpose pass.
+ * The arithmetic is exactly that of dit_qk_rmsnorm_rope3d.
+ * Cited: the Sol-H3 abstract (its search covers memory layouts as well as
+ * kernel fusions); xhh.club Q&A for the operation itself.
+ *   q, k             token (b, n), head h, channel i at
+ *                    (b*N + n) * in_token_stride + h*Dh + i
+ *   in_token_stride  elements between consecutive tokens: a multiple of 8 and
+ *                    >= H*Dh (DIT_ERR_SHAPE otherwise)
+ *   out_layout       DIT_QK_TOKEN_MAJOR or DIT_QK_HEAD_MAJOR (else DIT_ERR_ARG)
+ *   q_out, k_out     [B][N][H][Dh] or [B][H][N][Dh]; in place (q_out == q,
+ *                    k_out == k) only when in_token_stride == H*Dh and the
+ *                    layout is token-major; any other overlap is rejected
+ * All other arguments and limits as for dit_qk_rmsnorm_rope3d.
+ */
+dit_status dit_qk_rmsnorm_rope3d_layout(const dit_bf16 *q, const dit_bf16 *k,
+                                        dit_bf16 *q_out, dit_bf16 *k_out,
+                                        const dit_bf16 *wq, const dit_bf16 *wk,
+                                        const int32_t *pos, int64_t B, int64_t N,
+                                        int64_t H, int64_t Dh,
+                                        int64_t in_token_stride,
+                                        int32_t out_layout, int32_t d_t,
+                                        int32_t d_h, int32_t d_w, float theta,
+                                        float eps, void *stream);
+
 /*
  * Gated residual fused with the AdaLN modulation that follows it:
  *   x_out = x + gate[b] * y                       (rounded once to bf16)

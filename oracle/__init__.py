@@ -73,6 +73,11 @@ def _bind(lib):
         _c_i64, _c_i64, _c_i64, _c_i64, _c_i32, _c_i32, _c_i32, _c_dbl, _c_dbl,
     ]
     lib.dit_oracle_qk_rmsnorm_rope3d.restype = ctypes.c_int
+    lib.dit_oracle_qk_rmsnorm_rope3d_layout.argtypes = [
+        _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p,
+        _c_i64, _c_i64, _c_i64, _c_i64, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _c_dbl, _c_dbl,
+    ]
+    lib.dit_oracle_qk_rmsnorm_rope3d_layout.restype = ctypes.c_int
     return lib
 
 
@@ -290,3 +295,27 @@ def qk_rmsnorm_rope3d(q, k, wq, wk, pos, bands, theta: float = 1e4, eps: float =
             jobs.append(job)
     _run(jobs, threads)
     return qo, ko
+
+
+def qk_rmsnorm_rope3d_layout(q, k, wq, wk, pos, bands, B, N, H, Dh, in_stride, out_layout,
+                             theta: float = 1e4, eps: float = 1e-6, lib=None):
+    """Strided q/k input (flat bf16 bits, token stride ``in_stride`` elements) -> (q', k') float64.
+
+    Output shape [B,N,H,Dh] for out_layout 0, [B,H,N,Dh] for out_layout 1.  ``q`` and ``k`` are flat
+    arrays that may be views into one buffer (e.g. q = qkv, k = qkv[H*Dh:]); their first element is
+    token 0's head 0.
+    """
+    lib = lib or load()
+    q, k, wq, wk = _bits(q), _bits(k), _bits(wq), _bits(wk)
+    pos = np.ascontiguousarray(pos, dtype=np.int32)
+    need = ((B * N - 1) * in_stride + H * Dh) if B * N else 0
+    assert q.size >= need and k.size >= need and pos.shape == (N, 3)
+    shape = (B, N, H, Dh) if out_layout == 0 else (B, H, N, Dh)
+    qo = np.empty(shape, dtype=np.float64)
+    ko = np.empty(shape, dtype=np.float64)
+    d_t, d_h, d_w = (int(b) for b in bands)
+    _check(lib.dit_oracle_qk_rmsnorm_rope3d_layout(
+        _ptr(q), _ptr(k), _ptr(wq), _ptr(wk), _ptr(pos), _ptr(qo), _ptr(ko), B, N, H, Dh, in_stride,
+        out_layout, d_t, d_h, d_w, theta, eps), "qk_rmsnorm_rope3d_layout")
+    return qo, ko
+

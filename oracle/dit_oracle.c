@@ -365,3 +365,67 @@ int dit_oracle_gated_residual_adaln(const uint16_t *x, const uint16_t *y,
     return status;
 }
 
+/*
+ * QK RMSNorm + 3D RoPE with the memory layouts of a fused QKV projection and
+ * of an attention kernel's input.
+ * Cited: the Sol-H3 abstract describes searching over memory layouts as well
+ * as fusions; the arithmetic is that of dit_oracle_qk_rmsnorm_rope3d.
+ * Layouts (element offsets):
+ *   input  q, k: token (b, n), head h, channel i at ((b*N + n) * in_stride + h*Dh + i),
+ *          in_stride >= H*Dh (3*H*Dh with q, k, v interleaved per token);
+ *   output out_layout 0: ((b*N + n) * H + h) * Dh + i      (token-major)
+ *          out_layout 1: ((b*H + h) * N + n) * Dh + i      (head-major).
+ */
+int dit_oracle_qk_rmsnorm_rope3d_layout(const uint16_t *q, const uint16_t *k,
+                                        const uint16_t *wq, const uint16_t *wk,
+                                        const int32_t *pos, double *q_out,
+                                        double *k_out, int64_t B, int64_t N,
+                                        int64_t H, int64_t Dh, int64_t in_stride,
+                                        int32_t out_layout, int32_t d_t,
+                                        int32_t d_h, int32_t d_w, double theta,
+                                        double eps)
+{
+    if (!q || !k || !wq || !wk || !pos || !q_out || !k_out || B < 0 || N < 0 ||
+        H <= 0 || Dh <= 0 || in_stride < H * Dh || (out_layout != 0 && out_layout != 1) ||
+        !(eps > 0) || !(theta > 0))
+        return ORACLE_BAD_ARG;
+    if ((d_t | d_h | d_w) & 1 || d_t < 0 || d_h < 0 || d_w < 0 ||
+        (int64_t)d_t + d_h + d_w != Dh)
+        return ORACLE_BAD_ARG;
+
+    double *w_q = malloc(sizeof(double) * (size_t)Dh);
+    double *w_k = malloc(sizeof(double) * (size_t)Dh);
+    double *v = malloc(sizeof(double) * (size_t)Dh);
+    double *u = malloc(sizeof(double) * (size_t)Dh);
+    if (!w_q || !w_k || !v || !u) {
+        free(w_q); free(w_k); free(v); free(u);
+        return ORACLE_BAD_ARG;
+    }
+    for (int64_t i = 0; i < Dh; ++i) {
+        w_q[i] = bf16_to_double(wq[i]);
+        w_k[i] = bf16_to_double(wk[i]);
+    }
+    int status = ORACLE_OK;
+    for (int64_t b = 0; b < B && status == ORACLE_OK; ++b)
+        for (int64_t n = 0; n < N && status == ORACLE_OK; ++n)
+            for (int64_t h = 0; h < H && status == ORACLE_OK; ++h) {
+                int64_t src = (b * N + n) * in_stride + h * Dh;
+                int64_t dst = out_layout == 0 ? ((b * N + n) * H + h) * Dh
+                                              : ((b * H + h) * N + n) * Dh;
+                for (int which = 0; which < 2 && status == ORACLE_OK; ++which) {
+                    const uint16_t *in = which == 0 ? q : k;
+                    double *out = which == 0 ? q_out : k_out;
+                    for (int64_t i = 0; i < Dh; ++i)
+                        v[i] = bf16_to_double(in[src + i]);
+                    status = dit_oracle_rmsnorm(v, which == 0 ? w_q : w_k, u, Dh, eps);
+                    if (status == ORACLE_OK)
+                        status = dit_oracle_rope3d(u, Dh, d_t, d_h, d_w, pos[3 * n],
+                                                   pos[3 * n + 1], pos[3 * n + 2], theta);
+                    for (int64_t i = 0; i < Dh && status == ORACLE_OK; ++i)
+                        out[dst + i] = u[i];
+                }
+            }
+    free(w_q); free(w_k); free(v); free(u);
+    return status;
+}
+

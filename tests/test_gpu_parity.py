@@ -292,6 +292,42 @@ def test_qk_shapes(B, N, H, Dh, bands):
     assert_close(ko, kr, f"k {B}x{N}x{H}x{Dh}")
 
 
+QK_LAYOUT_SHAPES = [(1, 33, 32, 128, (16, 56, 56), 3), (2, 17, 4, 64, (16, 24, 24), 3), (1, 9, 3, 256, (64, 96, 96), 2),
+                    (2, 7, 5, 16, (4, 6, 6), 4), (1, 5, 48, 128, (16, 56, 56), 3)]
+
+
+@pytest.mark.parametrize("B,N,H,Dh,bands,parts", QK_LAYOUT_SHAPES)
+@pytest.mark.parametrize("head_major", [True, False])
+def test_qk_layout_fused_qkv(B, N, H, Dh, bands, parts, head_major):
+    """q and k read out of a [B,N,parts*H*Dh] projection; outputs head- or token-major."""
+    qkv = randn_bf16((B, N, parts * H * Dh), seed=N * H + Dh + parts)
+    qkv[..., 2 * H * Dh:] = float("nan")  # anything past k (e.g. v) must not be read
+    wq, wk = weights(Dh, 141), weights(Dh, 142)
+    pos = random_positions(N, seed=N + 7)
+    qo, ko = dit.dit_qk_rmsnorm_rope3d_layout(qkv, H, Dh, wq, wk, pos.to(DEV), bands, head_major=head_major)
+    sync()
+    flat = bits(qkv).ravel()
+    qr, kr = oracle.qk_rmsnorm_rope3d_layout(flat, flat[H * Dh:], bits(wq), bits(wk), pos.numpy(), bands,
+                                             B, N, H, Dh, parts * H * Dh, 1 if head_major else 0)
+    assert_close(qo, qr, f"q layout {B}x{N}x{H}x{Dh} hm={head_major}")
+    assert_close(ko, kr, f"k layout {B}x{N}x{H}x{Dh} hm={head_major}")
+
+
+def test_qk_layout_plain_case_equals_qk():
+    B, N, H, Dh = 2, 65, 32, 128
+    q = randn_bf16((B, N, H, Dh), seed=151)
+    k = randn_bf16((B, N, H, Dh), seed=152)
+    wq, wk = weights(Dh, 153), weights(Dh, 154)
+    pos = random_positions(N, seed=155).to(DEV)
+    a = dit.dit_qk_rmsnorm_rope3d(q, k, wq, wk, pos, (16, 56, 56))
+    qkv = torch.cat([q.reshape(B, N, -1), k.reshape(B, N, -1)], dim=-1).contiguous()
+    b = dit.dit_qk_rmsnorm_rope3d_layout(qkv, H, Dh, wq, wk, pos, (16, 56, 56), head_major=False)
+    c = dit.dit_qk_rmsnorm_rope3d_layout(qkv, H, Dh, wq, wk, pos, (16, 56, 56), head_major=True)
+    sync()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+    assert torch.equal(a[0].transpose(1, 2), c[0]) and torch.equal(a[1].transpose(1, 2), c[1])
+
+
 def test_qk_heavy_tails_and_large_positions():
     B, N, H, Dh = 1, 64, 32, 128
     g = torch.Generator(device=DEV).manual_seed(81)
@@ -459,7 +495,26 @@ def test_full_workload_sampled(name):
                                           bits(ins["wq"]), bits(ins["wk"]), pos_ref[n:n + 1], wl.bands, wl.theta, wl.eps)
         assert_close(qof[r], qr[0, 0], f"{name} q row {r}")
         assert_close(kof[r], kr[0, 0], f"{name} k row {r}")
-    del ins, qo, ko
+    del qo, ko
+    # The same op on a fused QKV projection buffer with head-major outputs.
+    qkv = torch.cat([ins["q"].reshape(B, N, -1), ins["k"].reshape(B, N, -1),
+                     ins["q"].reshape(B, N, -1)], dim=-1)  # [q | k | a stand-in for v]
+    del ins["q"], ins["k"]
+    torch.cuda.empty_cache()
+    qo, ko = dit.dit_qk_rmsnorm_rope3d_layout(qkv, wl.H, wl.Dh, ins["wq"], ins["wk"], pos, wl.bands,
+                                              head_major=True, theta=wl.theta, eps=wl.eps)
+    sync()
+    assert torch.isfinite(qo).all() and torch.isfinite(ko).all()
+    S = qkv.shape[-1]
+    qkv_rows = qkv.reshape(R, S)
+    for r in rows[:24]:
+        b, n = divmod(r, N)
+        flat = bits(qkv_rows[r])
+        qr, kr = oracle.qk_rmsnorm_rope3d_layout(flat, flat[wl.H * wl.Dh:], bits(ins["wq"]), bits(ins["wk"]),
+                                                 pos_ref[n:n + 1], wl.bands, 1, 1, wl.H, wl.Dh, S, 1, wl.theta, wl.eps)
+        assert_close(qo[b, :, n], qr[0, :, 0], f"{name} q head-major row {r}")
+        assert_close(ko[b, :, n], kr[0, :, 0], f"{name} k head-major row {r}")
+    del ins, qo, ko, qkv, qkv_rows
     torch.cuda.empty_cache()
     # Rows of a sample are the same computation for every sample: the same
     # inputs give the same outputs wherever they sit in the batch.

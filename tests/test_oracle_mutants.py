@@ -74,6 +74,11 @@ MUTANTS = {
     "fused_normalises_input_x": ("stored[i] = dit_oracle_bf16_encode(x_out[i]);", "stored[i] = x[i];"),
     "fused_truncates_store": ("stored[i] = dit_oracle_bf16_encode(x_out[i]);",
                               "{ float f = (float)x_out[i]; uint32_t w; memcpy(&w, &f, 4); stored[i] = (uint16_t)(w >> 16); }"),
+    # QK memory layouts
+    "layout_head_major_wrong_order": ("                                              : ((b * H + h) * N + n) * Dh;",
+                                      "                                              : ((n * H + h) * B + b) * Dh;"),
+    "layout_ignores_stride": ("int64_t src = (b * N + n) * in_stride + h * Dh;", "int64_t src = (b * N + n) * H * Dh + h * Dh;"),
+    "layout_k_uses_q": ("const uint16_t *in = which == 0 ? q : k;", "const uint16_t *in = q;"),
     # bf16 decode
     "decode_wrong_shift": ("uint32_t word = (uint32_t)bits << 16;", "uint32_t word = (uint32_t)bits << 15;"),
 }

@@ -439,6 +439,60 @@ def pin_residual_adaln_is_the_pipeline(lib):
     assert np.array_equal(x_out, (f64(x) + f64(g)[:, None, :] * f64(y)).numpy())  # exact in fp64
 
 
+# --------------------------------------------------------------------------- QK with memory layouts
+
+def _qkv(B, N, H, Dh, seed, v_fill=None):
+    """A fused [B,N,3,H,Dh] projection buffer; v is filled with NaN bits to catch stray reads."""
+    qkv = rand_bf16((B, N, 3, H, Dh), seed=seed)
+    if v_fill is not None:
+        qkv[:, :, 2] = v_fill
+    return qkv
+
+
+def pin_qk_layout_plain_case_matches_qk(lib):
+    B, N, H, Dh = 2, 5, 3, 64
+    q = rand_bf16((B, N, H, Dh), seed=111)
+    k = rand_bf16((B, N, H, Dh), seed=112)
+    w1, w2 = _weights(Dh, 113), _weights(Dh, 114)
+    pos = np.array([[t, t % 3, 2 * t + 1] for t in range(N)], dtype=np.int32)
+    ref = oracle.qk_rmsnorm_rope3d(bits(q), bits(k), bits(w1), bits(w2), pos, BANDS, lib=lib)
+    got = oracle.qk_rmsnorm_rope3d_layout(bits(q).ravel(), bits(k).ravel(), bits(w1), bits(w2), pos, BANDS,
+                                          B, N, H, Dh, H * Dh, 0, lib=lib)
+    assert np.array_equal(got[0], ref[0]) and np.array_equal(got[1], ref[1])
+
+
+def pin_qk_layout_head_major_is_a_transpose(lib):
+    """Brute force over a tiny case: every (b, n, h) head lands at ((b*H + h)*N + n)."""
+    B, N, H, Dh = 2, 4, 3, 64
+    q = rand_bf16((B, N, H, Dh), seed=121)
+    k = rand_bf16((B, N, H, Dh), seed=122)
+    w1, w2 = _weights(Dh, 123), _weights(Dh, 124)
+    pos = np.array([[t, 2 * t, 3 * t] for t in range(N)], dtype=np.int32)
+    tm = oracle.qk_rmsnorm_rope3d_layout(bits(q).ravel(), bits(k).ravel(), bits(w1), bits(w2), pos, BANDS,
+                                         B, N, H, Dh, H * Dh, 0, lib=lib)
+    hm = oracle.qk_rmsnorm_rope3d_layout(bits(q).ravel(), bits(k).ravel(), bits(w1), bits(w2), pos, BANDS,
+                                         B, N, H, Dh, H * Dh, 1, lib=lib)
+    for b in range(B):
+        for n in range(N):
+            for h in range(H):
+                assert np.array_equal(hm[0][b, h, n], tm[0][b, n, h]) and np.array_equal(hm[1][b, h, n], tm[1][b, n, h])
+
+
+def pin_qk_layout_reads_q_and_k_from_a_fused_qkv_buffer(lib):
+    B, N, H, Dh = 2, 3, 2, 64
+    nan_bits = torch.tensor(0x7FC0, dtype=torch.int16).view(torch.bfloat16)
+    qkv = _qkv(B, N, H, Dh, seed=131, v_fill=nan_bits)
+    flat = bits(qkv).ravel()
+    w1, w2 = _weights(Dh, 132), _weights(Dh, 133)
+    pos = np.array([[1, 2, 3], [4, 5, 6], [7, 8, 9]], dtype=np.int32)
+    got = oracle.qk_rmsnorm_rope3d_layout(flat, flat[H * Dh:], bits(w1), bits(w2), pos, BANDS,
+                                          B, N, H, Dh, 3 * H * Dh, 1, lib=lib)
+    ref = oracle.qk_rmsnorm_rope3d(bits(qkv[:, :, 0].contiguous()), bits(qkv[:, :, 1].contiguous()),
+                                   bits(w1), bits(w2), pos, BANDS, lib=lib)
+    assert np.all(np.isfinite(got[0])) and np.all(np.isfinite(got[1]))
+    assert np.array_equal(got[0], ref[0].transpose(0, 2, 1, 3)) and np.array_equal(got[1], ref[1].transpose(0, 2, 1, 3))
+
+
 # --------------------------------------------------------------------------- argument checks and threading
 
 def pin_rope_rejects_bad_bands(lib):

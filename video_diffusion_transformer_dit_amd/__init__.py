@@ -8,6 +8,8 @@ hand-written HIP kernels (``csrc/``; declarations in ``include/dit_ops.h``):
   dit_gated_residual_adaln  the two fused: x_out = x + gate * y, z = AdaLN(x_out)
   dit_swiglu              out = silu(a) * b over [a | b] rows
   dit_qk_rmsnorm_rope3d   per-head RMSNorm of q and k, then 3D (t, h, w) RoPE
+  dit_qk_rmsnorm_rope3d_layout  the same, reading q/k from a fused QKV buffer and
+                          writing head-major outputs
   dit_packed_positions    (t, h, w) coordinates of a packed token sequence
   dit_copy16              plain 16-byte-vector copy (bandwidth ceiling)
 
@@ -21,6 +23,8 @@ from ._binding import (  # noqa: F401
     DIT_ERR_NULL,
     DIT_ERR_SHAPE,
     DIT_OK,
+    DIT_QK_HEAD_MAJOR,
+    DIT_QK_TOKEN_MAJOR,
     LIB_PATH,
     SIGNATURES,
     DitError,
@@ -31,6 +35,7 @@ from ._binding import (  # noqa: F401
     dit_gated_residual_adaln,
     dit_packed_positions,
     dit_qk_rmsnorm_rope3d,
+    dit_qk_rmsnorm_rope3d_layout,
     dit_status_str,
     dit_swiglu,
     load_library,

@@ -28,6 +28,8 @@ SIGNATURES = {
     "dit_swiglu": ([_P, _P, _I64, _I64, _P], ctypes.c_int),
     "dit_qk_rmsnorm_rope3d": ([_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I32, _I32, _I32, _F32, _F32, _P],
                               ctypes.c_int),
+    "dit_qk_rmsnorm_rope3d_layout": ([_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I32, _I32, _I32,
+                                      _I32, _F32, _F32, _P], ctypes.c_int),
     "dit_gated_residual_adaln": ([_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _F32, _P], ctypes.c_int),
     "dit_packed_positions": ([_P, _I64, _I64, _I64, _I64, _P], ctypes.c_int),
     "dit_copy16": ([_P, _P, _I64, _P], ctypes.c_int),
@@ -192,6 +194,40 @@ def dit_qk_rmsnorm_rope3d(q, k, wq, wk, pos, bands, q_out=None, k_out=None, thet
         _check("dit_qk_rmsnorm_rope3d", load_library().dit_qk_rmsnorm_rope3d(
             q.data_ptr(), k.data_ptr(), q_out.data_ptr(), k_out.data_ptr(), wq.data_ptr(), wk.data_ptr(),
             pos.data_ptr(), B, N, H, Dh, d_t, d_h, d_w, float(theta), float(eps), _stream(stream, dev)))
+    return q_out, k_out
+
+
+DIT_QK_TOKEN_MAJOR, DIT_QK_HEAD_MAJOR = 0, 1
+
+
+def dit_qk_rmsnorm_rope3d_layout(qkv, H: int, Dh: int, wq, wk, pos, bands, head_major: bool = True,
+                                 q_out=None, k_out=None, theta: float = 1e4, eps: float = 1e-6, stream=None):
+    """Per-head RMSNorm + 3D RoPE of the q and k parts of a fused projection ``qkv`` [B,N,S] whose last
+    dimension holds q at [0, H*Dh) and k at [H*Dh, 2*H*Dh) (S >= 2*H*Dh, e.g. 3*H*Dh with v after k).
+
+    Outputs are head-major [B,H,N,Dh] (or token-major [B,N,H,Dh] with ``head_major=False``).
+    Returns (q_out, k_out).
+    """
+    _tensor(qkv, "qkv", ndim=3)
+    B, N, S = qkv.shape
+    if S < 2 * H * Dh:
+        raise ValueError(f"qkv's last dimension {S} cannot hold q and k of {H}x{Dh}")
+    _shape(_tensor(wq, "wq"), "wq", (Dh,))
+    _shape(_tensor(wk, "wk"), "wk", (Dh,))
+    _shape(_tensor(pos, "pos", dtype=torch.int32), "pos", (N, 3))
+    shape = (B, H, N, Dh) if head_major else (B, N, H, Dh)
+    q_out = torch.empty(shape, dtype=qkv.dtype, device=qkv.device) if q_out is None else q_out
+    k_out = torch.empty(shape, dtype=qkv.dtype, device=qkv.device) if k_out is None else k_out
+    _shape(_tensor(q_out, "q_out"), "q_out", shape)
+    _shape(_tensor(k_out, "k_out"), "k_out", shape)
+    d_t, d_h, d_w = (int(b) for b in bands)
+    dev = _same_device(qkv, wq, wk, pos, q_out, k_out)
+    k_ptr = qkv.data_ptr() + H * Dh * qkv.element_size()
+    with torch.cuda.device(dev):
+        _check("dit_qk_rmsnorm_rope3d_layout", load_library().dit_qk_rmsnorm_rope3d_layout(
+            qkv.data_ptr(), k_ptr, q_out.data_ptr(), k_out.data_ptr(), wq.data_ptr(), wk.data_ptr(), pos.data_ptr(),
+            B, N, H, Dh, S, DIT_QK_HEAD_MAJOR if head_major else DIT_QK_TOKEN_MAJOR, d_t, d_h, d_w, float(theta),
+            float(eps), _stream(stream, dev)))
     return q_out, k_out
 
 

@@ -134,17 +134,20 @@ dit_status dit_swiglu(const dit_bf16 *in, dit_bf16 *out, int64_t M, int64_t F, v
     return launched(dit::launch_swiglu(in, out, M, F, (hipStream_t)stream));
 }
 
-dit_status dit_qk_rmsnorm_rope3d(const dit_bf16 *q, const dit_bf16 *k, dit_bf16 *q_out, dit_bf16 *k_out,
-                                 const dit_bf16 *wq, const dit_bf16 *wk, const int32_t *pos, int64_t B, int64_t N,
-                                 int64_t H, int64_t Dh, int32_t d_t, int32_t d_h, int32_t d_w, float theta, float eps,
-                                 void *stream)
+dit_status dit_qk_rmsnorm_rope3d_layout(const dit_bf16 *q, const dit_bf16 *k, dit_bf16 *q_out, dit_bf16 *k_out,
+                                        const dit_bf16 *wq, const dit_bf16 *wk, const int32_t *pos, int64_t B,
+                                        int64_t N, int64_t H, int64_t Dh, int64_t in_token_stride,
+                                        int32_t out_layout, int32_t d_t, int32_t d_h, int32_t d_w, float theta,
+                                        float eps, void *stream)
 {
     const int64_t rows = row_count(B, N);
-    if (rows < 0 || H < 0 || Dh < 0)
+    if (rows < 0 || H < 0 || Dh < 0 || in_token_stride < 0 || in_token_stride > kMaxWidth)
+        return DIT_ERR_ARG;
+    if (out_layout != DIT_QK_TOKEN_MAJOR && out_layout != DIT_QK_HEAD_MAJOR)
         return DIT_ERR_ARG;
     const bool dh_ok = Dh == 8 || Dh == 16 || Dh == 32 || Dh == 64 || Dh == 128 || Dh == 256;
     if (!dh_ok || H < 1 || H * Dh > kMaxHeadRow || d_t < 0 || d_h < 0 || d_w < 0 || (d_t | d_h | d_w) & 1 ||
-        (int64_t)d_t + d_h + d_w != Dh)
+        (int64_t)d_t + d_h + d_w != Dh || in_token_stride % 8 != 0 || in_token_stride < H * Dh)
         return DIT_ERR_SHAPE;
     if (!(eps > 0.f) || !isfinite(eps) || !(theta > 1.f) || !isfinite(theta))
         return DIT_ERR_ARG;
@@ -155,14 +158,35 @@ dit_status dit_qk_rmsnorm_rope3d(const dit_bf16 *q, const dit_bf16 *k, dit_bf16 
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(q_out, 16) || !aligned(k_out, 16) || !aligned(wq, 16) ||
         !aligned(wk, 16) || !aligned(pos, 4))
         return DIT_ERR_ALIGN;
-    const int64_t nt = rows * H * Dh * 2, nw = Dh * 2, np = N * 12;
-    if (bad_alias(q_out, q, nt) || overlap(q_out, nt, k, nt) || overlap(q_out, nt, wq, nw) ||
-        overlap(q_out, nt, wk, nw) || overlap(q_out, nt, pos, np) || bad_alias(k_out, k, nt) ||
-        overlap(k_out, nt, q, nt) || overlap(k_out, nt, wq, nw) || overlap(k_out, nt, wk, nw) ||
-        overlap(k_out, nt, pos, np) || overlap(k_out, nt, q_out, nt))
+    const int64_t nt = rows * H * Dh * 2;                          // bytes of each output
+    const int64_t ni = ((rows - 1) * in_token_stride + H * Dh) * 2; // byte extent of each input
+    const int64_t nw = Dh * 2, np = N * 12;
+    // In place (q_out == q, k_out == k) only where the layouts coincide.
+    const bool same_layout = in_token_stride == H * Dh && out_layout == DIT_QK_TOKEN_MAJOR;
+    const bool q_bad = same_layout ? bad_alias(q_out, q, nt) : overlap(q_out, nt, q, ni);
+    const bool k_bad = same_layout ? bad_alias(k_out, k, nt) : overlap(k_out, nt, k, ni);
+    if (q_bad || k_bad || overlap(q_out, nt, k, ni) || overlap(k_out, nt, q, ni) || overlap(k_out, nt, q_out, nt))
         return DIT_ERR_ARG;
-    return launched(dit::launch_qk_rmsnorm_rope3d(q, k, q_out, k_out, wq, wk, pos, rows, N, H, Dh, d_t, d_h, d_w,
-                                                  theta, eps, (hipStream_t)stream));
+    const void *small[3] = {wq, wk, pos};
+    const int64_t small_n[3] = {nw, nw, np};
+    for (int i = 0; i < 3; ++i)
+        if (overlap(q_out, nt, small[i], small_n[i]) || overlap(k_out, nt, small[i], small_n[i]))
+            return DIT_ERR_ARG;
+    return launched(dit::launch_qk_rmsnorm_rope3d(q, k, q_out, k_out, wq, wk, pos, rows, N, H, Dh, in_token_stride,
+                                                  out_layout == DIT_QK_HEAD_MAJOR, d_t, d_h, d_w, theta, eps,
+                                                  (hipStream_t)stream));
+}
+
+dit_status dit_qk_rmsnorm_rope3d(const dit_bf16 *q, const dit_bf16 *k, dit_bf16 *q_out, dit_bf16 *k_out,
+                                 const dit_bf16 *wq, const dit_bf16 *wk, const int32_t *pos, int64_t B, int64_t N,
+                                 int64_t H, int64_t Dh, int32_t d_t, int32_t d_h, int32_t d_w, float theta, float eps,
+                                 void *stream)
+{
+    // Token-major q and k in, token-major out: the layout entry point with the plain layout.
+    if (H < 0 || Dh < 0 || H > kMaxHeadRow || Dh > kMaxHeadRow)
+        return H < 0 || Dh < 0 ? DIT_ERR_ARG : DIT_ERR_SHAPE;
+    return dit_qk_rmsnorm_rope3d_layout(q, k, q_out, k_out, wq, wk, pos, B, N, H, Dh, H * Dh, DIT_QK_TOKEN_MAJOR, d_t,
+                                        d_h, d_w, theta, eps, stream);
 }
 
 dit_status dit_gated_residual_adaln(const dit_bf16 *x, const dit_bf16 *y, const dit_bf16 *gate, const dit_bf16 *shift,

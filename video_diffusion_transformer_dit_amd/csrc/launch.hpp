@@ -19,10 +19,13 @@ hipError_t launch_gated_residual(const void *x, const void *y, const void *gate,
 // out[r][j] = silu(in[r][j]) * in[r][F+j]; F % 8 == 0.
 hipError_t launch_swiglu(const void *in, void *out, int64_t M, int64_t F, hipStream_t stream);
 
-// Per-head RMSNorm + 3D RoPE of q and k; Dh in {8,...,256} (power of two).
+// Per-head RMSNorm + 3D RoPE of q and k; Dh in {8,...,256} (power of two).  Inputs have
+// in_token_stride elements (a multiple of 8, >= H*Dh) between consecutive tokens; outputs are
+// [B][N][H][Dh], or [B][H][N][Dh] when head_major.
 hipError_t launch_qk_rmsnorm_rope3d(const void *q, const void *k, void *q_out, void *k_out,
                                     const void *wq, const void *wk, const int32_t *pos,
                                     int64_t rows, int64_t N, int64_t H, int64_t Dh,
+                                    int64_t in_token_stride, bool head_major,
                                     int d_t, int d_h, int d_w, float theta, float eps,
                                     hipStream_t stream);
 

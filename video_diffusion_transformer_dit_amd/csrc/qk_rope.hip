@@ -71,19 +71,30 @@ __device__ __forceinline__ u32x4 norm_rotate(u32x4 raw, const float w[8], const 
 }
 
 // LPH = Dh/8 lanes per head.  half_parts = workgroups per q (or k) row.
-template <int LPH>
+// in_stride = vectors from one token's q (or k) to the next token's.
+// HEAD_MAJOR: outputs [B][H][N][Dh] instead of [B][N][H][Dh].
+template <int LPH, bool HEAD_MAJOR>
 __global__ __launch_bounds__(kQKThreads) void qk_rmsnorm_rope3d_kernel(
     const u32x4 *q, const u32x4 *k, u32x4 *q_out, u32x4 *k_out, const u32x4 *__restrict__ wq,
-    const u32x4 *__restrict__ wk, const int32_t *__restrict__ pos, int N, int B, int VPR, int half_parts,
-    float inv_dh, float eps, const RotaryPlan plan)
+    const u32x4 *__restrict__ wk, const int32_t *__restrict__ pos, int N, int B, int H, int VPR, int64_t in_stride,
+    int half_parts, float inv_dh, float eps, const RotaryPlan plan)
 {
     __shared__ float2 rot[4 * LPH]; // (cos, sin) of each channel pair of a head
     const int tid = threadIdx.x;
     const unsigned row = blockIdx.x;
     const int which = (int)blockIdx.y >= half_parts; // 0: q, 1: k
     const int c = ((int)blockIdx.y - which * half_parts) * kQKThreads + tid;
-    const size_t at = (size_t)row * VPR + c;
     const bool valid = c < VPR;
+    const int n = B == 1 ? (int)row : (int)(row % (unsigned)N);
+    const size_t src = (size_t)row * in_stride + c;
+    size_t dst;
+    if constexpr (HEAD_MAJOR) {
+        const int b = B == 1 ? 0 : (int)(row / (unsigned)N);
+        const int h = c / LPH; // LPH is a power of two
+        dst = ((size_t)(b * H + h) * N + n) * LPH + (c % LPH);
+    } else {
+        dst = (size_t)row * VPR + c;
+    }
 
     // The lane's weights and the pair's rotary plan entry are read before the
     // row, so that waiting for them leaves the row load in flight (vector
@@ -98,13 +109,12 @@ __global__ __launch_bounds__(kQKThreads) void qk_rmsnorm_rope3d_kernel(
     }
     // Unconditional load (lanes past the row read the row's first vector and
     // then zero it), so no branch forces a full wait on the plan load above.
-    u32x4 raw = load_stream((which ? k : q) + (valid ? at : (size_t)row * VPR));
+    u32x4 raw = load_stream((which ? k : q) + (valid ? src : (size_t)row * in_stride));
     if (!valid)
         raw = u32x4{0u, 0u, 0u, 0u};
 
     // The token's coordinates are the same for the whole workgroup: three
     // scalar loads, then a per-lane select of the pair's axis.
-    const int n = B == 1 ? (int)row : (int)(row % (unsigned)N);
     const int32_t *p = pos + 3 * (size_t)n;
     const int p_t = p[0], p_h = p[1], p_w = p[2];
     if (tid < 4 * LPH) {
@@ -127,18 +137,22 @@ __global__ __launch_bounds__(kQKThreads) void qk_rmsnorm_rope3d_kernel(
     // a multiple of LPH, so every DPP group is wholly in or wholly out.
     const u32x4 o = norm_rotate<LPH>(raw, w, cs, sn, inv_dh, eps);
     if (valid)
-        store_stream((which ? k_out : q_out) + at, o);
+        store_stream((which ? k_out : q_out) + dst, o);
 }
 
 template <int LPH>
 hipError_t launch_lph(const u32x4 *q, const u32x4 *k, u32x4 *qo, u32x4 *ko, const u32x4 *wq, const u32x4 *wk,
-                      const int32_t *pos, int rows, int N, int VPR, float inv_dh, float eps, const RotaryPlan &plan,
-                      hipStream_t stream)
+                      const int32_t *pos, int rows, int N, int H, int VPR, int64_t in_stride, bool head_major,
+                      float inv_dh, float eps, const RotaryPlan &plan, hipStream_t stream)
 {
     const int half_parts = (VPR + kQKThreads - 1) / kQKThreads;
     const dim3 grid((unsigned)rows, (unsigned)(2 * half_parts)), block(kQKThreads);
-    hipLaunchKernelGGL((qk_rmsnorm_rope3d_kernel<LPH>), grid, block, 0, stream, q, k, qo, ko, wq, wk, pos, N,
-                       rows / N, VPR, half_parts, inv_dh, eps, plan);
+    if (head_major)
+        hipLaunchKernelGGL((qk_rmsnorm_rope3d_kernel<LPH, true>), grid, block, 0, stream, q, k, qo, ko, wq, wk, pos,
+                           N, rows / N, H, VPR, in_stride, half_parts, inv_dh, eps, plan);
+    else
+        hipLaunchKernelGGL((qk_rmsnorm_rope3d_kernel<LPH, false>), grid, block, 0, stream, q, k, qo, ko, wq, wk, pos,
+                           N, rows / N, H, VPR, in_stride, half_parts, inv_dh, eps, plan);
     return hipGetLastError();
 }
 
@@ -146,7 +160,8 @@ hipError_t launch_lph(const u32x4 *q, const u32x4 *k, u32x4 *qo, u32x4 *ko, cons
 
 hipError_t launch_qk_rmsnorm_rope3d(const void *q, const void *k, void *q_out, void *k_out, const void *wq,
                                     const void *wk, const int32_t *pos, int64_t rows, int64_t N, int64_t H,
-                                    int64_t Dh, int d_t, int d_h, int d_w, float theta, float eps, hipStream_t stream)
+                                    int64_t Dh, int64_t in_token_stride, bool head_major, int d_t, int d_h, int d_w,
+                                    float theta, float eps, hipStream_t stream)
 {
     const auto *qv = static_cast<const u32x4 *>(q);
     const auto *kv = static_cast<const u32x4 *>(k);
@@ -155,8 +170,9 @@ hipError_t launch_qk_rmsnorm_rope3d(const void *q, const void *k, void *q_out, v
     const auto *wqv = static_cast<const u32x4 *>(wq);
     const auto *wkv = static_cast<const u32x4 *>(wk);
     const int VPR = (int)(H * Dh / 8);
+    const int64_t in_stride = in_token_stride / 8;
     const float inv_dh = 1.f / (float)Dh;
-    const int r = (int)rows, n = (int)N;
+    const int r = (int)rows, n = (int)N, h = (int)H;
 
     RotaryPlan plan = {};
     const double log2_theta = log2((double)theta);
@@ -173,15 +189,17 @@ hipError_t launch_qk_rmsnorm_rope3d(const void *q, const void *k, void *q_out, v
         plan.axis[i] = axis;
         plan.turns_per_unit[i] = exp2(-(double)(ch - lo) / (double)width * log2_theta) / (2.0 * M_PI);
     }
+#define DIT_QK_LAUNCH(L) launch_lph<L>(qv, kv, qo, ko, wqv, wkv, pos, r, n, h, VPR, in_stride, head_major, inv_dh, eps, plan, stream)
     switch (Dh) {
-    case 8: return launch_lph<1>(qv, kv, qo, ko, wqv, wkv, pos, r, n, VPR, inv_dh, eps, plan, stream);
-    case 16: return launch_lph<2>(qv, kv, qo, ko, wqv, wkv, pos, r, n, VPR, inv_dh, eps, plan, stream);
-    case 32: return launch_lph<4>(qv, kv, qo, ko, wqv, wkv, pos, r, n, VPR, inv_dh, eps, plan, stream);
-    case 64: return launch_lph<8>(qv, kv, qo, ko, wqv, wkv, pos, r, n, VPR, inv_dh, eps, plan, stream);
-    case 128: return launch_lph<16>(qv, kv, qo, ko, wqv, wkv, pos, r, n, VPR, inv_dh, eps, plan, stream);
-    case 256: return launch_lph<32>(qv, kv, qo, ko, wqv, wkv, pos, r, n, VPR, inv_dh, eps, plan, stream);
+    case 8: return DIT_QK_LAUNCH(1);
+    case 16: return DIT_QK_LAUNCH(2);
+    case 32: return DIT_QK_LAUNCH(4);
+    case 64: return DIT_QK_LAUNCH(8);
+    case 128: return DIT_QK_LAUNCH(16);
+    case 256: return DIT_QK_LAUNCH(32);
     default: return hipErrorInvalidValue;
     }
+#undef DIT_QK_LAUNCH
 }
 
 } // namespace dit
