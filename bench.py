@@ -22,6 +22,9 @@ The printed JSON line reports:
                  timed on its own after the chain (not part of `value`)
   next_qk_layout QK read from a fused QKV buffer, written head-major, timed
                  on its own after the chain (not part of `value`)
+  next_residual_change
+                 the Cache-DiT residual-change statistic over the sequence,
+                 timed on its own after the chain (not part of `value`)
   cpu_baseline   the fp64 oracle on a bounded sample of the same workload,
                  on the host cores (and the GPU outputs of that sample checked
                  against it)
@@ -248,6 +251,25 @@ def main(argv=None) -> int:
               "passes_avoided": "splitting q, k out of the QKV buffer and transposing q', k' to head-major: "
                                 "each a further read and write of q and k (2 x 4.1 GB here)"}
 
+    # Cache-DiT residual-change statistic over the packed sequence (the two
+    # residual inputs stand in for the current and cached boundary residuals).
+    change_bytes = 2 * wl.R * wl.D * 2
+    change_out = torch.empty((wl.B, 3), dtype=torch.float64, device=dev)
+    change_ws = torch.empty(max(16, dit.dit_residual_change_workspace_bytes(wl.B, wl.N, wl.D)), dtype=torch.uint8,
+                            device=dev)
+    cev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for i in range(args.warmup + args.steps):
+        if i >= args.warmup:
+            cev[i - args.warmup][0].record(stream)
+        dit.dit_residual_change(ins["res_x"], ins["res_y"], out=change_out, workspace=change_ws, stream=stream)
+        if i >= args.warmup:
+            cev[i - args.warmup][1].record(stream)
+    torch.cuda.synchronize()
+    change_ms = sum(a.elapsed_time(b) for a, b in cev) / args.steps
+    change = {"op": "dit_residual_change (two launches: partials, fixed-order reduce)", "avg_ms": round(change_ms, 5),
+              "bytes": change_bytes, "GB_s": round(change_bytes / (change_ms * 1e-3) / 1e9, 1),
+              "pct_of_peak": round(100.0 * change_bytes / (change_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2)}
+
     # A plain streaming copy on the same device: the practical ceiling.
     cbytes = 2 << 30
     src = torch.empty(cbytes, dtype=torch.uint8, device=dev)
@@ -307,6 +329,7 @@ def main(argv=None) -> int:
         "block_mix": block_mix,
         "next_fused_residual_adaln": fused,
         "next_qk_layout": layout,
+        "next_residual_change": change,
         "block_mix_fused": block_mix_fused,
     }
     if not args.no_cpu_baseline:

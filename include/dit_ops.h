@@ -212,6 +212,42 @@ dit_status dit_gated_residual_adaln(const dit_bf16 *x, const dit_bf16 *y,
                                     int64_t D, float eps, void *stream);
 
 /*
+ * Cache-DiT residual-change statistic, per sample b over every token (video
+ * and audio alike) and channel of the packed sequence:
+ *   out[3b + 0] = sum |r - r_cached|
+ *   out[3b + 1] = sum |r_cached|
+ *   out[3b + 2] = out[3b] / out[3b + 1]   (0 if both sums are 0, +inf if only
+ *                                          the second is)
+ * Cited: xhh.club summary, Q&A on Cache-DiT (after warm-up, boundary blocks'
+ * normalised residual change against the cached state decides whether the
+ * middle blocks are reused); stamatios.com summary, "Resultado principal"
+ * (one joint decision for the packed video+audio stack).  Reading: the
+ * normalised change is this relative L1 distance; the threshold and the
+ * reuse policy are the caller's.
+ *   r, r_cached   [B][N][D] bf16
+ *   out           [B][3] double, device memory, 8-byte aligned
+ *   workspace     device scratch owned by the caller, 16-byte aligned, at
+ *                 least dit_residual_change_workspace_bytes(B, N, D) bytes
+ *                 (DIT_ERR_ARG if smaller); its contents on entry do not
+ *                 matter and on return are unspecified
+ *   D             multiple of 8; B <= 65535
+ * Sums are fp32 over each 8-value vector and fp64 above, in a fixed order:
+ * repeated calls give bit-identical results.  B == 0 is a no-op; N == 0
+ * writes zeros.  No buffer may overlap another (DIT_ERR_ARG).
+ */
+dit_status dit_residual_change(const dit_bf16 *r, const dit_bf16 *r_cached,
+                               double *out, void *workspace,
+                               int64_t workspace_bytes, int64_t B, int64_t N,
+                               int64_t D, void *stream);
+
+/*
+ * Bytes of workspace dit_residual_change needs for these sizes (16 bytes per
+ * 1024 16-byte vectors of each sample, rounded up), or -1 if the sizes are
+ * invalid.  Host-only; makes no HIP call.
+ */
+int64_t dit_residual_change_workspace_bytes(int64_t B, int64_t N, int64_t D);
+
+/*
  * Packed token coordinates for the 3D rotary embedding.
  * Cited: stamatios.com summary, "Resultado principal" (video and audio tokens
  * in one packed DiT sequence); xhh.club Q&A ("3D RoPE").

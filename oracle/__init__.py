@@ -78,6 +78,8 @@ def _bind(lib):
         _c_i64, _c_i64, _c_i64, _c_i64, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _c_dbl, _c_dbl,
     ]
     lib.dit_oracle_qk_rmsnorm_rope3d_layout.restype = ctypes.c_int
+    lib.dit_oracle_residual_change.argtypes = [_c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64]
+    lib.dit_oracle_residual_change.restype = ctypes.c_int
     return lib
 
 
@@ -318,4 +320,15 @@ def qk_rmsnorm_rope3d_layout(q, k, wq, wk, pos, bands, B, N, H, Dh, in_stride, o
         _ptr(q), _ptr(k), _ptr(wq), _ptr(wk), _ptr(pos), _ptr(qo), _ptr(ko), B, N, H, Dh, in_stride,
         out_layout, d_t, d_h, d_w, theta, eps), "qk_rmsnorm_rope3d_layout")
     return qo, ko
+
+
+def residual_change(r, r_cached, lib=None) -> np.ndarray:
+    """r, r_cached [B,N,D] (bf16 bits) -> [B,3] float64: (sum |r-rc|, sum |rc|, ratio) per sample."""
+    lib = lib or load()
+    r, r_cached = _bits(r), _bits(r_cached)
+    B, N, D = r.shape
+    assert r_cached.shape == r.shape
+    out = np.empty((B, 3), dtype=np.float64)
+    _check(lib.dit_oracle_residual_change(_ptr(r), _ptr(r_cached), _ptr(out), B, N, D), "residual_change")
+    return out
 

@@ -429,3 +429,36 @@ int dit_oracle_qk_rmsnorm_rope3d_layout(const uint16_t *q, const uint16_t *k,
     return status;
 }
 
+/*
+ * Cache-DiT residual-change statistic.
+ * Cited: "8×H200 上的 MiniMax-H3…" (xhh.club), Q&A on how Cache-DiT reuses
+ * computation: after warm-up steps the boundary blocks are evaluated and their
+ * normalised residual change against the cached state decides reuse; and
+ * "SGLang acelera vídeo do MiniMax-H3…" (stamatios.com), "Resultado
+ * principal": the packed video+audio stack gets one joint decision.
+ * Reading: the normalised change is the relative L1 distance over every
+ * token (video and audio alike) and channel of a sample:
+ *   num_b = sum |r - r_cached|,  den_b = sum |r_cached|,  ratio_b = num_b / den_b
+ * with ratio 0 when both sums are 0 and +inf when only den is 0.
+ * r, r_cached: [B][N][D]; out: [B][3] = (num, den, ratio).
+ */
+int dit_oracle_residual_change(const uint16_t *r, const uint16_t *r_cached,
+                               double *out, int64_t B, int64_t N, int64_t D)
+{
+    if (!r || !r_cached || !out || B < 0 || N < 0 || D <= 0)
+        return ORACLE_BAD_ARG;
+    for (int64_t b = 0; b < B; ++b) {
+        double num = 0.0, den = 0.0;
+        for (int64_t i = 0; i < N * D; ++i) {
+            double a = bf16_to_double(r[b * N * D + i]);
+            double c = bf16_to_double(r_cached[b * N * D + i]);
+            num += fabs(a - c);
+            den += fabs(c);
+        }
+        out[3 * b + 0] = num;
+        out[3 * b + 1] = den;
+        out[3 * b + 2] = den > 0.0 ? num / den : (num > 0.0 ? INFINITY : 0.0);
+    }
+    return ORACLE_OK;
+}
+

@@ -190,6 +190,28 @@ def test_qk_layout_validation(lib):
     assert f(q=0, k=0, qo=0, ko=0, wq=0, wk=0, pos=0, N=0) == DIT_OK
 
 
+def test_residual_change_validation(lib):
+    ws = lib.dit_residual_change_workspace_bytes
+    assert ws(1, 124992, 4096) == 16 * ((124992 * 512 + 1023) // 1024)
+    assert ws(2, 3, 8) == 2 * 16
+    assert ws(1, 0, 8) == 0
+    assert ws(-1, 4, 8) == -1 and ws(1, 4, 12) == -1 and ws(70000, 4, 8) == -1
+
+    def f(r=P, rc=Q, out=R, w=S, wb=1 << 20, B=1, N=4, D=4096):
+        return lib.dit_residual_change(r, rc, out, w, wb, B, N, D, None)
+
+    assert f(B=-1) == DIT_ERR_ARG
+    assert f(D=12) == DIT_ERR_SHAPE
+    assert f(wb=0) == DIT_ERR_ARG  # workspace too small
+    assert f(out=0) == DIT_ERR_NULL
+    assert f(w=0) == DIT_ERR_NULL
+    assert f(out=R + 4) == DIT_ERR_ALIGN
+    assert f(w=S + 8) == DIT_ERR_ALIGN
+    assert f(out=P + 64) == DIT_ERR_ARG  # output inside r
+    assert f(w=Q) == DIT_ERR_ARG  # workspace over r_cached
+    assert f(r=0, rc=0, out=0, w=0, B=0) == DIT_OK
+
+
 def test_positions_validation(lib):
     f = lib.dit_packed_positions
     assert f(P, -1, 4, 4, 0, None) == DIT_ERR_ARG

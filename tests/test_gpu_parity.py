@@ -5,6 +5,8 @@ workloads (the shapes the benchmark launches, through the same entry points)
 on sampled rows that the oracle recomputes one by one, plus properties that
 hold at any size.  Positions (integer work) must match bit for bit.
 """
+import math
+
 import numpy as np
 import pytest
 import torch
@@ -218,6 +220,59 @@ def test_gated_residual_adaln_rounding_ties():
     assert torch.all(x_out[0, 0, 0::2] == 1.0) and torch.all(x_out[0, 1, 0::2] == 1.0 + 2.0 ** -6)
     xr, zr = oracle.gated_residual_adaln(bits(x), bits(y), bits(g), bits(sh), bits(sc))
     assert_close(z, zr, "fused z at rounding ties")
+
+
+# --------------------------------------------------------------------------- Cache-DiT residual change
+
+CHANGE_RTOL = 2e-6  # fp32 over 8 values per vector, fp64 above: relative error below 8 * 2^-24
+
+
+def check_change(got, ref, what):
+    got = got.cpu().numpy()
+    assert got.shape == ref.shape, what
+    for b in range(ref.shape[0]):
+        for j in range(3):
+            g, r = float(got[b, j]), float(ref[b, j])
+            if math.isinf(r) or r == 0.0:
+                assert g == r, (what, b, j, g, r)
+            else:
+                assert abs(g - r) <= CHANGE_RTOL * abs(r), (what, b, j, g, r, abs(g - r) / abs(r))
+
+
+@pytest.mark.parametrize("B,N,D", [(1, 33, 4096), (2, 1953, 4096), (3, 5, 264), (1, 1, 8), (2, 257, 1000)])
+def test_residual_change_shapes(B, N, D):
+    r = randn_bf16((B, N, D), seed=B + N + D)
+    rc = randn_bf16((B, N, D), seed=B + N + D + 1, scale=0.9)
+    out = dit.dit_residual_change(r, rc)
+    sync()
+    check_change(out, oracle.residual_change(bits(r), bits(rc)), f"change {B}x{N}x{D}")
+
+
+def test_residual_change_special_cases():
+    rc = randn_bf16((2, 300, 4096), seed=171)
+    zero = torch.zeros_like(rc)
+    same = dit.dit_residual_change(rc, rc)
+    double = dit.dit_residual_change((rc.float() * 2).to(torch.bfloat16), rc)
+    from_zero = dit.dit_residual_change(rc, zero)
+    both_zero = dit.dit_residual_change(zero, zero)
+    empty = dit.dit_residual_change(rc[:, :0], rc[:, :0])
+    sync()
+    assert torch.all(same[:, 0] == 0) and torch.all(same[:, 2] == 0)
+    assert torch.all(double[:, 2] == 1.0)  # |2c - c| and |c| take the same fp32 sums
+    assert torch.all(torch.isinf(from_zero[:, 2])) and torch.all(both_zero == 0) and torch.all(empty == 0)
+
+
+def test_residual_change_deterministic_and_workspace_reuse():
+    r = randn_bf16((2, 5000, 4096), seed=181)
+    rc = randn_bf16((2, 5000, 4096), seed=182)
+    ws = torch.empty(dit.dit_residual_change_workspace_bytes(2, 5000, 4096), dtype=torch.uint8, device=DEV)
+    ws.fill_(0xFF)  # stale contents must not matter
+    a = dit.dit_residual_change(r, rc, workspace=ws)
+    b = dit.dit_residual_change(r, rc, workspace=ws)
+    c = dit.dit_residual_change(r[:1, :17], rc[:1, :17], workspace=ws)
+    sync()
+    assert torch.equal(a, b)
+    check_change(c, oracle.residual_change(bits(r[:1, :17]), bits(rc[:1, :17])), "smaller call after larger")
 
 
 # --------------------------------------------------------------------------- SwiGLU
@@ -454,6 +509,14 @@ def test_full_workload_sampled(name):
                                     bits(row_of(ins["res_y"], r)).reshape(1, 1, -1), bits(ins["gate"][b:b + 1]))
         assert_close(row_of(out, r), ref.reshape(-1), f"{name} residual row {r}")
     del ins, out
+
+    # Cache-DiT residual change over the whole packed sequence (the residual
+    # inputs stand in for the current and cached boundary residuals)
+    ins = si.make_inputs(wl, device=DEV, names=("res_x", "res_y"))
+    stat = dit.dit_residual_change(ins["res_x"], ins["res_y"])
+    sync()
+    check_change(stat, oracle.residual_change(bits(ins["res_x"]), bits(ins["res_y"])), f"{name} residual change")
+    del ins, stat
 
     # fused gated residual + AdaLN (residual inputs, AdaLN vectors)
     ins = si.make_inputs(wl, device=DEV, names=("res_x", "res_y", "gate", "shift", "scale"))

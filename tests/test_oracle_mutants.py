@@ -79,6 +79,11 @@ MUTANTS = {
                                       "                                              : ((n * H + h) * B + b) * Dh;"),
     "layout_ignores_stride": ("int64_t src = (b * N + n) * in_stride + h * Dh;", "int64_t src = (b * N + n) * H * Dh + h * Dh;"),
     "layout_k_uses_q": ("const uint16_t *in = which == 0 ? q : k;", "const uint16_t *in = q;"),
+    # Cache-DiT residual change
+    "change_den_of_r": ("den += fabs(c);", "den += fabs(a);"),
+    "change_signed_difference": ("num += fabs(a - c);", "num += a - c;"),
+    "change_sample_zero": ("double a = bf16_to_double(r[b * N * D + i]);", "double a = bf16_to_double(r[i]);"),
+    "change_zero_den_ratio": ("(num > 0.0 ? INFINITY : 0.0)", "0.0"),
     # bf16 decode
     "decode_wrong_shift": ("uint32_t word = (uint32_t)bits << 16;", "uint32_t word = (uint32_t)bits << 15;"),
 }

@@ -493,6 +493,35 @@ def pin_qk_layout_reads_q_and_k_from_a_fused_qkv_buffer(lib):
     assert np.array_equal(got[0], ref[0].transpose(0, 2, 1, 3)) and np.array_equal(got[1], ref[1].transpose(0, 2, 1, 3))
 
 
+# --------------------------------------------------------------------------- Cache-DiT residual change
+
+def pin_residual_change_hand_cases(lib):
+    for case in cases("residual_change_hand.txt"):
+        D = len(case["r"])
+        r = b16([evaluate(v) for v in case["r"]], (1, 1, D))
+        rc = b16([evaluate(v) for v in case["rc"]], (1, 1, D))
+        out = oracle.residual_change(r, rc, lib=lib)[0]
+        expect = [evaluate(case["num"][0]), evaluate(case["den"][0]), evaluate(case["ratio"][0])]
+        assert out[0] == expect[0] and out[1] == expect[1], (case, out)
+        assert out[2] == expect[2] or math.isclose(out[2], expect[2], rel_tol=1e-15), (case, out)
+
+
+def pin_residual_change_matches_library_per_sample(lib):
+    B, N, D = 3, 7, 40
+    r = rand_bf16((B, N, D), seed=161)
+    rc = rand_bf16((B, N, D), seed=162, scale=2.0)
+    out = oracle.residual_change(bits(r), bits(rc), lib=lib)
+    num = (f64(r) - f64(rc)).abs().sum(dim=(1, 2))
+    den = f64(rc).abs().sum(dim=(1, 2))
+    assert np.allclose(out[:, 0], num.numpy(), rtol=1e-14) and np.allclose(out[:, 1], den.numpy(), rtol=1e-14)
+    assert np.allclose(out[:, 2], (num / den).numpy(), rtol=1e-14)
+    # samples are separate: changing sample 1 leaves samples 0 and 2 alone
+    r2 = r.clone()
+    r2[1] += 1.0
+    out2 = oracle.residual_change(bits(r2), bits(rc), lib=lib)
+    assert np.array_equal(out2[[0, 2]], out[[0, 2]]) and out2[1, 0] != out[1, 0]
+
+
 # --------------------------------------------------------------------------- argument checks and threading
 
 def pin_rope_rejects_bad_bands(lib):

@@ -10,6 +10,7 @@ hand-written HIP kernels (``csrc/``; declarations in ``include/dit_ops.h``):
   dit_qk_rmsnorm_rope3d   per-head RMSNorm of q and k, then 3D (t, h, w) RoPE
   dit_qk_rmsnorm_rope3d_layout  the same, reading q/k from a fused QKV buffer and
                           writing head-major outputs
+  dit_residual_change     Cache-DiT statistic: sum |r - r_cached| / sum |r_cached| per sample
   dit_packed_positions    (t, h, w) coordinates of a packed token sequence
   dit_copy16              plain 16-byte-vector copy (bandwidth ceiling)
 
@@ -36,6 +37,8 @@ from ._binding import (  # noqa: F401
     dit_packed_positions,
     dit_qk_rmsnorm_rope3d,
     dit_qk_rmsnorm_rope3d_layout,
+    dit_residual_change,
+    dit_residual_change_workspace_bytes,
     dit_status_str,
     dit_swiglu,
     load_library,

@@ -31,6 +31,8 @@ SIGNATURES = {
     "dit_qk_rmsnorm_rope3d_layout": ([_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I32, _I32, _I32,
                                       _I32, _F32, _F32, _P], ctypes.c_int),
     "dit_gated_residual_adaln": ([_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _F32, _P], ctypes.c_int),
+    "dit_residual_change": ([_P, _P, _P, _P, _I64, _I64, _I64, _I64, _P], ctypes.c_int),
+    "dit_residual_change_workspace_bytes": ([_I64, _I64, _I64], ctypes.c_int64),
     "dit_packed_positions": ([_P, _I64, _I64, _I64, _I64, _P], ctypes.c_int),
     "dit_copy16": ([_P, _P, _I64, _P], ctypes.c_int),
 }
@@ -229,6 +231,36 @@ def dit_qk_rmsnorm_rope3d_layout(qkv, H: int, Dh: int, wq, wk, pos, bands, head_
             B, N, H, Dh, S, DIT_QK_HEAD_MAJOR if head_major else DIT_QK_TOKEN_MAJOR, d_t, d_h, d_w, float(theta),
             float(eps), _stream(stream, dev)))
     return q_out, k_out
+
+
+def dit_residual_change_workspace_bytes(B: int, N: int, D: int) -> int:
+    return load_library().dit_residual_change_workspace_bytes(B, N, D)
+
+
+def dit_residual_change(r, r_cached, out=None, workspace=None, stream=None):
+    """Per sample (sum |r - r_cached|, sum |r_cached|, ratio) as a [B, 3] float64 device tensor.
+
+    ``workspace`` (optional) is a device tensor of at least dit_residual_change_workspace_bytes bytes.
+    """
+    _tensor(r, "r", ndim=3)
+    B, N, D = r.shape
+    _shape(_tensor(r_cached, "r_cached"), "r_cached", (B, N, D))
+    out = torch.empty((B, 3), dtype=torch.float64, device=r.device) if out is None else out
+    _shape(_tensor(out, "out", dtype=torch.float64), "out", (B, 3))
+    need = dit_residual_change_workspace_bytes(B, N, D)
+    if need < 0:
+        raise ValueError(f"unsupported sizes {(B, N, D)}")
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=r.device)
+    if not isinstance(workspace, torch.Tensor) or not workspace.is_contiguous() or workspace.device != r.device:
+        raise ValueError("workspace must be a contiguous tensor on the same device")
+    nbytes = workspace.numel() * workspace.element_size()
+    dev = _same_device(r, r_cached, out)
+    with torch.cuda.device(dev):
+        _check("dit_residual_change", load_library().dit_residual_change(
+            r.data_ptr(), r_cached.data_ptr(), out.data_ptr(), workspace.data_ptr(), nbytes, B, N, D,
+            _stream(stream, dev)))
+    return out
 
 
 def dit_packed_positions(T: int, Hg: int, Wg: int, n_extra: int = 0, pos=None, device=None, stream=None):

@@ -220,6 +220,48 @@ dit_status dit_gated_residual_adaln(const dit_bf16 *x, const dit_bf16 *y, const 
         dit::launch_gated_residual_adaln(x, y, gate, shift, scale, x_out, z, rows, N, D, eps, (hipStream_t)stream));
 }
 
+// Samples per call of the residual-change statistic (one grid row each) and
+// tiles per sample (the grid's x extent, kept below 2^24 workgroups).
+constexpr int64_t kMaxSamples = 65535;
+constexpr int64_t kMaxChangeTiles = (int64_t(1) << 24) - 1;
+
+int64_t dit_residual_change_workspace_bytes(int64_t B, int64_t N, int64_t D)
+{
+    if (B < 0 || N < 0 || D < 8 || D % 8 != 0 || D > kMaxWidth || B > kMaxSamples || N > kMaxRows)
+        return -1;
+    const int64_t tiles = dit::residual_change_tiles(N, D);
+    if (tiles > kMaxChangeTiles)
+        return -1;
+    return B * tiles * 16;
+}
+
+dit_status dit_residual_change(const dit_bf16 *r, const dit_bf16 *r_cached, double *out, void *workspace,
+                               int64_t workspace_bytes, int64_t B, int64_t N, int64_t D, void *stream)
+{
+    if (B < 0 || N < 0 || D < 0 || workspace_bytes < 0 || B > kMaxSamples || N > kMaxRows)
+        return DIT_ERR_ARG;
+    if (D < 8 || D % 8 != 0 || D > kMaxWidth)
+        return DIT_ERR_SHAPE;
+    const int64_t need = dit_residual_change_workspace_bytes(B, N, D);
+    if (need < 0)
+        return DIT_ERR_ARG;
+    if (B == 0)
+        return DIT_OK;
+    if (!out || (N > 0 && (!r || !r_cached)) || (need > 0 && !workspace))
+        return DIT_ERR_NULL;
+    if (!aligned(out, 8) || (N > 0 && (!aligned(r, 16) || !aligned(r_cached, 16))) ||
+        (need > 0 && !aligned(workspace, 16)))
+        return DIT_ERR_ALIGN;
+    if (workspace_bytes < need)
+        return DIT_ERR_ARG;
+    const int64_t nin = B * N * D * 2, nout = B * 3 * 8;
+    if (overlap(out, nout, workspace, need) || (N > 0 && (overlap(out, nout, r, nin) || overlap(out, nout, r_cached, nin) ||
+                                                          overlap(workspace, need, r, nin) ||
+                                                          overlap(workspace, need, r_cached, nin))))
+        return DIT_ERR_ARG;
+    return launched(dit::launch_residual_change(r, r_cached, out, workspace, B, N, D, (hipStream_t)stream));
+}
+
 dit_status dit_packed_positions(int32_t *pos, int64_t T, int64_t Hg, int64_t Wg, int64_t n_extra, void *stream)
 {
     if (T < 0 || Hg < 0 || Wg < 0 || n_extra < 0 || n_extra > kMaxRows)

@@ -34,6 +34,13 @@ hipError_t launch_gated_residual_adaln(const void *x, const void *y, const void 
                                        const void *scale, void *x_out, void *z, int64_t rows, int64_t N, int64_t D,
                                        float eps, hipStream_t stream);
 
+// Workgroup tiles per sample of the residual-change statistic (workspace holds B * tiles * 16 bytes).
+int64_t residual_change_tiles(int64_t N, int64_t D);
+
+// out[b] = (sum |r - r_cached|, sum |r_cached|, ratio) per sample, via per-tile partials in workspace.
+hipError_t launch_residual_change(const void *r, const void *r_cached, double *out, void *workspace, int64_t B,
+                                  int64_t N, int64_t D, hipStream_t stream);
+
 // Packed (t, h, w) coordinates of T*Hg*Wg video tokens then n_extra tokens.
 hipError_t launch_packed_positions(int32_t *pos, int64_t T, int64_t Hg, int64_t Wg, int64_t n_extra,
                                    hipStream_t stream);
