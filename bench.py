@@ -207,12 +207,15 @@ def main(argv=None) -> int:
     # The next fusion, measured on its own after the chain: gated residual ->
     # AdaLN in one kernel (x and y read once, x_out and z written once).
     fused_bytes = 4 * wl.R * wl.D * 2 + 3 * wl.B * wl.D * 2
+    # Own output buffers: the chain's outputs stay intact for the oracle check.
+    fused_x = torch.empty_like(out)
+    fused_z = torch.empty_like(y)
     fev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     for i in range(args.warmup + args.steps):
         if i >= args.warmup:
             fev[i - args.warmup][0].record(stream)
-        dit.dit_gated_residual_adaln(ins["res_x"], ins["res_y"], ins["gate"], ins["shift"], ins["scale"], x_out=out,
-                                     z=y, eps=wl.eps, stream=stream)
+        dit.dit_gated_residual_adaln(ins["res_x"], ins["res_y"], ins["gate"], ins["shift"], ins["scale"],
+                                     x_out=fused_x, z=fused_z, eps=wl.eps, stream=stream)
         if i >= args.warmup:
             fev[i - args.warmup][1].record(stream)
     torch.cuda.synchronize()
@@ -231,8 +234,8 @@ def main(argv=None) -> int:
     qkv[..., :HD].copy_(ins["q"].reshape(wl.B, wl.N, HD))
     qkv[..., HD:2 * HD].copy_(ins["k"].reshape(wl.B, wl.N, HD))
     qkv[..., 2 * HD:].zero_()
-    qo_hm = qo.view(wl.B, wl.H, wl.N, wl.Dh)
-    ko_hm = ko.view(wl.B, wl.H, wl.N, wl.Dh)
+    qo_hm = torch.empty((wl.B, wl.H, wl.N, wl.Dh), dtype=torch.bfloat16, device=dev)
+    ko_hm = torch.empty_like(qo_hm)
     lev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     for i in range(args.warmup + args.steps):
         if i >= args.warmup:
@@ -300,6 +303,17 @@ def main(argv=None) -> int:
                        "GB_s": round(fused_mix_bytes / (fused_mix_ms * 1e-3) / 1e9, 1),
                        "tokens_per_s": round(wl.R / (fused_mix_ms * 1e-3))}
 
+    # The next-row outputs against the chain's own: the fused residual is the
+    # plain residual bit for bit, and the head-major q', k' are the token-major
+    # ones transposed (the oracle check below covers the fused z).
+    consistency = {
+        "fused_x_out_equals_residual": bool(torch.equal(fused_x, out)),
+        "head_major_equals_token_major": bool(
+            torch.equal(qo_hm.permute(0, 2, 1, 3), qo.view(wl.B, wl.N, wl.H, wl.Dh))
+            and torch.equal(ko_hm.permute(0, 2, 1, 3), ko.view(wl.B, wl.N, wl.H, wl.Dh))),
+    }
+    del qo_hm, ko_hm, fused_x
+
     value = chain_bytes / (ms_per_step * 1e-3) / 1e9
     result = {
         "metric": METRIC,
@@ -331,10 +345,15 @@ def main(argv=None) -> int:
         "next_qk_layout": layout,
         "next_residual_change": change,
         "block_mix_fused": block_mix_fused,
+        "next_consistency": consistency,
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(wl, ins, {"y": y, "out": out, "sw": sw, "qo": qo, "ko": ko},
-                                              args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(wl, ins, {"y": y, "out": out, "sw": sw, "qo": qo, "ko": ko,
+                                                        "fz": fused_z}, args.cpu_seconds)
+    ok = all(consistency.values()) and result.get("cpu_baseline", {}).get("parity_ok", True)
+    if not ok:
+        print("[bench] WARNING: GPU outputs disagree with the oracle or with each other", file=sys.stderr,
+              flush=True)
     print(json.dumps(result), flush=True)
     return 0
 
@@ -365,7 +384,7 @@ def cpu_baseline(wl, ins, outs, target_s: float) -> dict:
             "k": bits(ins["k"].reshape(R, -1).index_select(0, idx)),
         }
         gpu = {k: outs[k].reshape(R, -1).index_select(0, idx).float().cpu().double().numpy()
-               for k in ("y", "out", "sw", "qo", "ko")}
+               for k in ("y", "out", "sw", "qo", "ko", "fz")}
         return host, gpu
 
     shift, scale, gate = bits(ins["shift"]), bits(ins["scale"]), bits(ins["gate"])
@@ -394,6 +413,21 @@ def cpu_baseline(wl, ins, outs, target_s: float) -> dict:
         res["sw"].append((np.arange(len(rows)), oracle.swiglu(host["sw"], threads=threads)))
         return res
 
+    def fused_check(rows, host, gpu):
+        """Fused residual -> AdaLN z on the same rows (not part of the timed oracle work)."""
+        samples = np.asarray(rows) // N
+        ratio = 0.0
+        for b in range(B):
+            sel = np.nonzero(samples == b)[0]
+            if sel.size == 0:
+                continue
+            n = sel.size
+            _, z = oracle.gated_residual_adaln(host["rx"][sel].reshape(1, n, -1), host["ry"][sel].reshape(1, n, -1),
+                                               gate[b:b + 1], shift[b:b + 1], scale[b:b + 1], eps=wl.eps,
+                                               threads=threads)
+            ratio = max(ratio, worst_ratio(gpu["fz"][sel], z.reshape(n, -1)))
+        return ratio
+
     def check(res, gpu):
         """Largest |gpu - oracle| / bound over the chunk (<= 1 passes)."""
         ratio = 0.0
@@ -413,7 +447,7 @@ def cpu_baseline(wl, ins, outs, target_s: float) -> dict:
         res = run_oracle(rows, host)
         elapsed += time.perf_counter() - t
         done += len(rows)
-        max_ratio = max(max_ratio, check(res, gpu))
+        max_ratio = max(max_ratio, check(res, gpu), fused_check(rows, host, gpu))
         if elapsed >= target_s:
             break
     tokens_per_s = done / elapsed
@@ -425,7 +459,7 @@ def cpu_baseline(wl, ins, outs, target_s: float) -> dict:
         "kind": "oracle",
         "sample": f"{done} of {R} tokens (seeded uniform random rows) of the {wl.name} workload; all four ops "
                   f"in the fp64 C oracle on {threads} host threads; {elapsed:.1f} s of oracle time (the same "
-                  f"tokens' GPU outputs are checked against it)",
+                  f"tokens' GPU outputs, and the fused residual->AdaLN z, are checked against it)",
         "parity_rows_checked": done,
         "parity_max_err_over_bound": round(max_ratio, 4),
         "parity_ok": bool(max_ratio <= 1.0),

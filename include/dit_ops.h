@@ -242,7 +242,7 @@ dit_status dit_residual_change(const dit_bf16 *r, const dit_bf16 *r_cached,
 
 /*
  * Bytes of workspace dit_residual_change needs for these sizes (16 bytes per
- * 1024 16-byte vectors of each sample, rounded up), or -1 if the sizes are
+ * 2048 16-byte vectors of each sample, rounded up), or -1 if the sizes are
  * invalid.  Host-only; makes no HIP call.
  */
 int64_t dit_residual_change_workspace_bytes(int64_t B, int64_t N, int64_t D);

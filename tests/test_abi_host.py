@@ -192,7 +192,7 @@ def test_qk_layout_validation(lib):
 
 def test_residual_change_validation(lib):
     ws = lib.dit_residual_change_workspace_bytes
-    assert ws(1, 124992, 4096) == 16 * ((124992 * 512 + 1023) // 1024)
+    assert ws(1, 124992, 4096) == 16 * ((124992 * 512 + 2047) // 2048)
     assert ws(2, 3, 8) == 2 * 16
     assert ws(1, 0, 8) == 0
     assert ws(-1, 4, 8) == -1 and ws(1, 4, 12) == -1 and ws(70000, 4, 8) == -1

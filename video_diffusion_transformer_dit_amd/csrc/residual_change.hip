@@ -9,7 +9,7 @@
 // HBM-bound read-only reduction: 4 bytes per element, nothing written but
 // three doubles per sample.
 //
-// Determinism: stage 1 writes one fp64 (num, den) partial per 1024-vector
+// Determinism: stage 1 writes one fp64 (num, den) partial per 2048-vector
 // tile into the caller's workspace; stage 2 reduces each sample's partials
 // in a fixed order.  Every sum has a fixed shape (fp32 over the 8 values of a
 // 16-byte vector, then fp64), so repeated calls give bit-identical results.
@@ -19,8 +19,8 @@
 namespace dit {
 namespace {
 
-constexpr int kPartialThreads = 256;
-constexpr int kPartialU = 4; // vectors per thread per input
+constexpr int kPartialThreads = 1024;
+constexpr int kPartialU = 2; // vectors per thread per input
 constexpr int kTileVectors = kPartialThreads * kPartialU;
 constexpr int kFinalThreads = 1024;
 
@@ -95,10 +95,22 @@ __global__ __launch_bounds__(kFinalThreads) void residual_change_final_kernel(co
     const int tid = threadIdx.x;
     const size_t b = blockIdx.x;
     double num = 0.0, den = 0.0;
-    for (int t = tid; t < tiles; t += kFinalThreads) {
-        const double2 p = ws[b * tiles + t];
-        num += p.x;
-        den += p.y;
+    // Thread tid adds partials tid, tid + 1024, ... in that order, with eight
+    // loads in flight: a single workgroup reads every partial, so latency,
+    // not bandwidth, bounds this stage.
+    constexpr int kInFlight = 8;
+    for (int t0 = tid; t0 < tiles; t0 += kFinalThreads * kInFlight) {
+        double2 p[kInFlight];
+#pragma unroll
+        for (int j = 0; j < kInFlight; ++j) {
+            const int t = t0 + j * kFinalThreads;
+            p[j] = t < tiles ? ws[b * tiles + t] : make_double2(0.0, 0.0);
+        }
+#pragma unroll
+        for (int j = 0; j < kInFlight; ++j) {
+            num += p[j].x;
+            den += p[j].y;
+        }
     }
     num = wave_sum_f64(num);
     den = wave_sum_f64(den);
