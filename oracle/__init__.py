@@ -80,6 +80,14 @@ def _bind(lib):
     lib.dit_oracle_qk_rmsnorm_rope3d_layout.restype = ctypes.c_int
     lib.dit_oracle_residual_change.argtypes = [_c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64]
     lib.dit_oracle_residual_change.restype = ctypes.c_int
+    lib.dit_oracle_subblock_pool.argtypes = [_c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64]
+    lib.dit_oracle_subblock_pool.restype = ctypes.c_int
+    lib.dit_oracle_subblock_scores.argtypes = [_c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64]
+    lib.dit_oracle_subblock_scores.restype = ctypes.c_int
+    lib.dit_oracle_subblock_keep.argtypes = [_c_i64, _c_dbl]
+    lib.dit_oracle_subblock_keep.restype = _c_i64
+    lib.dit_oracle_subblock_topk.argtypes = [_c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64]
+    lib.dit_oracle_subblock_topk.restype = ctypes.c_int
     return lib
 
 
@@ -332,3 +340,64 @@ def residual_change(r, r_cached, lib=None) -> np.ndarray:
     _check(lib.dit_oracle_residual_change(_ptr(r), _ptr(r_cached), _ptr(out), B, N, D), "residual_change")
     return out
 
+
+
+# --------------------------------------------------------------------------- SubBlock routing
+
+SUBBLOCK_TOKENS = 64  # tokens per SubBlock attention block
+
+
+def subblock_pool(x, block: int = SUBBLOCK_TOKENS, lib=None) -> np.ndarray:
+    """x [B,N,H,Dh] (bf16 bits, token-major) -> [B,H,nb,Dh] float64 block means, nb = ceil(N/block)."""
+    lib = lib or load()
+    x = _bits(x)
+    B, N, H, Dh = x.shape
+    nb = -(-N // block)
+    out = np.empty((B, H, nb, Dh), dtype=np.float64)
+    _check(lib.dit_oracle_subblock_pool(_ptr(x), _ptr(out), B, N, H, Dh, block), "subblock_pool")
+    return out
+
+
+def subblock_scores(qp, kp, lib=None) -> np.ndarray:
+    """Pooled means qp [B,H,nq,Dh], kp [B,H,nk,Dh] float64 -> scores [B,H,nq,nk].
+
+    The means are rounded to bf16 before the products.  ``qp`` may hold any
+    selection of query blocks (e.g. a sample of rows); every key block is scored.
+    """
+    lib = lib or load()
+    qp = np.ascontiguousarray(qp, dtype=np.float64)
+    kp = np.ascontiguousarray(kp, dtype=np.float64)
+    assert qp.ndim == 4 and kp.ndim == 4 and qp.shape[:2] == kp.shape[:2] and qp.shape[3] == kp.shape[3]
+    B, H, nq, Dh = qp.shape
+    nk = kp.shape[2]
+    s = np.empty((B, H, nq, nk), dtype=np.float64)
+    _check(lib.dit_oracle_subblock_scores(_ptr(qp), _ptr(kp), _ptr(s), B, H, nq, nk, Dh), "subblock_scores")
+    return s
+
+
+def subblock_keep(nb: int, sparsity: float, lib=None) -> int:
+    """Key blocks kept per query block for a sparsity (fraction of blocks that may be dropped)."""
+    lib = lib or load()
+    keep = lib.dit_oracle_subblock_keep(nb, sparsity)
+    _check(0 if keep >= 0 else -1, "subblock_keep")
+    return int(keep)
+
+
+def subblock_topk(s, keep: int, lib=None) -> np.ndarray:
+    """Scores [B,H,nq,nb] float64 -> kept key blocks [B,H,nq,keep] int32, ascending per query block."""
+    lib = lib or load()
+    s = np.ascontiguousarray(s, dtype=np.float64)
+    B, H, nq, nb = s.shape
+    idx = np.empty((B, H, nq, keep), dtype=np.int32)
+    _check(lib.dit_oracle_subblock_topk(_ptr(s), _ptr(idx), B, H, nq, nb, keep), "subblock_topk")
+    return idx
+
+
+def subblock_route(q, k, sparsity: float, block: int = SUBBLOCK_TOKENS, lib=None):
+    """q', k' [B,N,H,Dh] (bf16 bits) -> (qp, kp, scores, kept indices) of SubBlock routing."""
+    lib = lib or load()
+    qp = subblock_pool(q, block, lib=lib)
+    kp = subblock_pool(k, block, lib=lib)
+    s = subblock_scores(qp, kp, lib=lib)
+    idx = subblock_topk(s, subblock_keep(qp.shape[2], sparsity, lib=lib), lib=lib)
+    return qp, kp, s, idx

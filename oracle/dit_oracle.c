@@ -17,6 +17,11 @@
  *     kernels cut memory traffic, intermediates and launches while leaving the
  *     arithmetic unchanged, and that video and audio tokens share one packed
  *     DiT stack.
+ *   - The same stamatios.com summary, "De onde vêm os ganhos" and "Resultado
+ *     principal", and the xhh.club Q&A on the sparsity parameter describe the
+ *     SubBlock attention router: 64-token blocks, scored by estimated
+ *     contribution, a fraction of the key blocks kept per query block.  The
+ *     routing functions at the end compute that selection step by step.
  *   So each function below is the plain, unfused definition of its operation,
  *   evaluated in double precision with no blocking or reordering.  Inputs are
  *   raw bf16 bit patterns (decoded exactly to double); outputs are unrounded
@@ -462,3 +467,159 @@ int dit_oracle_residual_change(const uint16_t *r, const uint16_t *r_cached,
     return ORACLE_OK;
 }
 
+
+/*
+ * SubBlock routing, step 1: block pooling.
+ * Cited: "SGLang acelera vídeo do MiniMax-H3…" (stamatios.com), "De onde vêm
+ * os ganhos": SubBlock attention cuts the sequence into 64-token blocks and
+ * routes over the key blocks; "Resultado principal": the blocks dropped are
+ * those whose estimated contribution is smaller.
+ * Reading: a block is summarised by the mean of its tokens' head vectors (q or
+ * k after RMSNorm and RoPE).  Blocks never span two samples; the last block of
+ * a sample may hold fewer tokens and averages only those.
+ * x: [B][N][H][Dh] bf16 bits (token-major); out: [B][H][nb][Dh] with
+ * nb = ceil(N / block).
+ */
+int dit_oracle_subblock_pool(const uint16_t *x, double *out, int64_t B, int64_t N,
+                             int64_t H, int64_t Dh, int64_t block)
+{
+    if (!x || !out || B < 0 || N < 0 || H <= 0 || Dh <= 0 || block <= 0)
+        return ORACLE_BAD_ARG;
+    const int64_t nb = (N + block - 1) / block;
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t h = 0; h < H; ++h)
+            for (int64_t i = 0; i < nb; ++i) {
+                const int64_t first = i * block;
+                const int64_t last = first + block < N ? first + block : N;
+                double *o = out + ((b * H + h) * nb + i) * Dh;
+                for (int64_t d = 0; d < Dh; ++d) {
+                    double sum = 0.0;
+                    for (int64_t n = first; n < last; ++n)
+                        sum += bf16_to_double(x[((b * N + n) * H + h) * Dh + d]);
+                    o[d] = sum / (double)(last - first);
+                }
+            }
+    return ORACLE_OK;
+}
+
+/*
+ * SubBlock routing, step 2: block scores.
+ * Cited: as for the pooling (stamatios.com, "De onde vêm os ganhos" and
+ * "Resultado principal").
+ * Reading: the estimated contribution of key block j to query block i is the
+ * dot product of their pooled means, per sample and head, with no 1/sqrt(Dh)
+ * factor (a positive scale leaves the order unchanged).  The means enter the
+ * product rounded to bf16, the operand precision of the attention path that
+ * consumes the routing; the products are exact and summed in double.
+ *   s[b][h][i][j] = sum_d bf16(qp[b][h][i][d]) * bf16(kp[b][h][j][d])
+ * qp: [B][H][nq][Dh] (any nq query blocks), kp: [B][H][nk][Dh],
+ * s: [B][H][nq][nk].
+ */
+int dit_oracle_subblock_scores(const double *qp, const double *kp, double *s, int64_t B,
+                               int64_t H, int64_t nq, int64_t nk, int64_t Dh)
+{
+    if (!qp || !kp || !s || B < 0 || H <= 0 || nq < 0 || nk < 0 || Dh <= 0)
+        return ORACLE_BAD_ARG;
+    const int64_t nqe = B * H * nq * Dh, nke = B * H * nk * Dh;
+    double *qr = malloc(sizeof(double) * (size_t)(nqe > 0 ? nqe : 1));
+    double *kr = malloc(sizeof(double) * (size_t)(nke > 0 ? nke : 1));
+    if (!qr || !kr) {
+        free(qr); free(kr);
+        return ORACLE_BAD_ARG;
+    }
+    for (int64_t e = 0; e < nqe; ++e)
+        qr[e] = bf16_to_double(dit_oracle_bf16_encode(qp[e]));
+    for (int64_t e = 0; e < nke; ++e)
+        kr[e] = bf16_to_double(dit_oracle_bf16_encode(kp[e]));
+    for (int64_t bh = 0; bh < B * H; ++bh)
+        for (int64_t i = 0; i < nq; ++i)
+            for (int64_t j = 0; j < nk; ++j) {
+                const double *qi = qr + (bh * nq + i) * Dh;
+                const double *kj = kr + (bh * nk + j) * Dh;
+                double acc = 0.0;
+                for (int64_t d = 0; d < Dh; ++d)
+                    acc += qi[d] * kj[d];
+                s[(bh * nq + i) * nk + j] = acc;
+            }
+    free(qr); free(kr);
+    return ORACLE_OK;
+}
+
+/*
+ * SubBlock routing: key blocks kept per query block.
+ * Cited: "8×H200 上的 MiniMax-H3…" (xhh.club), Q&A on the sparsity parameter:
+ * sparsity is the fraction of key blocks that may be dropped, so 0.75 keeps
+ * about a quarter of them.
+ * Reading: floor(sparsity * nb) blocks are dropped and the rest kept, with at
+ * least one kept; sparsity must lie in [0, 1).  Returns -1 on bad arguments.
+ */
+int64_t dit_oracle_subblock_keep(int64_t nb, double sparsity)
+{
+    if (nb < 0 || !(sparsity >= 0.0) || !(sparsity < 1.0))
+        return -1;
+    if (nb == 0)
+        return 0;
+    int64_t keep = nb - (int64_t)floor(sparsity * (double)nb);
+    return keep < 1 ? 1 : keep;
+}
+
+struct scored_block {
+    double score;
+    int64_t index;
+};
+
+/* Larger score first; equal scores lower block index first. */
+static int by_score_then_index(const void *pa, const void *pb)
+{
+    const struct scored_block *a = pa, *b = pb;
+    if (a->score != b->score)
+        return a->score > b->score ? -1 : 1;
+    return a->index < b->index ? -1 : (a->index > b->index);
+}
+
+/*
+ * SubBlock routing, step 3: the kept key blocks.
+ * Cited: stamatios.com, "Resultado principal" (blocks of smaller estimated
+ * contribution are dropped) and "De onde vêm os ganhos" (routing keeps part of
+ * the key blocks).
+ * Reading: each query block keeps the `keep` key blocks of largest score;
+ * among equal scores the lower block index is kept.  The kept indices are
+ * listed in ascending block order.  Scores must be finite.
+ * s: [B][H][nq][nb] (nq query blocks' rows over nb key blocks);
+ * idx: [B][H][nq][keep] int32.
+ */
+int dit_oracle_subblock_topk(const double *s, int32_t *idx, int64_t B, int64_t H, int64_t nq,
+                             int64_t nb, int64_t keep)
+{
+    if (!s || !idx || B < 0 || H <= 0 || nq < 0 || nb < 0 || keep < 0 || keep > nb)
+        return ORACLE_BAD_ARG;
+    if (nb == 0)
+        return ORACLE_OK;
+    struct scored_block *row = malloc(sizeof(*row) * (size_t)nb);
+    unsigned char *kept = malloc((size_t)nb);
+    if (!row || !kept) {
+        free(row); free(kept);
+        return ORACLE_BAD_ARG;
+    }
+    int status = ORACLE_OK;
+    for (int64_t r = 0; r < B * H * nq && status == ORACLE_OK; ++r) {
+        for (int64_t j = 0; j < nb; ++j) {
+            row[j].score = s[r * nb + j];
+            row[j].index = j;
+            if (!isfinite(row[j].score))
+                status = ORACLE_BAD_ARG;
+        }
+        if (status != ORACLE_OK)
+            break;
+        qsort(row, (size_t)nb, sizeof(*row), by_score_then_index);
+        memset(kept, 0, (size_t)nb);
+        for (int64_t t = 0; t < keep; ++t)
+            kept[row[t].index] = 1;
+        int64_t at = 0;
+        for (int64_t j = 0; j < nb; ++j)
+            if (kept[j])
+                idx[r * keep + at++] = (int32_t)j;
+    }
+    free(row); free(kept);
+    return status;
+}

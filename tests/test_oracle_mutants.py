@@ -84,6 +84,27 @@ MUTANTS = {
     "change_signed_difference": ("num += fabs(a - c);", "num += a - c;"),
     "change_sample_zero": ("double a = bf16_to_double(r[b * N * D + i]);", "double a = bf16_to_double(r[i]);"),
     "change_zero_den_ratio": ("(num > 0.0 ? INFINITY : 0.0)", "0.0"),
+    # SubBlock routing
+    "pool_divides_by_block": ("o[d] = sum / (double)(last - first);", "o[d] = sum / (double)block;"),
+    "pool_drops_short_block": ("const int64_t nb = (N + block - 1) / block;", "const int64_t nb = N / block;"),
+    "pool_ignores_sample": ("sum += bf16_to_double(x[((b * N + n) * H + h) * Dh + d]);",
+                            "sum += bf16_to_double(x[(n * H + h) * Dh + d]);"),
+    "pool_ignores_head": ("sum += bf16_to_double(x[((b * N + n) * H + h) * Dh + d]);",
+                          "sum += bf16_to_double(x[((b * N + n) * H) * Dh + d]);"),
+    "scores_unrounded": ("kr[e] = bf16_to_double(dit_oracle_bf16_encode(kp[e]));", "kr[e] = kp[e];"),
+    "scores_transposed": ("s[(bh * nq + i) * nk + j] = acc;", "s[(bh * nk + j) * nq + i] = acc;"),
+    "scores_k_with_q": ("const double *kj = kr + (bh * nk + j) * Dh;", "const double *kj = qr + (bh * nk + j) * Dh;"),
+    "keep_rounds_drop_up": ("int64_t keep = nb - (int64_t)floor(sparsity * (double)nb);",
+                            "int64_t keep = nb - (int64_t)ceil(sparsity * (double)nb);"),
+    "keep_is_sparsity_share": ("int64_t keep = nb - (int64_t)floor(sparsity * (double)nb);",
+                               "int64_t keep = (int64_t)floor(sparsity * (double)nb);"),
+    "topk_smallest": ("return a->score > b->score ? -1 : 1;", "return a->score < b->score ? -1 : 1;"),
+    "topk_ties_high_index": ("return a->index < b->index ? -1 : (a->index > b->index);",
+                             "return a->index > b->index ? -1 : (a->index < b->index);"),
+    "topk_score_order": ("        int64_t at = 0;\n        for (int64_t j = 0; j < nb; ++j)\n"
+                         "            if (kept[j])\n                idx[r * keep + at++] = (int32_t)j;",
+                         "        for (int64_t t = 0; t < keep; ++t)\n"
+                         "            idx[r * keep + t] = (int32_t)row[t].index;"),
     # bf16 decode
     "decode_wrong_shift": ("uint32_t word = (uint32_t)bits << 16;", "uint32_t word = (uint32_t)bits << 15;"),
 }

@@ -522,6 +522,144 @@ def pin_residual_change_matches_library_per_sample(lib):
     assert np.array_equal(out2[[0, 2]], out[[0, 2]]) and out2[1, 0] != out[1, 0]
 
 
+# --------------------------------------------------------------------------- SubBlock routing
+
+def pin_subblock_pool_hand_cases(lib):
+    for case in cases("subblock_pool_hand.txt"):
+        block, N, H, Dh = (int(case[k][0]) for k in ("block", "N", "H", "Dh"))
+        x = b16(values(case["x"]), (1, N, H, Dh))
+        out = oracle.subblock_pool(x, block, lib=lib)
+        nb = -(-N // block)
+        assert out.shape == (1, H, nb, Dh), case
+        assert close(out.reshape(-1), values(case["out"]), rel=1e-15), (case, out)
+
+
+def pin_subblock_pool_matches_library_mean(lib):
+    # numpy's mean over each block's token slice (its own summation order)
+    B, N, H, Dh = 2, 150, 3, 8
+    x = rand_bf16((B, N, H, Dh), seed=181)
+    for block in (64, 7):
+        out = oracle.subblock_pool(bits(x), block, lib=lib)
+        xf = f64(x).numpy()
+        nb = -(-N // block)
+        assert out.shape == (B, H, nb, Dh)
+        for i in range(nb):
+            ref = xf[:, i * block:(i + 1) * block].mean(axis=1)  # [B, H, Dh]
+            assert np.allclose(out[:, :, i], ref, rtol=1e-13, atol=1e-15), (block, i)
+
+
+def pin_subblock_pool_invariants(lib):
+    # a block of equal tokens pools to that token; a ramp pools to its midpoint;
+    # changing sample 1 leaves sample 0 alone
+    B, N, H, Dh, block = 2, 64 * 3, 2, 4, 64
+    vals = np.zeros((B, N, H, Dh))
+    for i in range(3):
+        vals[:, i * block:(i + 1) * block] = (i + 1) * 0.5
+    vals[1, :block, 1, 2] = np.arange(block) * 0.25  # ramp 0 .. 15.75, mean 7.875
+    x = b16(vals.reshape(-1), (B, N, H, Dh))
+    out = oracle.subblock_pool(x, block, lib=lib)
+    assert np.all(out[0, :, 0] == 0.5) and np.all(out[0, :, 1] == 1.0) and np.all(out[0, :, 2] == 1.5)
+    assert out[1, 1, 0, 2] == 7.875 and out[1, 0, 0, 2] == 0.5
+    vals[1] += 1.0
+    out2 = oracle.subblock_pool(b16(vals.reshape(-1), (B, N, H, Dh)), block, lib=lib)
+    assert np.array_equal(out2[0], out[0]) and np.array_equal(out2[1], out[1] + 1.0)
+
+
+def pin_subblock_scores_hand_cases(lib):
+    for case in cases("subblock_scores_hand.txt"):
+        nb, Dh = int(case["nb"][0]), int(case["Dh"][0])
+        qp = np.array(values(case["qp"])).reshape(1, 1, nb, Dh)
+        kp = np.array(values(case["kp"])).reshape(1, 1, nb, Dh)
+        s = oracle.subblock_scores(qp, kp, lib=lib)
+        assert s.reshape(-1).tolist() == values(case["s"]), (case, s)
+
+
+def pin_subblock_scores_match_library(lib):
+    # torch's own bf16 rounding of the means, then an fp64 matmul per (sample, head)
+    g = torch.Generator().manual_seed(191)
+    B, H, nb, Dh = 2, 3, 9, 16
+    qp = torch.randn((B, H, nb, Dh), generator=g, dtype=torch.float64) * 0.3
+    kp = torch.randn((B, H, nb, Dh), generator=g, dtype=torch.float64) * 0.3
+    s = oracle.subblock_scores(qp.numpy(), kp.numpy(), lib=lib)
+    qb = qp.to(torch.bfloat16).to(torch.float64)
+    kb = kp.to(torch.bfloat16).to(torch.float64)
+    ref = torch.matmul(qb, kb.transpose(-1, -2).contiguous())
+    assert np.allclose(s, ref.numpy(), rtol=1e-13, atol=1e-15)
+    # the rounding matters for these inputs: unrounded products differ
+    assert not np.allclose(s, torch.matmul(qp, kp.transpose(-1, -2).contiguous()).numpy(), rtol=1e-6)
+
+
+def pin_subblock_row_subset(lib):
+    # scoring and routing a subset of query blocks gives those rows of the full result
+    g = torch.Generator().manual_seed(193)
+    qp = (torch.randn((1, 2, 11, 8), generator=g, dtype=torch.float64) * 0.3).numpy()
+    kp = (torch.randn((1, 2, 11, 8), generator=g, dtype=torch.float64) * 0.3).numpy()
+    rows = [0, 4, 10]
+    full = oracle.subblock_scores(qp, kp, lib=lib)
+    part = oracle.subblock_scores(qp[:, :, rows], kp, lib=lib)
+    assert part.shape == (1, 2, 3, 11) and np.array_equal(part, full[:, :, rows])
+    assert np.array_equal(oracle.subblock_topk(part, 4, lib=lib), oracle.subblock_topk(full, 4, lib=lib)[:, :, rows])
+
+
+def pin_subblock_keep_cases(lib):
+    for case in cases("subblock_keep_hand.txt"):
+        nb, sparsity = int(case["nb"][0]), evaluate(case["sparsity"][0])
+        assert oracle.subblock_keep(nb, sparsity, lib=lib) == int(case["keep"][0]), case
+    for bad in (-0.1, 1.0, float("nan")):
+        with pytest.raises(ValueError):
+            oracle.subblock_keep(10, bad, lib=lib)
+
+
+def pin_subblock_topk_hand_cases(lib):
+    for case in cases("subblock_topk_hand.txt"):
+        row = values(case["s"])
+        keep = int(case["keep"][0])
+        idx = oracle.subblock_topk(np.array(row).reshape(1, 1, 1, -1).repeat(len(row), axis=2), keep, lib=lib)
+        for r in range(len(row)):
+            assert idx[0, 0, r].tolist() == [int(v) for v in case["idx"]], (case, idx[0, 0, r])
+
+
+def pin_subblock_topk_brute_force(lib):
+    # numpy's stable lexsort on (score descending, index ascending); scores drawn
+    # from a few values so that ties are common
+    rng = np.random.default_rng(201)
+    B, H, nb = 2, 2, 23
+    s = rng.integers(-3, 4, size=(B, H, nb, nb)).astype(np.float64) * 0.5
+    for keep in (0, 1, 5, 12, nb):
+        idx = oracle.subblock_topk(s, keep, lib=lib)
+        for b in range(B):
+            for h in range(H):
+                for i in range(nb):
+                    order = np.lexsort((np.arange(nb), -s[b, h, i]))
+                    assert idx[b, h, i].tolist() == sorted(order[:keep].tolist()), (keep, b, h, i)
+
+
+def pin_subblock_route_structured(lib):
+    # Query block i is made of tokens +-e_i (mean e_i exactly); key block j of
+    # tokens c_j +- d (mean c_j), so score (i, j) = c_j[i] and the kept blocks
+    # follow from the table c by hand.
+    block, nb, Dh = 4, 4, 8
+    c = np.array([[2.0, -1.0, 0.5, 3.0, 0, 0, 0, 0],   # key block 0
+                  [1.0, 4.0, 0.5, -2.0, 0, 0, 0, 0],   # key block 1
+                  [3.0, 0.0, 0.25, 1.0, 0, 0, 0, 0],   # key block 2
+                  [-1.0, 2.0, 0.75, 3.0, 0, 0, 0, 0]])  # key block 3
+    q = np.zeros((1, nb * block, 1, Dh))
+    k = np.zeros((1, nb * block, 1, Dh))
+    for i in range(nb):
+        for t in range(block):
+            sign = 1.0 if t % 2 == 0 else -1.0
+            q[0, i * block + t, 0, i] = 1.0 + sign * 0.5
+            k[0, i * block + t, 0] = c[i] + sign * 0.125
+    qp, kp, s, idx = oracle.subblock_route(b16(q.reshape(-1), q.shape), b16(k.reshape(-1), k.shape), 0.5,
+                                           block=block, lib=lib)
+    assert np.array_equal(qp[0, 0], np.eye(nb, Dh)) and np.array_equal(kp[0, 0], c)
+    assert np.array_equal(s[0, 0], c[:, :nb].T)
+    # keep = 4 - floor(0.5 * 4) = 2 per query block: the two largest of c[:, i].
+    # Query block 2 sees (0.5, 0.5, 0.25, 0.75): block 3, then the tie of blocks
+    # 0 and 1 goes to the lower index.
+    assert idx[0, 0].tolist() == [[0, 2], [1, 3], [0, 3], [0, 3]]
+
+
 # --------------------------------------------------------------------------- argument checks and threading
 
 def pin_rope_rejects_bad_bands(lib):
