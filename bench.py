@@ -273,6 +273,60 @@ def main(argv=None) -> int:
               "bytes": change_bytes, "GB_s": round(change_bytes / (change_ms * 1e-3) / 1e9, 1),
               "pct_of_peak": round(100.0 * change_bytes / (change_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2)}
 
+    # SubBlock routing front-end on the chain's q', k' at sparsity 0.75: block
+    # means (both input layouts), block scores alone (keep = 0 runs only the
+    # score kernel), then scores plus the kept blocks.
+    def timed(fn):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        for i in range(args.warmup + args.steps):
+            if i >= args.warmup:
+                ev[i - args.warmup][0].record(stream)
+            fn()
+            if i >= args.warmup:
+                ev[i - args.warmup][1].record(stream)
+        torch.cuda.synchronize()
+        return sum(a.elapsed_time(b) for a, b in ev) / args.steps
+
+    def rate(nbytes_, ms):
+        return {"avg_ms": round(ms, 5), "bytes": nbytes_, "GB_s": round(nbytes_ / (ms * 1e-3) / 1e9, 1),
+                "pct_of_peak": round(100.0 * nbytes_ / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2)}
+
+    sparsity = 0.75
+    nb = -(-wl.N // 64)
+    keep = dit.dit_subblock_keep(nb, sparsity)
+    ld = dit.dit_subblock_scores_ld(nb)
+    qp_s = torch.empty((wl.B, wl.H, nb, wl.Dh), dtype=torch.float32, device=dev)
+    kp_s = torch.empty_like(qp_s)
+    sc = torch.empty((wl.B, wl.H, nb, ld), dtype=torch.float32, device=dev)
+    kept = torch.empty((wl.B, wl.H, nb, keep), dtype=torch.int32, device=dev)
+    kept0 = torch.empty((wl.B, wl.H, nb, 0), dtype=torch.int32, device=dev)
+    pool_ms = timed(lambda: dit.dit_subblock_pool(qo, ko, q_pooled=qp_s, k_pooled=kp_s, stream=stream))
+    # the same bytes read as head-major [B, H, N, Dh] (timing only)
+    qo_as_hm = qo.view(wl.B, wl.H, wl.N, wl.Dh)
+    ko_as_hm = ko.view(wl.B, wl.H, wl.N, wl.Dh)
+    pool_hm_ms = timed(lambda: dit.dit_subblock_pool(qo_as_hm, ko_as_hm, head_major=True, q_pooled=qp_s,
+                                                     k_pooled=kp_s, stream=stream))
+    dit.dit_subblock_pool(qo, ko, q_pooled=qp_s, k_pooled=kp_s, stream=stream)
+    scores_ms = timed(lambda: dit.dit_subblock_route(qp_s, kp_s, keep=0, scores=sc, kept=kept0, stream=stream))
+    route_ms = timed(lambda: dit.dit_subblock_route(qp_s, kp_s, keep=keep, scores=sc, kept=kept, stream=stream))
+    pooled_bytes = 2 * wl.B * wl.H * nb * wl.Dh * 4
+    score_elems = wl.B * wl.H * nb * nb
+    pool_bytes = 2 * wl.R * wl.H * wl.Dh * 2 + pooled_bytes
+    scores_bytes = pooled_bytes + score_elems * 4
+    topk_bytes = score_elems * 4 + wl.B * wl.H * nb * keep * 4
+    score_flops = 2 * score_elems * wl.Dh
+    topk_ms = route_ms - scores_ms
+    subblock = {
+        "sparsity": sparsity, "blocks": nb, "keep": keep,
+        "pool": rate(pool_bytes, pool_ms),
+        "pool_head_major": rate(pool_bytes, pool_hm_ms),
+        "scores": {**rate(scores_bytes, scores_ms), "TFLOP_s": round(score_flops / (scores_ms * 1e-3) / 1e12, 1),
+                   "pct_of_bf16_mfma_peak": round(100.0 * score_flops / (scores_ms * 1e-3) / 2.5e15, 2)},
+        "topk": rate(topk_bytes, topk_ms),
+        "total_ms": round(pool_ms + route_ms, 5),
+    }
+    del qp_s, kp_s, sc, kept, kept0
+
     # A plain streaming copy on the same device: the practical ceiling.
     cbytes = 2 << 30
     src = torch.empty(cbytes, dtype=torch.uint8, device=dev)
@@ -344,6 +398,7 @@ def main(argv=None) -> int:
         "next_fused_residual_adaln": fused,
         "next_qk_layout": layout,
         "next_residual_change": change,
+        "next_subblock_routing": subblock,
         "block_mix_fused": block_mix_fused,
         "next_consistency": consistency,
     }

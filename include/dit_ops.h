@@ -248,6 +248,83 @@ dit_status dit_residual_change(const dit_bf16 *r, const dit_bf16 *r_cached,
 int64_t dit_residual_change_workspace_bytes(int64_t B, int64_t N, int64_t D);
 
 /*
+ * SubBlock sparse-attention routing, front-end.
+ * Cited: stamatios.com summary, "De onde vêm os ganhos" (SubBlock attention
+ * splits the sequence into 64-token blocks and routing keeps only part of the
+ * key blocks) and "Resultado principal" (the blocks dropped are those of
+ * smaller estimated contribution); xhh.club Q&A on the sparsity parameter
+ * (sparsity is the share of key blocks that may be dropped: 0.75 keeps about
+ * 25%).  Readings: a block is summarised by the mean of its tokens' q' (or k')
+ * head vectors; the estimated contribution of key block j to query block i is
+ * the dot product of the two means, rounded to bf16 first (the attention
+ * operands' precision), per sample and head, without a 1/sqrt(Dh) factor; ties
+ * are kept lowest index first.  Blocks never span two samples; the last block
+ * of a sample may be shorter and averages only its own tokens.
+ * The dense fallback for short calls and the first steps, and the sparse
+ * attention itself, are the caller's.
+ */
+#define DIT_SUBBLOCK_TOKENS 64
+
+/*
+ * Key blocks kept per query block for `nb` blocks at `sparsity`:
+ * nb - floor(sparsity * nb), at least 1 (0 when nb == 0); -1 if nb < 0 or
+ * sparsity is not in [0, 1).  Host-only; makes no HIP call.
+ */
+int64_t dit_subblock_keep(int64_t nb, double sparsity);
+
+/*
+ * Row stride (in floats) of the score matrix dit_subblock_route writes: nb
+ * rounded up to a multiple of 4; -1 if nb < 0 or nb > 4096.  Host-only.
+ */
+int64_t dit_subblock_scores_ld(int64_t nb);
+
+/*
+ * Block means of q' and k':
+ *   q_pooled[b][h][i][d] = mean of q[b][n][h][d] over the tokens n of block i
+ *   (n = 64 i .. min(64 i + 64, N) - 1), the same for k; fp32 sums of the
+ *   bf16 inputs, one fp32 division.
+ *   q, k      bf16, [B][N][H][Dh] for layout DIT_QK_TOKEN_MAJOR or
+ *             [B][H][N][Dh] for DIT_QK_HEAD_MAJOR (else DIT_ERR_ARG); may be
+ *             the same buffer
+ *   q_pooled, k_pooled
+ *             fp32 [B][H][nb][Dh], nb = ceil(N / 64), 16-byte aligned; they
+ *             overlap neither each other nor the inputs (DIT_ERR_ARG)
+ *   Dh in {16, 32, 64, 128, 256}, H*Dh <= 65536 (else DIT_ERR_SHAPE);
+ *   N <= 262,144 (4096 blocks) and B <= 65535 (else DIT_ERR_ARG).
+ * Deterministic: a fixed summation order per layout.  B == 0 or N == 0 is a
+ * no-op.
+ */
+dit_status dit_subblock_pool(const dit_bf16 *q, const dit_bf16 *k,
+                             float *q_pooled, float *k_pooled, int64_t B,
+                             int64_t N, int64_t H, int64_t Dh, int32_t layout,
+                             void *stream);
+
+/*
+ * Block scores and the kept key blocks of every query block:
+ *   scores[b][h][i][j] = sum_d bf16(q_pooled[b][h][i][d]) *
+ *                               bf16(k_pooled[b][h][j][d])
+ *   (round-to-nearest-even operands, fp32 accumulation on the matrix cores);
+ *   kept[b][h][i][0 .. keep-1] = the keep key blocks j of largest score (equal
+ *   scores: lower j first), in ascending order of j.
+ *   q_pooled, k_pooled  fp32 [B][H][nb][Dh], 16-byte aligned (as written by
+ *                       dit_subblock_pool); may be the same buffer
+ *   scores    fp32 [B][H][nb][ld], ld = dit_subblock_scores_ld(nb), 16-byte
+ *             aligned, an output; entries j >= nb of a row are not written
+ *   kept      int32 [B][H][nb][keep], 4-byte aligned; unused if keep == 0
+ *   keep      0 <= keep <= nb (else DIT_ERR_ARG); dit_subblock_keep gives the
+ *             count for a sparsity
+ *   Dh in {16, 32, 64, 128, 256}, H*Dh <= 65536 (else DIT_ERR_SHAPE);
+ *   nb <= 4096 and B <= 65535 (else DIT_ERR_ARG).
+ * Scores are expected finite; with NaN pooled values the kept lists are still
+ * keep distinct, ascending, in-range indices.  scores and kept overlap no
+ * other buffer (DIT_ERR_ARG).  Deterministic.  B == 0 or nb == 0 is a no-op.
+ */
+dit_status dit_subblock_route(const float *q_pooled, const float *k_pooled,
+                              float *scores, int32_t *kept, int64_t B,
+                              int64_t H, int64_t nb, int64_t Dh, int64_t keep,
+                              void *stream);
+
+/*
  * Packed token coordinates for the 3D rotary embedding.
  * Cited: stamatios.com summary, "Resultado principal" (video and audio tokens
  * in one packed DiT sequence); xhh.club Q&A ("3D RoPE").

@@ -169,6 +169,23 @@ def op_inputs(wl: Workload | str, op: str, device="cpu", seed: int = 0) -> dict:
     return make_inputs(wl, device, seed, OP_TENSORS[op])
 
 
+def correlated_heads(shape, seed: int = 0, run: int = 48, device="cpu") -> torch.Tensor:
+    """bf16 [B, N, H, Dh] head vectors with local correlation along the sequence.
+
+    Each token is 0.5 * N(0, 1) noise plus an offset N(0, 1) shared by the
+    ``run`` consecutive tokens it falls in (per sample and head), the way
+    neighbouring video tokens resemble each other.  Runs are not aligned to any
+    block size the consumer uses.
+    """
+    B, N, H, Dh = shape
+    g = torch.Generator(device=device)
+    g.manual_seed(seed * 1_000_003 + 101)
+    runs = -(-N // run) if N else 0
+    offset = torch.randn((B, runs, H, Dh), generator=g, device=device)
+    noise = torch.randn((B, N, H, Dh), generator=g, device=device) * 0.5
+    return (noise + offset.repeat_interleave(run, dim=1)[:, :N]).to(torch.bfloat16)
+
+
 def bits(t: torch.Tensor):
     """Raw bf16 bit patterns of a tensor as a host numpy uint16 array."""
     assert t.dtype == torch.bfloat16

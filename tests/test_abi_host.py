@@ -212,6 +212,55 @@ def test_residual_change_validation(lib):
     assert f(r=0, rc=0, out=0, w=0, B=0) == DIT_OK
 
 
+def test_subblock_keep_and_ld(lib):
+    keep = lib.dit_subblock_keep
+    assert keep(1953, 0.75) == 489 and keep(3914, 0.8) == 783 and keep(7, 0.5) == 4
+    assert keep(10, 0.0) == 10 and keep(100, 0.999) == 1 and keep(0, 0.75) == 0
+    assert keep(-1, 0.5) == -1 and keep(10, 1.0) == -1 and keep(10, -0.1) == -1 and keep(10, math.nan) == -1
+    ld = lib.dit_subblock_scores_ld
+    assert ld(1953) == 1956 and ld(4) == 4 and ld(1) == 4 and ld(0) == 0 and ld(4096) == 4096
+    assert ld(4097) == -1 and ld(-1) == -1
+
+
+def test_subblock_pool_validation(lib):
+    # B=1, N=128, H=2, Dh=16: inputs 8 KiB each, outputs 2*2*16 floats
+    def f(q=P, k=Q, qp=R, kp=S, B=1, N=128, H=2, Dh=16, layout=0):
+        return lib.dit_subblock_pool(q, k, qp, kp, B, N, H, Dh, layout, None)
+
+    assert f(B=-1, qp=0) == DIT_ERR_ARG
+    assert f(N=4096 * 64 + 1, qp=0) == DIT_ERR_ARG  # more than 4096 blocks
+    assert f(B=70000, qp=0) == DIT_ERR_ARG
+    assert f(layout=2) == DIT_ERR_ARG
+    assert f(Dh=8) == DIT_ERR_SHAPE and f(Dh=48) == DIT_ERR_SHAPE and f(Dh=512) == DIT_ERR_SHAPE
+    assert f(H=0) == DIT_ERR_SHAPE and f(H=4096, Dh=32) == DIT_ERR_SHAPE  # H*Dh beyond 65536
+    assert f(qp=0) == DIT_ERR_NULL and f(k=0) == DIT_ERR_NULL
+    assert f(q=P + 8) == DIT_ERR_ALIGN and f(kp=S + 4) == DIT_ERR_ALIGN
+    assert f(qp=P + 64) == DIT_ERR_ARG  # output inside q
+    assert f(kp=Q + 4096) == DIT_ERR_ARG  # output inside k
+    assert f(kp=R + 128) == DIT_ERR_ARG  # outputs overlap
+    assert f(q=0, k=0, qp=0, kp=0, N=0) == DIT_OK
+    assert f(q=0, k=0, qp=0, kp=0, B=0) == DIT_OK
+
+
+def test_subblock_route_validation(lib):
+    # B=1, H=2, nb=5, Dh=16: pooled 640 B each, scores 2*5*8 floats, kept 2*5*keep ints
+    def f(qp=P, kp=Q, sc=R, kept=S, B=1, H=2, nb=5, Dh=16, keep=2):
+        return lib.dit_subblock_route(qp, kp, sc, kept, B, H, nb, Dh, keep, None)
+
+    assert f(B=-1, sc=0) == DIT_ERR_ARG
+    assert f(nb=4097, sc=0) == DIT_ERR_ARG
+    assert f(keep=-1) == DIT_ERR_ARG
+    assert f(keep=6) == DIT_ERR_ARG  # more than nb
+    assert f(Dh=8) == DIT_ERR_SHAPE and f(Dh=100) == DIT_ERR_SHAPE and f(H=0) == DIT_ERR_SHAPE
+    assert f(sc=0) == DIT_ERR_NULL and f(kept=0) == DIT_ERR_NULL and f(qp=0) == DIT_ERR_NULL
+    assert f(qp=P + 4) == DIT_ERR_ALIGN and f(sc=R + 8) == DIT_ERR_ALIGN and f(kept=S + 2) == DIT_ERR_ALIGN
+    assert f(sc=P + 64) == DIT_ERR_ARG  # scores over q_pooled
+    assert f(kept=R + 16) == DIT_ERR_ARG  # kept over scores
+    assert f(kept=Q) == DIT_ERR_ARG  # kept over k_pooled
+    assert f(qp=0, kp=0, sc=0, kept=0, nb=0, keep=0) == DIT_OK
+    assert f(qp=0, kp=0, sc=0, kept=0, B=0) == DIT_OK
+
+
 def test_positions_validation(lib):
     f = lib.dit_packed_positions
     assert f(P, -1, 4, 4, 0, None) == DIT_ERR_ARG

@@ -1,0 +1,336 @@
+"""GPU parity of the SubBlock routing front-end against the fp64 oracle.
+
+Pooled means: fp32 sums of at most 64 bf16 values and one division, so each
+mean is within 64 u mean|x| + u |mean| of the exact one (u = 2^-24); the test
+allows twice that.
+
+Scores: the kernel multiplies the bf16-rounded fp32 means with fp32
+accumulation.  Against the oracle (bf16 rounding of the exact fp64 means, exact
+products, fp64 sum) two errors remain: the fp32 accumulation, at most
+Dh u sum_d |q~_d k~_d|, and a bf16 rounding that the pooling error can flip
+where a mean lies within its own bound of a rounding boundary.  The test
+computes both per score from the oracle's means and allows twice their sum.
+Where the pooled inputs are given exactly (route-only cases), no flip is
+possible.
+
+Kept blocks: several selections are correct where scores fall within their
+bounds of the keep-th largest.  Each selection must be keep distinct ascending
+in-range indices; every kept block must be able to outrank every dropped one
+within the bounds (so every block whose oracle score clears the boundary by
+more than the bounds is decided exactly as the oracle decides it); and under
+the kernel's own scores the selection must be a top-keep set with ties to the
+lower index.  On inputs whose products and sums are exact in fp32 the scores
+equal the oracle's and the kept lists must equal the oracle's bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import video_diffusion_transformer_dit_amd as dit
+from synthetic_inputs import WORKLOADS, bits, correlated_heads
+
+pytestmark = pytest.mark.gpu
+
+U = 2.0 ** -24
+DEV = "cuda"
+
+
+# --------------------------------------------------------------------------- bounds and checks
+
+def pool_bound(q_bits, ref):
+    """Per-element bound on |gpu mean - exact mean| for token-major bf16 bits q_bits [B,N,H,Dh]."""
+    mean_abs = oracle.subblock_pool(q_bits & np.uint16(0x7FFF))
+    return 2.0 * (64.0 * U * mean_abs + U * np.abs(ref)) + 1e-38
+
+
+def bf16_round(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(torch.bfloat16).to(torch.float64).numpy()
+
+
+def flip_room(mean, bound):
+    """Largest change of bf16(mean') over |mean' - mean| <= bound."""
+    r = bf16_round(mean)
+    return np.maximum(np.abs(bf16_round(mean + bound) - r), np.abs(bf16_round(mean - bound) - r))
+
+
+def score_bound(qp, kp, dq=None, dk=None):
+    """Bound on |gpu score - oracle score| for oracle means qp [B,H,nq,Dh], kp [B,H,nk,Dh]."""
+    qa, ka = np.abs(bf16_round(qp)), np.abs(bf16_round(kp))
+    Dh = qp.shape[-1]
+    e = Dh * U * np.matmul(qa, np.swapaxes(ka, -1, -2))
+    if dq is not None:
+        e = e + np.matmul(dq, np.swapaxes(ka, -1, -2)) + np.matmul(qa, np.swapaxes(dk, -1, -2)) \
+            + np.matmul(dq, np.swapaxes(dk, -1, -2))
+    return 2.0 * e + 1e-30
+
+
+def check_kept_lists(kept, nb, keep):
+    """Every row: keep distinct indices in [0, nb), ascending."""
+    assert kept.shape[-1] == keep
+    if keep == 0:
+        return
+    assert kept.min() >= 0 and kept.max() < nb
+    if keep > 1:
+        assert np.all(np.diff(kept, axis=-1) > 0), "kept lists not strictly ascending"
+
+
+def kept_mask(kept, nb):
+    mask = np.zeros(kept.shape[:-1] + (nb,), dtype=bool)
+    np.put_along_axis(mask, kept.astype(np.int64), True, axis=-1)
+    return mask
+
+
+def check_valid_against_oracle(kept, s_ref, e):
+    """Every kept block can outrank every dropped one within the bounds e."""
+    nb = s_ref.shape[-1]
+    keep = kept.shape[-1]
+    if keep in (0, nb):
+        return
+    mask = kept_mask(kept, nb)
+    lo_kept = np.where(mask, s_ref + e, np.inf).min(axis=-1)
+    hi_dropped = np.where(mask, -np.inf, s_ref - e).max(axis=-1)
+    bad = lo_kept < hi_dropped
+    assert not bad.any(), f"{bad.sum()} rows keep a block that is outranked beyond the bounds"
+
+
+def check_top_set_of_own_scores(kept, s_gpu):
+    """Under the kernel's own scores, the kept set is a top-keep set with ties to the lower index.
+
+    kept [B,H,nq,keep], s_gpu [B,H,nq,nb] (any float dtype); checked one head at a time.
+    """
+    nb = s_gpu.shape[-1]
+    keep = kept.shape[-1]
+    if keep in (0, nb):
+        if keep == nb:
+            assert np.array_equal(kept, np.broadcast_to(np.arange(nb), kept.shape))
+        return
+    idx = np.arange(nb)
+    for b in range(kept.shape[0]):
+        for h in range(kept.shape[1]):
+            sk, kk = s_gpu[b, h], kept[b, h]
+            mask = kept_mask(kk, nb)
+            t = np.where(mask, sk, np.inf).min(axis=-1, keepdims=True)  # smallest kept score
+            assert not np.any(~mask & (sk > t)), f"({b},{h}): a dropped block outscores a kept one"
+            last_tied_kept = np.where(mask & (sk == t), idx, -1).max(axis=-1)
+            first_tied_dropped = np.where(~mask & (sk == t), idx, nb).min(axis=-1)
+            assert np.all(last_tied_kept < first_tied_dropped), f"({b},{h}): a tie went to a higher index"
+
+
+def set_agreement(kept, kept_ref, nb):
+    """Mean share of each row's kept blocks that the oracle keeps too."""
+    keep = kept.shape[-1]
+    if keep == 0:
+        return 1.0
+    both = kept_mask(kept, nb) & kept_mask(kept_ref, nb)
+    return float(both.sum(axis=-1).mean() / keep)
+
+
+def to_host(t):
+    return t.cpu().numpy()
+
+
+# --------------------------------------------------------------------------- pooling
+
+POOL_SHAPES = [
+    # B, N, H, Dh
+    (1, 200, 2, 64),
+    (2, 321, 3, 16),    # ragged last block of 1 token; 6 vectors per token
+    (1, 130, 2, 256),
+    (1, 64, 1, 32),     # exactly one block
+    (1, 1, 4, 128),     # one token
+    (1, 100, 5, 128),   # 80 vectors per token: a partial second column chunk
+    (2, 1000, 4, 32),
+]
+
+
+@pytest.mark.parametrize("head_major", [False, True], ids=["token_major", "head_major"])
+@pytest.mark.parametrize("shape", POOL_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_pool_matches_oracle(shape, head_major):
+    B, N, H, Dh = shape
+    q = correlated_heads(shape, seed=11 + N, device=DEV)
+    k = correlated_heads(shape, seed=12 + N, device=DEV)
+    qin = q.permute(0, 2, 1, 3).contiguous() if head_major else q
+    kin = k.permute(0, 2, 1, 3).contiguous() if head_major else k
+    qp, kp = dit.dit_subblock_pool(qin, kin, head_major=head_major)
+    torch.cuda.synchronize()
+    for got, src in ((qp, q), (kp, k)):
+        ref = oracle.subblock_pool(bits(src))
+        err = np.abs(to_host(got).astype(np.float64) - ref)
+        bound = pool_bound(bits(src), ref)
+        assert np.all(err <= bound), f"worst err/bound {(err / bound).max():.3g}"
+
+
+def test_pool_layouts_and_repeats_agree():
+    shape = (2, 515, 4, 64)
+    q = correlated_heads(shape, seed=21, device=DEV)
+    k = correlated_heads(shape, seed=22, device=DEV)
+    a = dit.dit_subblock_pool(q, k)
+    b = dit.dit_subblock_pool(q, k)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])  # deterministic
+    # q and k may be the same buffer
+    c = dit.dit_subblock_pool(q, q)
+    torch.cuda.synchronize()
+    assert torch.equal(c[0], a[0]) and torch.equal(c[1], a[0])
+
+
+# --------------------------------------------------------------------------- route on given pooled means
+
+ROUTE_SHAPES = [
+    # B, H, nb, Dh
+    (1, 1, 1, 16),
+    (1, 2, 5, 32),
+    (2, 3, 64, 64),
+    (1, 2, 65, 128),
+    (1, 1, 130, 256),
+    (1, 2, 700, 128),
+    (1, 1, 2100, 64),   # more than 2048 blocks
+]
+
+
+def route_inputs(shape, seed):
+    g = torch.Generator().manual_seed(seed)
+    qp = torch.randn(shape, generator=g) * 0.25
+    kp = torch.randn(shape, generator=g) * 0.25
+    return qp, kp
+
+
+@pytest.mark.parametrize("shape", ROUTE_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_route_matches_oracle(shape):
+    B, H, nb, Dh = shape
+    qp, kp = route_inputs(shape, seed=31 + nb)
+    s_ref = oracle.subblock_scores(qp.double().numpy(), kp.double().numpy())
+    e = score_bound(qp.double().numpy(), kp.double().numpy())
+    qd, kd = qp.to(DEV), kp.to(DEV)
+    for keep in sorted({0, 1, max(1, nb // 4), nb - 1, nb} - {-1}):
+        if keep > nb or keep < 0:
+            continue
+        kept, scores = dit.dit_subblock_route(qd, kd, keep=keep)
+        torch.cuda.synchronize()
+        s_gpu = to_host(scores)[..., :nb].astype(np.float64)
+        err = np.abs(s_gpu - s_ref)
+        assert np.all(err <= e), f"keep {keep}: worst score err/bound {(err / e).max():.3g}"
+        kh = to_host(kept)
+        check_kept_lists(kh, nb, keep)
+        check_valid_against_oracle(kh, s_ref, e)
+        check_top_set_of_own_scores(kh, s_gpu)
+
+
+@pytest.mark.parametrize("nb", [7, 64, 200, 2100])
+def test_route_exact_scores_and_ties_bit_exact(nb):
+    # Means on a 1/8 grid: every product is a multiple of 1/64 and every sum of
+    # Dh of them stays below 2^10, so fp32 holds all scores exactly and the
+    # kernel's scores equal the oracle's.  Key blocks repeat a few rows, so
+    # most scores tie and the tie rule decides.
+    B, H, Dh = 1, 2, 32
+    rng = np.random.default_rng(nb)
+    qp = rng.integers(-16, 17, size=(B, H, nb, Dh)) / 8.0
+    rows = rng.integers(-16, 17, size=(B, H, 5, Dh)) / 8.0
+    kp = np.ascontiguousarray(rows[:, :, rng.integers(0, 5, size=nb)])
+    s_ref = oracle.subblock_scores(qp, kp)
+    qd = torch.from_numpy(qp).float().to(DEV)
+    kd = torch.from_numpy(kp).float().to(DEV)
+    for sparsity in (0.0, 0.5, 0.75, 0.8, 0.95):
+        keep = oracle.subblock_keep(nb, sparsity)
+        assert keep == dit.dit_subblock_keep(nb, sparsity)
+        kept, scores = dit.dit_subblock_route(qd, kd, sparsity=sparsity)
+        torch.cuda.synchronize()
+        assert np.array_equal(to_host(scores)[..., :nb].astype(np.float64), s_ref)
+        assert np.array_equal(to_host(kept), oracle.subblock_topk(s_ref, keep)), sparsity
+
+
+def test_route_special_values():
+    # all-zero means: every score is +0 or -0, all tie, the lowest indices are kept
+    B, H, nb, Dh = 1, 1, 9, 16
+    z = torch.zeros((B, H, nb, Dh), device=DEV)
+    zn = z.clone()
+    zn[0, 0, ::2] = -0.0
+    kept, scores = dit.dit_subblock_route(z, zn, keep=4)
+    torch.cuda.synchronize()
+    assert to_host(kept).tolist() == [[[list(range(4)) for _ in range(nb)]]]
+    # NaN in one key block: kept lists stay keep distinct ascending in-range indices
+    kn = torch.randn((B, H, nb, Dh), device=DEV)
+    kn[0, 0, 3, 5] = float("nan")
+    kept, _ = dit.dit_subblock_route(torch.randn((B, H, nb, Dh), device=DEV), kn, keep=4)
+    torch.cuda.synchronize()
+    check_kept_lists(to_host(kept), nb, 4)
+
+
+def test_route_deterministic_and_buffers_reused():
+    shape = (1, 3, 300, 128)
+    qp, kp = route_inputs(shape, seed=41)
+    qd, kd = qp.to(DEV), kp.to(DEV)
+    kept, scores = dit.dit_subblock_route(qd, kd, sparsity=0.75)
+    kept2 = torch.full_like(kept, -7)
+    scores2 = torch.full_like(scores, 3.0)
+    dit.dit_subblock_route(qd, kd, sparsity=0.75, scores=scores2, kept=kept2)
+    torch.cuda.synchronize()
+    assert torch.equal(kept, kept2) and torch.equal(scores[..., :300], scores2[..., :300])
+    # self-routing: q and k pooled from one buffer
+    k_self, _ = dit.dit_subblock_route(qd, qd, keep=10)
+    torch.cuda.synchronize()
+    check_kept_lists(to_host(k_self), 300, 10)
+
+
+# --------------------------------------------------------------------------- end to end: q', k' -> kept blocks
+
+def end_to_end(B, N, H, Dh, sparsity, seed, head_major=False, sample_rows=None, check_pool_blocks=None):
+    shape = (B, N, H, Dh)
+    q = correlated_heads(shape, seed=seed, device=DEV)
+    k = correlated_heads(shape, seed=seed + 1, device=DEV)
+    qin = q.permute(0, 2, 1, 3).contiguous() if head_major else q
+    kin = k.permute(0, 2, 1, 3).contiguous() if head_major else k
+    qp, kp = dit.dit_subblock_pool(qin, kin, head_major=head_major)
+    kept, scores = dit.dit_subblock_route(qp, kp, sparsity=sparsity)
+    torch.cuda.synchronize()
+    nb = qp.shape[2]
+    keep = dit.dit_subblock_keep(nb, sparsity)
+    del qin, kin
+
+    qb, kb = bits(q), bits(k)
+    del q, k
+    kp_ref = oracle.subblock_pool(kb)
+    dk = flip_room(kp_ref, pool_bound(kb, kp_ref))
+    err_k = np.abs(to_host(kp).astype(np.float64) - kp_ref)
+    assert np.all(err_k <= pool_bound(kb, kp_ref)), "k pooling"
+    rows = np.arange(nb) if sample_rows is None else np.unique(sample_rows)
+    # Tokens of the sampled query blocks only, in block order: each sampled
+    # block is a whole 64-token slice and only the sample's last block can be
+    # shorter (it sorts last), so pooling the concatenation pools each block.
+    qb_rows = np.concatenate([qb[:, 64 * i:64 * i + 64] for i in rows], axis=1)
+    qp_ref = oracle.subblock_pool(qb_rows)
+    q_bound = pool_bound(qb_rows, qp_ref)
+    dq = flip_room(qp_ref, q_bound)
+    qp_gpu = to_host(qp)[:, :, rows].astype(np.float64)
+    assert np.all(np.abs(qp_gpu - qp_ref) <= q_bound), "q pooling"
+
+    s_ref = oracle.subblock_scores(qp_ref, kp_ref)
+    e = score_bound(qp_ref, kp_ref, dq, dk)
+    s_all = to_host(scores)[..., :nb]
+    s_gpu = s_all[:, :, rows].astype(np.float64)
+    err = np.abs(s_gpu - s_ref)
+    assert np.all(err <= e), f"worst score err/bound {(err / e).max():.3g}"
+    kh = to_host(kept)
+    check_kept_lists(kh, nb, keep)
+    check_valid_against_oracle(kh[:, :, rows], s_ref, e)
+    check_top_set_of_own_scores(kh, s_all)
+    return set_agreement(kh[:, :, rows], oracle.subblock_topk(s_ref, keep), nb)
+
+
+@pytest.mark.parametrize("head_major", [False, True], ids=["token_major", "head_major"])
+def test_end_to_end_small(head_major):
+    agree = end_to_end(2, 64 * 37 + 29, 4, 64, 0.75, seed=51, head_major=head_major)
+    assert agree > 0.95
+
+
+@pytest.mark.parametrize("name", ["lowres", "full5s", "full10s"])
+def test_end_to_end_workload(name):
+    wl = WORKLOADS[name]
+    nb = -(-wl.N // 64)
+    rows = np.random.default_rng(61).choice(nb, size=12, replace=False)
+    rows = np.concatenate([rows, [0, nb - 1]])  # first and (short) last block
+    print(f"[subblock] {name}: N={wl.N} nb={nb} H={wl.H} Dh={wl.Dh}", flush=True)
+    agree = end_to_end(wl.B, wl.N, wl.H, wl.Dh, 0.75, seed=71, sample_rows=rows)
+    print(f"[subblock] {name}: kept-set agreement with the oracle {agree:.4f}", flush=True)
+    assert agree > 0.95

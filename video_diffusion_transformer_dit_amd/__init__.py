@@ -11,6 +11,8 @@ hand-written HIP kernels (``csrc/``; declarations in ``include/dit_ops.h``):
   dit_qk_rmsnorm_rope3d_layout  the same, reading q/k from a fused QKV buffer and
                           writing head-major outputs
   dit_residual_change     Cache-DiT statistic: sum |r - r_cached| / sum |r_cached| per sample
+  dit_subblock_pool       SubBlock routing: means of each 64-token block of q' and k'
+  dit_subblock_route      SubBlock routing: block scores and the kept key blocks per query block
   dit_packed_positions    (t, h, w) coordinates of a packed token sequence
   dit_copy16              plain 16-byte-vector copy (bandwidth ceiling)
 
@@ -26,6 +28,7 @@ from ._binding import (  # noqa: F401
     DIT_OK,
     DIT_QK_HEAD_MAJOR,
     DIT_QK_TOKEN_MAJOR,
+    DIT_SUBBLOCK_TOKENS,
     LIB_PATH,
     SIGNATURES,
     DitError,
@@ -40,6 +43,10 @@ from ._binding import (  # noqa: F401
     dit_residual_change,
     dit_residual_change_workspace_bytes,
     dit_status_str,
+    dit_subblock_keep,
+    dit_subblock_pool,
+    dit_subblock_route,
+    dit_subblock_scores_ld,
     dit_swiglu,
     load_library,
 )

@@ -33,6 +33,10 @@ SIGNATURES = {
     "dit_gated_residual_adaln": ([_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _F32, _P], ctypes.c_int),
     "dit_residual_change": ([_P, _P, _P, _P, _I64, _I64, _I64, _I64, _P], ctypes.c_int),
     "dit_residual_change_workspace_bytes": ([_I64, _I64, _I64], ctypes.c_int64),
+    "dit_subblock_keep": ([_I64, ctypes.c_double], ctypes.c_int64),
+    "dit_subblock_scores_ld": ([_I64], ctypes.c_int64),
+    "dit_subblock_pool": ([_P, _P, _P, _P, _I64, _I64, _I64, _I64, _I32, _P], ctypes.c_int),
+    "dit_subblock_route": ([_P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _P], ctypes.c_int),
     "dit_packed_positions": ([_P, _I64, _I64, _I64, _I64, _P], ctypes.c_int),
     "dit_copy16": ([_P, _P, _I64, _P], ctypes.c_int),
 }
@@ -261,6 +265,76 @@ def dit_residual_change(r, r_cached, out=None, workspace=None, stream=None):
             r.data_ptr(), r_cached.data_ptr(), out.data_ptr(), workspace.data_ptr(), nbytes, B, N, D,
             _stream(stream, dev)))
     return out
+
+
+DIT_SUBBLOCK_TOKENS = 64
+
+
+def dit_subblock_keep(nb: int, sparsity: float) -> int:
+    """Key blocks kept per query block: nb - floor(sparsity * nb), at least 1."""
+    keep = load_library().dit_subblock_keep(int(nb), float(sparsity))
+    if keep < 0:
+        raise ValueError(f"sparsity must be in [0, 1) and nb >= 0, got nb={nb}, sparsity={sparsity}")
+    return keep
+
+
+def dit_subblock_scores_ld(nb: int) -> int:
+    ld = load_library().dit_subblock_scores_ld(int(nb))
+    if ld < 0:
+        raise ValueError(f"unsupported block count {nb}")
+    return ld
+
+
+def dit_subblock_pool(q, k, head_major: bool = False, q_pooled=None, k_pooled=None, stream=None):
+    """Means of each 64-token block of q' and k' -> (q_pooled, k_pooled) fp32 [B,H,nb,Dh].
+
+    q, k are bf16 [B,N,H,Dh] (or [B,H,N,Dh] with ``head_major=True``); nb = ceil(N/64).
+    """
+    _tensor(q, "q", ndim=4)
+    if head_major:
+        B, H, N, Dh = q.shape
+    else:
+        B, N, H, Dh = q.shape
+    _shape(_tensor(k, "k"), "k", tuple(q.shape))
+    nb = -(-N // DIT_SUBBLOCK_TOKENS)
+    shape = (B, H, nb, Dh)
+    q_pooled = torch.empty(shape, dtype=torch.float32, device=q.device) if q_pooled is None else q_pooled
+    k_pooled = torch.empty(shape, dtype=torch.float32, device=q.device) if k_pooled is None else k_pooled
+    _shape(_tensor(q_pooled, "q_pooled", dtype=torch.float32), "q_pooled", shape)
+    _shape(_tensor(k_pooled, "k_pooled", dtype=torch.float32), "k_pooled", shape)
+    dev = _same_device(q, k, q_pooled, k_pooled)
+    with torch.cuda.device(dev):
+        _check("dit_subblock_pool", load_library().dit_subblock_pool(
+            q.data_ptr(), k.data_ptr(), q_pooled.data_ptr(), k_pooled.data_ptr(), B, N, H, Dh,
+            DIT_QK_HEAD_MAJOR if head_major else DIT_QK_TOKEN_MAJOR, _stream(stream, dev)))
+    return q_pooled, k_pooled
+
+
+def dit_subblock_route(q_pooled, k_pooled, sparsity: float | None = None, keep: int | None = None, scores=None,
+                       kept=None, stream=None):
+    """Block scores and kept key blocks from pooled q', k' fp32 [B,H,nb,Dh].
+
+    Give ``sparsity`` (share of key blocks dropped) or ``keep`` (count kept).  Returns (kept, scores):
+    kept int32 [B,H,nb,keep] ascending per query block; scores fp32 [B,H,nb,ld] whose first nb
+    columns hold the scores (ld = dit_subblock_scores_ld(nb)).
+    """
+    _tensor(q_pooled, "q_pooled", dtype=torch.float32, ndim=4)
+    B, H, nb, Dh = q_pooled.shape
+    _shape(_tensor(k_pooled, "k_pooled", dtype=torch.float32), "k_pooled", (B, H, nb, Dh))
+    if (sparsity is None) == (keep is None):
+        raise ValueError("give exactly one of sparsity and keep")
+    keep = dit_subblock_keep(nb, sparsity) if keep is None else int(keep)
+    ld = dit_subblock_scores_ld(nb)
+    scores = torch.empty((B, H, nb, ld), dtype=torch.float32, device=q_pooled.device) if scores is None else scores
+    kept = torch.empty((B, H, nb, keep), dtype=torch.int32, device=q_pooled.device) if kept is None else kept
+    _shape(_tensor(scores, "scores", dtype=torch.float32), "scores", (B, H, nb, ld))
+    _shape(_tensor(kept, "kept", dtype=torch.int32), "kept", (B, H, nb, keep))
+    dev = _same_device(q_pooled, k_pooled, scores, kept)
+    with torch.cuda.device(dev):
+        _check("dit_subblock_route", load_library().dit_subblock_route(
+            q_pooled.data_ptr(), k_pooled.data_ptr(), scores.data_ptr(), kept.data_ptr(), B, H, nb, Dh, keep,
+            _stream(stream, dev)))
+    return kept, scores
 
 
 def dit_packed_positions(T: int, Hg: int, Wg: int, n_extra: int = 0, pos=None, device=None, stream=None):

@@ -262,6 +262,82 @@ dit_status dit_residual_change(const dit_bf16 *r, const dit_bf16 *r_cached, doub
     return launched(dit::launch_residual_change(r, r_cached, out, workspace, B, N, D, (hipStream_t)stream));
 }
 
+// SubBlock routing: at most 4096 blocks of 64 tokens per sample (262,144 tokens).
+constexpr int64_t kMaxSubBlocks = 4096;
+
+static bool subblock_head_ok(int64_t H, int64_t Dh)
+{
+    const bool dh_ok = Dh == 16 || Dh == 32 || Dh == 64 || Dh == 128 || Dh == 256;
+    return dh_ok && H >= 1 && H * Dh <= kMaxHeadRow;
+}
+
+int64_t dit_subblock_keep(int64_t nb, double sparsity)
+{
+    if (nb < 0 || !(sparsity >= 0.0) || !(sparsity < 1.0))
+        return -1;
+    if (nb == 0)
+        return 0;
+    const int64_t keep = nb - (int64_t)floor(sparsity * (double)nb);
+    return keep < 1 ? 1 : keep;
+}
+
+int64_t dit_subblock_scores_ld(int64_t nb)
+{
+    if (nb < 0 || nb > kMaxSubBlocks)
+        return -1;
+    return (nb + 3) / 4 * 4;
+}
+
+dit_status dit_subblock_pool(const dit_bf16 *q, const dit_bf16 *k, float *q_pooled, float *k_pooled, int64_t B,
+                             int64_t N, int64_t H, int64_t Dh, int32_t layout, void *stream)
+{
+    if (B < 0 || N < 0 || H < 0 || Dh < 0 || B > kMaxSamples || N > kMaxSubBlocks * DIT_SUBBLOCK_TOKENS)
+        return DIT_ERR_ARG;
+    if (layout != DIT_QK_TOKEN_MAJOR && layout != DIT_QK_HEAD_MAJOR)
+        return DIT_ERR_ARG;
+    if (!subblock_head_ok(H, Dh))
+        return DIT_ERR_SHAPE;
+    if (B == 0 || N == 0)
+        return DIT_OK;
+    if (!q || !k || !q_pooled || !k_pooled)
+        return DIT_ERR_NULL;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(q_pooled, 16) || !aligned(k_pooled, 16))
+        return DIT_ERR_ALIGN;
+    const int64_t nb = (N + DIT_SUBBLOCK_TOKENS - 1) / DIT_SUBBLOCK_TOKENS;
+    const int64_t ni = B * N * H * Dh * 2, no = B * H * nb * Dh * 4;
+    // q and k may be one buffer (they are only read); the outputs overlap nothing.
+    if (overlap(q_pooled, no, k_pooled, no) || overlap(q_pooled, no, q, ni) || overlap(q_pooled, no, k, ni) ||
+        overlap(k_pooled, no, q, ni) || overlap(k_pooled, no, k, ni))
+        return DIT_ERR_ARG;
+    return launched(dit::launch_subblock_pool(q, k, q_pooled, k_pooled, B, N, H, Dh, layout == DIT_QK_HEAD_MAJOR,
+                                              (hipStream_t)stream));
+}
+
+dit_status dit_subblock_route(const float *q_pooled, const float *k_pooled, float *scores, int32_t *kept, int64_t B,
+                              int64_t H, int64_t nb, int64_t Dh, int64_t keep, void *stream)
+{
+    if (B < 0 || H < 0 || nb < 0 || Dh < 0 || keep < 0 || B > kMaxSamples || nb > kMaxSubBlocks)
+        return DIT_ERR_ARG;
+    if (!subblock_head_ok(H, Dh))
+        return DIT_ERR_SHAPE;
+    if (keep > nb)
+        return DIT_ERR_ARG;
+    if (B == 0 || nb == 0)
+        return DIT_OK;
+    if (!q_pooled || !k_pooled || !scores || (keep > 0 && !kept))
+        return DIT_ERR_NULL;
+    if (!aligned(q_pooled, 16) || !aligned(k_pooled, 16) || !aligned(scores, 16) || (keep > 0 && !aligned(kept, 4)))
+        return DIT_ERR_ALIGN;
+    const int64_t ld = dit_subblock_scores_ld(nb);
+    const int64_t np = B * H * nb * Dh * 4, ns = B * H * nb * ld * 4, nk = B * H * nb * keep * 4;
+    if (overlap(scores, ns, q_pooled, np) || overlap(scores, ns, k_pooled, np))
+        return DIT_ERR_ARG;
+    if (keep > 0 && (overlap(kept, nk, scores, ns) || overlap(kept, nk, q_pooled, np) || overlap(kept, nk, k_pooled, np)))
+        return DIT_ERR_ARG;
+    return launched(
+        dit::launch_subblock_route(q_pooled, k_pooled, scores, kept, B, H, nb, Dh, ld, keep, (hipStream_t)stream));
+}
+
 dit_status dit_packed_positions(int32_t *pos, int64_t T, int64_t Hg, int64_t Wg, int64_t n_extra, void *stream)
 {
     if (T < 0 || Hg < 0 || Wg < 0 || n_extra < 0 || n_extra > kMaxRows)

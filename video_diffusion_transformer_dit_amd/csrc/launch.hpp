@@ -41,6 +41,17 @@ int64_t residual_change_tiles(int64_t N, int64_t D);
 hipError_t launch_residual_change(const void *r, const void *r_cached, double *out, void *workspace, int64_t B,
                                   int64_t N, int64_t D, hipStream_t stream);
 
+// Means of each 64-token block of q and of k, per sample and head: [B][H][ceil(N/64)][Dh] fp32.
+// Inputs [B][N][H][Dh] (token-major) or [B][H][N][Dh] (head_major); Dh in {16,...,256}, power of two.
+hipError_t launch_subblock_pool(const void *q, const void *k, float *q_pooled, float *k_pooled, int64_t B, int64_t N,
+                                int64_t H, int64_t Dh, bool head_major, hipStream_t stream);
+
+// Block scores [B][H][nb][ld] (bf16 operands, fp32 accumulation) and, for keep > 0, the keep
+// highest-scoring key blocks of every query block, ascending: kept [B][H][nb][keep].
+hipError_t launch_subblock_route(const float *q_pooled, const float *k_pooled, float *scores, int32_t *kept,
+                                 int64_t B, int64_t H, int64_t nb, int64_t Dh, int64_t ld, int64_t keep,
+                                 hipStream_t stream);
+
 // Packed (t, h, w) coordinates of T*Hg*Wg video tokens then n_extra tokens.
 hipError_t launch_packed_positions(int32_t *pos, int64_t T, int64_t Hg, int64_t Wg, int64_t n_extra,
                                    hipStream_t stream);

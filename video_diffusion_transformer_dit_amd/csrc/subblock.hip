@@ -1,0 +1,414 @@
+// subblock.hip -- front-end of the SubBlock sparse-attention router:
+//   1. block pooling:  per sample and head, the mean of each 64-token block of
+//      q' and of k' (after RMSNorm + RoPE), as fp32;
+//   2. block scores:   s[i][j] = bf16(qp[i]) . bf16(kp[j]) per sample and head,
+//      on the matrix cores (bf16 operands, fp32 accumulation);
+//   3. kept blocks:    per query block, the `keep` key blocks of largest score
+//      (ties to the lower index), listed in ascending order.
+//
+// SubBlock attention cuts the sequence into 64-token blocks and keeps only part
+// of the key blocks, dropping those of smaller estimated contribution
+// ("SGLang acelera vídeo do MiniMax-H3…", stamatios.com, "De onde vêm os
+// ganhos" and "Resultado principal"); sparsity is the dropped share, so 0.75
+// keeps about a quarter ("8×H200 上的 MiniMax-H3…", xhh.club, Q&A on the
+// sparsity parameter).
+//
+// Roofline per step (1344x768 5 s: 124,992 tokens, 1953 blocks, 32 x 128 heads):
+//   pooling reads q' and k' once (2 x 1.02 GB) and writes 2 x 32 MB: HBM-bound;
+//   scores are a batched 1953 x 1953 x 128 product per head (31 GFLOP, bf16
+//   matrix cores) whose cost is writing 488 MB of fp32 scores;
+//   selection reads the scores once and writes the kept indices.
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace dit {
+namespace {
+
+constexpr int kBlockTokens = 64;
+
+// ---------------------------------------------------------------- pooling
+
+__device__ __forceinline__ void add8(float acc[8], u32x4 v)
+{
+    float f[8];
+    unpack8(v, f);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        acc[i] += f[i];
+}
+
+__device__ __forceinline__ void store_mean8(float *o, const float acc[8], float count)
+{
+    float4 *o4 = reinterpret_cast<float4 *>(o);
+    o4[0] = make_float4(acc[0] / count, acc[1] / count, acc[2] / count, acc[3] / count);
+    o4[1] = make_float4(acc[4] / count, acc[5] / count, acc[6] / count, acc[7] / count);
+}
+
+// Token-major input [B][N][H][Dh], C = H*Dh/8 16-byte vectors per token.
+// grid (chunks * nb, 2 (q then k), B), 256 threads.  A workgroup pools one
+// 64-vector column chunk of one block: lane = vector column, wave w adds tokens
+// w, w+4, ..., w+60 (sixteen loads in flight), then wave 0 adds the other
+// waves' partials in order and writes the means.
+__global__ __launch_bounds__(256) void subblock_pool_token_major_kernel(const u32x4 *__restrict__ q,
+                                                                        const u32x4 *__restrict__ k,
+                                                                        float *__restrict__ qp,
+                                                                        float *__restrict__ kp, int N, int nb,
+                                                                        int C, int chunks, int vph_shift)
+{
+    constexpr int kWaves = 4, kPerWave = kBlockTokens / kWaves;
+    __shared__ float4 part[kWaves - 1][2][kWave];
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    const int chunk = blockIdx.x % chunks, blk = blockIdx.x / chunks;
+    const size_t b = blockIdx.z;
+    const u32x4 *src = blockIdx.y ? k : q;
+    float *dst = blockIdx.y ? kp : qp;
+    const int c = chunk * kWave + lane;
+    const int n0 = blk * kBlockTokens;
+    const int count = min(kBlockTokens, N - n0);
+
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (c < C) {
+        const u32x4 *base = src + ((size_t)b * N + n0) * C + c;
+        u32x4 v[kPerWave];
+#pragma unroll
+        for (int t = 0; t < kPerWave; ++t) {
+            const int n = wave + kWaves * t; // wave-uniform
+            v[t] = n < count ? load_stream(base + (size_t)n * C) : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int t = 0; t < kPerWave; ++t)
+            add8(acc, v[t]);
+    }
+    if (wave > 0) {
+        part[wave - 1][0][lane] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+        part[wave - 1][1][lane] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+    }
+    __syncthreads();
+    if (wave == 0 && c < C) {
+#pragma unroll
+        for (int w = 0; w < kWaves - 1; ++w) {
+            const float4 lo = part[w][0][lane], hi = part[w][1][lane];
+            acc[0] += lo.x, acc[1] += lo.y, acc[2] += lo.z, acc[3] += lo.w;
+            acc[4] += hi.x, acc[5] += hi.y, acc[6] += hi.z, acc[7] += hi.w;
+        }
+        const int H = C >> vph_shift;
+        const int h = c >> vph_shift, dv = c & ((1 << vph_shift) - 1);
+        const int Dh = 8 << vph_shift;
+        store_mean8(dst + (((size_t)b * H + h) * nb + blk) * Dh + dv * 8, acc, (float)count);
+    }
+}
+
+// Head-major input [B][H][N][Dh]: a block of one head is 64*Dh contiguous
+// values.  grid (nb, 2*H (q heads then k heads), B), 256 threads.  Thread t
+// reads vectors t, t+256, ... of the block; with VPT = Dh/8 vectors per token
+// every one of them is column t % VPT.  Lanes of one column are summed with
+// lane swaps, then the four waves through LDS in order.
+template <int VPT>
+__global__ __launch_bounds__(256) void subblock_pool_head_major_kernel(const u32x4 *__restrict__ q,
+                                                                       const u32x4 *__restrict__ k,
+                                                                       float *__restrict__ qp,
+                                                                       float *__restrict__ kp, int N, int nb, int H)
+{
+    constexpr int kVectors = kBlockTokens * VPT;              // per block of one head
+    constexpr int kLoads = kVectors >= 256 ? kVectors / 256 : 1;
+    constexpr int kDh = VPT * 8;
+    __shared__ float4 part[4][2][VPT];
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    const int blk = blockIdx.x;
+    const bool is_k = blockIdx.y >= (unsigned)H;
+    const int h = is_k ? blockIdx.y - H : blockIdx.y;
+    const size_t b = blockIdx.z;
+    const u32x4 *src = (is_k ? k : q) + (((size_t)b * H + h) * N + (size_t)blk * kBlockTokens) * VPT;
+    const int count = min(kBlockTokens, N - blk * kBlockTokens);
+
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    u32x4 v[kLoads];
+#pragma unroll
+    for (int u = 0; u < kLoads; ++u) {
+        const int e = threadIdx.x + 256 * u;
+        v[u] = (e < kVectors && e / VPT < count) ? load_stream(src + e) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < kLoads; ++u)
+        add8(acc, v[u]);
+    // lanes l, l + VPT, l + 2 VPT, ... hold the same column
+#pragma unroll
+    for (int off = VPT; off < kWave; off <<= 1)
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            acc[i] += __shfl_xor(acc[i], off, kWave);
+    if (lane < VPT) {
+        part[wave][0][lane] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+        part[wave][1][lane] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+    }
+    __syncthreads();
+    if (threadIdx.x < VPT) {
+        float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const float4 lo = part[w][0][threadIdx.x], hi = part[w][1][threadIdx.x];
+            s[0] += lo.x, s[1] += lo.y, s[2] += lo.z, s[3] += lo.w;
+            s[4] += hi.x, s[5] += hi.y, s[6] += hi.z, s[7] += hi.w;
+        }
+        float *dst = is_k ? kp : qp;
+        store_mean8(dst + (((size_t)b * H + h) * nb + blk) * kDh + threadIdx.x * 8, s, (float)count);
+    }
+}
+
+// ---------------------------------------------------------------- scores
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kScoreTile = 64;
+
+// grid (tiles * tiles, H, B), 256 threads; tiles = ceil(nb / 64).  A
+// workgroup computes a 64 x 64 tile of one head's score matrix: both 64-row
+// operand tiles are rounded to bf16 into LDS (rows padded by 4 values so the
+// 16 rows one MFMA reads fall in different banks), then wave w multiplies
+// query rows 16w .. 16w+15 with all 64 key rows, Dh/16 MFMA 16x16x16 steps
+// per 16 x 16 output tile.  Operand layout of v_mfma_f32_16x16x16_bf16: lane l
+// supplies row l % 16, reduction elements 4(l/16) .. 4(l/16)+3 of A and of B;
+// it receives output rows 4(l/16) .. +3 of column l % 16.
+template <int DH>
+__global__ __launch_bounds__(256) void subblock_scores_kernel(const float *__restrict__ qp,
+                                                              const float *__restrict__ kp,
+                                                              float *__restrict__ scores, int nb, int ld, int tiles,
+                                                              int H)
+{
+    constexpr int kRow = DH + 4; // bf16 per padded LDS row
+    constexpr int kF4PerRow = DH / 4;
+    __shared__ __align__(16) uint16_t lds_q[kScoreTile * kRow];
+    __shared__ __align__(16) uint16_t lds_k[kScoreTile * kRow];
+
+    const int ti = blockIdx.x / tiles, tj = blockIdx.x % tiles;
+    const size_t bh = (size_t)blockIdx.z * H + blockIdx.y;
+    const float4 *qa = reinterpret_cast<const float4 *>(qp + (bh * nb + (size_t)ti * kScoreTile) * DH);
+    const float4 *kb = reinterpret_cast<const float4 *>(kp + (bh * nb + (size_t)tj * kScoreTile) * DH);
+    const int q_rows = min(kScoreTile, nb - ti * kScoreTile);
+    const int k_rows = min(kScoreTile, nb - tj * kScoreTile);
+
+    for (int e = threadIdx.x; e < kScoreTile * kF4PerRow; e += 256) {
+        const int r = e / kF4PerRow, c4 = e % kF4PerRow;
+        const float4 a = r < q_rows ? qa[e] : make_float4(0.f, 0.f, 0.f, 0.f);
+        const float4 c = r < k_rows ? kb[e] : make_float4(0.f, 0.f, 0.f, 0.f);
+        uint2 pa, pc;
+        pa.x = pack_bf16x2(a.x, a.y), pa.y = pack_bf16x2(a.z, a.w);
+        pc.x = pack_bf16x2(c.x, c.y), pc.y = pack_bf16x2(c.z, c.w);
+        *reinterpret_cast<uint2 *>(&lds_q[r * kRow + 4 * c4]) = pa;
+        *reinterpret_cast<uint2 *>(&lds_k[r * kRow + 4 * c4]) = pc;
+    }
+    __syncthreads();
+
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    const int r16 = lane & 15, quad = lane >> 4;
+    f32x4 acc[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+        acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < DH / 16; ++s) {
+        const int kof = 16 * s + 4 * quad;
+        const s16x4 a = *reinterpret_cast<const s16x4 *>(&lds_q[(16 * wave + r16) * kRow + kof]);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const s16x4 bv = *reinterpret_cast<const s16x4 *>(&lds_k[(16 * t + r16) * kRow + kof]);
+            acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, bv, acc[t], 0, 0, 0);
+        }
+    }
+
+    float *out = scores + (bh * nb + (size_t)ti * kScoreTile) * ld + (size_t)tj * kScoreTile;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int row = 16 * wave + 4 * quad + e, col = 16 * t + r16;
+            if (row < q_rows && col < k_rows)
+                out[(size_t)row * ld + col] = acc[t][e];
+        }
+}
+
+// ---------------------------------------------------------------- selection
+
+// Order-preserving map of an fp32 score to an unsigned key; -0 and +0 map to
+// the same key so that they tie, as equal scores do.
+__device__ __forceinline__ uint32_t score_key(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    u = (u == 0x80000000u) ? 0u : u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ int lanes_below(uint64_t mask)
+{
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+// One wave (one workgroup) per query block; grid (nb, H, B).  Lane l holds the
+// keys of key blocks l, l + 64, ..., l + 64 (R - 1) in registers.  A radix
+// select over four 8-bit digits, most significant first, finds the keep-th
+// largest key T and how many keys equal to T are kept (LDS histogram of the
+// keys that still match the chosen prefix, then a suffix scan across lanes).
+// The kept blocks are those above T plus the lowest-indexed keys equal to T;
+// they are written in ascending order with ballots.
+template <int R>
+__global__ __launch_bounds__(kWave) void subblock_topk_kernel(const float *__restrict__ scores,
+                                                              int32_t *__restrict__ kept, int nb, int ld, int keep,
+                                                              int H)
+{
+    __shared__ __align__(16) uint32_t hist[256];
+    const int lane = threadIdx.x;
+    const size_t row = ((size_t)blockIdx.z * H + blockIdx.y) * nb + blockIdx.x;
+    const float *s = scores + row * ld;
+    int32_t *out = kept + row * keep;
+
+    uint32_t key[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int j = lane + kWave * r;
+        key[r] = j < nb ? score_key(__builtin_nontemporal_load(s + j)) : 0u;
+    }
+
+    uint32_t prefix = 0u, mask = 0u;
+    uint32_t need = (uint32_t)keep;
+#pragma unroll 1
+    for (int pass = 0; pass < 4; ++pass) {
+        const int shift = 24 - 8 * pass;
+        reinterpret_cast<uint4 *>(hist)[lane] = make_uint4(0u, 0u, 0u, 0u);
+        __syncthreads();
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int j = lane + kWave * r;
+            if (j < nb && (key[r] & mask) == prefix)
+                atomicAdd(&hist[(key[r] >> shift) & 0xffu], 1u);
+        }
+        __syncthreads();
+        const uint4 h4 = reinterpret_cast<const uint4 *>(hist)[lane]; // digits 4l .. 4l+3
+        const uint32_t c = h4.x + h4.y + h4.z + h4.w;
+        uint32_t suffix = c; // keys of digits >= 4l
+#pragma unroll
+        for (int off = 1; off < kWave; off <<= 1) {
+            const uint32_t o = __shfl_down(suffix, off, kWave);
+            suffix += (lane + off < kWave) ? o : 0u;
+        }
+        const uint32_t above = suffix - c;
+        const bool mine = above < need && need <= suffix; // exactly one lane
+        uint32_t digit = 4u * lane, greater = above;
+        if (mine) {
+            if (above + h4.w >= need) {
+                digit += 3u;
+            } else if (above + h4.w + h4.z >= need) {
+                digit += 2u, greater += h4.w;
+            } else if (above + h4.w + h4.z + h4.y >= need) {
+                digit += 1u, greater += h4.w + h4.z;
+            } else {
+                greater += h4.w + h4.z + h4.y;
+            }
+        }
+        const int src = __builtin_ctzll(__ballot(mine));
+        digit = __builtin_amdgcn_readlane(digit, src);
+        greater = __builtin_amdgcn_readlane(greater, src);
+        prefix |= digit << shift;
+        mask |= 0xffu << shift;
+        need -= greater;
+        __syncthreads(); // every lane has read the histogram before it is cleared
+    }
+
+    // prefix is now the keep-th largest key; `need` keys equal to it are kept.
+    uint32_t written = 0u, ties = 0u;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int j = lane + kWave * r;
+        const bool valid = j < nb;
+        const bool eq = valid && key[r] == prefix;
+        const uint64_t eq_mask = __ballot(eq);
+        const bool sel = (valid && key[r] > prefix) || (eq && ties + (uint32_t)lanes_below(eq_mask) < need);
+        const uint64_t sel_mask = __ballot(sel);
+        const uint32_t at = written + (uint32_t)lanes_below(sel_mask);
+        if (sel && at < (uint32_t)keep) // exactly keep are selected; the bound only guards the store
+            out[at] = j;
+        written += (uint32_t)__builtin_popcountll(sel_mask);
+        ties += (uint32_t)__builtin_popcountll(eq_mask);
+    }
+}
+
+template <int R>
+void launch_topk_r(const float *scores, int32_t *kept, int nb, int ld, int keep, int H, int B, hipStream_t stream)
+{
+    hipLaunchKernelGGL(subblock_topk_kernel<R>, dim3((unsigned)nb, (unsigned)H, (unsigned)B), dim3(kWave), 0, stream,
+                       scores, kept, nb, ld, keep, H);
+}
+
+template <int DH>
+void launch_scores_dh(const float *qp, const float *kp, float *scores, int nb, int ld, int H, int B,
+                      hipStream_t stream)
+{
+    const int tiles = (nb + kScoreTile - 1) / kScoreTile;
+    hipLaunchKernelGGL(subblock_scores_kernel<DH>, dim3((unsigned)(tiles * tiles), (unsigned)H, (unsigned)B),
+                       dim3(256), 0, stream, qp, kp, scores, nb, ld, tiles, H);
+}
+
+template <int VPT>
+void launch_pool_head_major(const u32x4 *q, const u32x4 *k, float *qp, float *kp, int N, int nb, int H, int B,
+                            hipStream_t stream)
+{
+    hipLaunchKernelGGL(subblock_pool_head_major_kernel<VPT>, dim3((unsigned)nb, (unsigned)(2 * H), (unsigned)B),
+                       dim3(256), 0, stream, q, k, qp, kp, N, nb, H);
+}
+
+} // namespace
+
+hipError_t launch_subblock_pool(const void *q, const void *k, float *q_pooled, float *k_pooled, int64_t B, int64_t N,
+                                int64_t H, int64_t Dh, bool head_major, hipStream_t stream)
+{
+    const int nb = (int)((N + kBlockTokens - 1) / kBlockTokens);
+    const auto *qv = static_cast<const u32x4 *>(q);
+    const auto *kv = static_cast<const u32x4 *>(k);
+    const int vph = (int)(Dh / 8);
+    if (!head_major) {
+        const int C = (int)(H * Dh / 8);
+        const int chunks = (C + kWave - 1) / kWave;
+        const int vph_shift = __builtin_ctz((unsigned)vph);
+        hipLaunchKernelGGL(subblock_pool_token_major_kernel, dim3((unsigned)(chunks * nb), 2u, (unsigned)B),
+                           dim3(256), 0, stream, qv, kv, q_pooled, k_pooled, (int)N, nb, C, chunks, vph_shift);
+        return hipGetLastError();
+    }
+    const int h = (int)H, n = (int)N, b = (int)B;
+    switch (vph) {
+    case 2: launch_pool_head_major<2>(qv, kv, q_pooled, k_pooled, n, nb, h, b, stream); break;
+    case 4: launch_pool_head_major<4>(qv, kv, q_pooled, k_pooled, n, nb, h, b, stream); break;
+    case 8: launch_pool_head_major<8>(qv, kv, q_pooled, k_pooled, n, nb, h, b, stream); break;
+    case 16: launch_pool_head_major<16>(qv, kv, q_pooled, k_pooled, n, nb, h, b, stream); break;
+    case 32: launch_pool_head_major<32>(qv, kv, q_pooled, k_pooled, n, nb, h, b, stream); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_subblock_route(const float *q_pooled, const float *k_pooled, float *scores, int32_t *kept,
+                                 int64_t B, int64_t H, int64_t nb, int64_t Dh, int64_t ld, int64_t keep,
+                                 hipStream_t stream)
+{
+    const int n = (int)nb, l = (int)ld, h = (int)H, b = (int)B;
+    switch (Dh) {
+    case 16: launch_scores_dh<16>(q_pooled, k_pooled, scores, n, l, h, b, stream); break;
+    case 32: launch_scores_dh<32>(q_pooled, k_pooled, scores, n, l, h, b, stream); break;
+    case 64: launch_scores_dh<64>(q_pooled, k_pooled, scores, n, l, h, b, stream); break;
+    case 128: launch_scores_dh<128>(q_pooled, k_pooled, scores, n, l, h, b, stream); break;
+    case 256: launch_scores_dh<256>(q_pooled, k_pooled, scores, n, l, h, b, stream); break;
+    default: return hipErrorInvalidValue;
+    }
+    if (keep == 0)
+        return hipGetLastError();
+    const int kp = (int)keep;
+    if (n <= 64) launch_topk_r<1>(scores, kept, n, l, kp, h, b, stream);
+    else if (n <= 128) launch_topk_r<2>(scores, kept, n, l, kp, h, b, stream);
+    else if (n <= 256) launch_topk_r<4>(scores, kept, n, l, kp, h, b, stream);
+    else if (n <= 512) launch_topk_r<8>(scores, kept, n, l, kp, h, b, stream);
+    else if (n <= 1024) launch_topk_r<16>(scores, kept, n, l, kp, h, b, stream);
+    else if (n <= 2048) launch_topk_r<32>(scores, kept, n, l, kp, h, b, stream);
+    else launch_topk_r<64>(scores, kept, n, l, kp, h, b, stream);
+    return hipGetLastError();
+}
+
+} // namespace dit
