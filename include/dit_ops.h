@@ -274,7 +274,8 @@ int64_t dit_subblock_keep(int64_t nb, double sparsity);
 
 /*
  * Row stride (in floats) of the score matrix dit_subblock_route writes: nb
- * rounded up to a multiple of 4; -1 if nb < 0 or nb > 4096.  Host-only.
+ * rounded up to a multiple of 32, so that every row starts on a 128-byte line;
+ * -1 if nb < 0 or nb > 4096.  Host-only.
  */
 int64_t dit_subblock_scores_ld(int64_t nb);
 
@@ -309,7 +310,8 @@ dit_status dit_subblock_pool(const dit_bf16 *q, const dit_bf16 *k,
  *   q_pooled, k_pooled  fp32 [B][H][nb][Dh], 16-byte aligned (as written by
  *                       dit_subblock_pool); may be the same buffer
  *   scores    fp32 [B][H][nb][ld], ld = dit_subblock_scores_ld(nb), 16-byte
- *             aligned, an output; entries j >= nb of a row are not written
+ *             aligned, an output; entries j >= nb of a row are unspecified
+ *             (the kernel may write them)
  *   kept      int32 [B][H][nb][keep], 4-byte aligned; unused if keep == 0
  *   keep      0 <= keep <= nb (else DIT_ERR_ARG); dit_subblock_keep gives the
  *             count for a sparsity

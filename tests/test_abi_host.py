@@ -218,7 +218,7 @@ def test_subblock_keep_and_ld(lib):
     assert keep(10, 0.0) == 10 and keep(100, 0.999) == 1 and keep(0, 0.75) == 0
     assert keep(-1, 0.5) == -1 and keep(10, 1.0) == -1 and keep(10, -0.1) == -1 and keep(10, math.nan) == -1
     ld = lib.dit_subblock_scores_ld
-    assert ld(1953) == 1956 and ld(4) == 4 and ld(1) == 4 and ld(0) == 0 and ld(4096) == 4096
+    assert ld(1953) == 1984 and ld(32) == 32 and ld(1) == 32 and ld(0) == 0 and ld(4096) == 4096
     assert ld(4097) == -1 and ld(-1) == -1
 
 

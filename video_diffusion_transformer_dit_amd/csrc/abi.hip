@@ -285,7 +285,7 @@ int64_t dit_subblock_scores_ld(int64_t nb)
 {
     if (nb < 0 || nb > kMaxSubBlocks)
         return -1;
-    return (nb + 3) / 4 * 4;
+    return (nb + 31) / 32 * 32;
 }
 
 dit_status dit_subblock_pool(const dit_bf16 *q, const dit_bf16 *k, float *q_pooled, float *k_pooled, int64_t B,

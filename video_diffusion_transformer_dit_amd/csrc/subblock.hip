@@ -178,8 +178,11 @@ __global__ __launch_bounds__(256) void subblock_scores_kernel(const float *__res
 {
     constexpr int kRow = DH + 4; // bf16 per padded LDS row
     constexpr int kF4PerRow = DH / 4;
-    __shared__ __align__(16) uint16_t lds_q[kScoreTile * kRow];
-    __shared__ __align__(16) uint16_t lds_k[kScoreTile * kRow];
+    constexpr int kOutRow = kScoreTile + 4; // floats per padded LDS row of the output tile
+    constexpr int kOperandBytes = 2 * kScoreTile * kRow * 2, kOutBytes = kScoreTile * kOutRow * 4;
+    __shared__ __align__(16) unsigned char lds_raw[kOperandBytes > kOutBytes ? kOperandBytes : kOutBytes];
+    uint16_t *lds_q = reinterpret_cast<uint16_t *>(lds_raw);
+    uint16_t *lds_k = lds_q + kScoreTile * kRow;
 
     const int ti = blockIdx.x / tiles, tj = blockIdx.x % tiles;
     const size_t bh = (size_t)blockIdx.z * H + blockIdx.y;
@@ -217,15 +220,27 @@ __global__ __launch_bounds__(256) void subblock_scores_kernel(const float *__res
         }
     }
 
-    float *out = scores + (bh * nb + (size_t)ti * kScoreTile) * ld + (size_t)tj * kScoreTile;
+    // The tile goes out through LDS as whole-row segments: 16 lanes store 256
+    // contiguous bytes of one row with non-temporal 16-byte stores, so each
+    // 128-byte line of a (128-byte-aligned) row is written whole by one
+    // instruction and nothing is read back or kept in the caches.
+    float *lds_s = reinterpret_cast<float *>(lds_raw);
+    __syncthreads(); // every wave has finished reading the operand tiles
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int row = 16 * wave + 4 * quad + e, col = 16 * t + r16;
-            if (row < q_rows && col < k_rows)
-                out[(size_t)row * ld + col] = acc[t][e];
-        }
+        for (int e = 0; e < 4; ++e)
+            lds_s[(16 * wave + 4 * quad + e) * kOutRow + 16 * t + r16] = acc[t][e];
+    __syncthreads();
+    float *out = scores + (bh * nb + (size_t)ti * kScoreTile) * ld + (size_t)tj * kScoreTile;
+#pragma unroll
+    for (int m = 0; m < kScoreTile * kScoreTile / 4 / 256; ++m) {
+        const int idx = threadIdx.x + 256 * m;
+        const int row = idx / (kScoreTile / 4), c4 = idx % (kScoreTile / 4);
+        if (row < q_rows && 4 * c4 < k_rows) // columns up to nb rounded up to 4, all inside ld
+            __builtin_nontemporal_store(*reinterpret_cast<const f32x4 *>(&lds_s[row * kOutRow + 4 * c4]),
+                                        reinterpret_cast<f32x4 *>(out + (size_t)row * ld + 4 * c4));
+    }
 }
 
 // ---------------------------------------------------------------- selection
@@ -244,98 +259,200 @@ __device__ __forceinline__ int lanes_below(uint64_t mask)
     return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
-// One wave (one workgroup) per query block; grid (nb, H, B).  Lane l holds the
-// keys of key blocks l, l + 64, ..., l + 64 (R - 1) in registers.  A radix
-// select over four 8-bit digits, most significant first, finds the keep-th
-// largest key T and how many keys equal to T are kept (LDS histogram of the
-// keys that still match the chosen prefix, then a suffix scan across lanes).
-// The kept blocks are those above T plus the lowest-indexed keys equal to T;
-// they are written in ascending order with ballots.
-template <int R>
+// Radix-select state: keys matching `prefix` under `mask` are still
+// candidates, `need` of them are kept, and `in_bin` of them share the prefix.
+struct RadixState {
+    uint32_t prefix, mask, need, in_bin;
+};
+
+// Picks the next 8-bit digit from a 256-bin histogram (lane l reads digits
+// 4l .. 4l+3): the largest digit whose keys, with those of all larger digits,
+// reach `need`.
+__device__ __forceinline__ void choose_digit(const uint32_t *hist, int lane, int shift, RadixState &st)
+{
+    const uint4 h4 = reinterpret_cast<const uint4 *>(hist)[lane];
+    const uint32_t c = h4.x + h4.y + h4.z + h4.w;
+    uint32_t suffix = c; // keys of digits >= 4l
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        const uint32_t o = __shfl_down(suffix, off, kWave);
+        suffix += (lane + off < kWave) ? o : 0u;
+    }
+    const uint32_t above = suffix - c;
+    const bool mine = above < st.need && st.need <= suffix; // exactly one lane
+    uint32_t digit = 4u * lane, greater = above, count = h4.x;
+    if (mine) {
+        if (above + h4.w >= st.need) {
+            digit += 3u, count = h4.w;
+        } else if (above + h4.w + h4.z >= st.need) {
+            digit += 2u, greater += h4.w, count = h4.z;
+        } else if (above + h4.w + h4.z + h4.y >= st.need) {
+            digit += 1u, greater += h4.w + h4.z, count = h4.y;
+        } else {
+            greater += h4.w + h4.z + h4.y;
+        }
+    }
+    const int src = __builtin_ctzll(__ballot(mine));
+    st.prefix |= (uint32_t)__builtin_amdgcn_readlane(digit, src) << shift;
+    st.mask |= 0xffu << shift;
+    st.need -= (uint32_t)__builtin_amdgcn_readlane(greater, src);
+    st.in_bin = (uint32_t)__builtin_amdgcn_readlane(count, src);
+}
+
+// Exclusive prefix sum over the wave of per-lane counts in 0 .. 7, and the
+// total, from one ballot per bit.
+__device__ __forceinline__ uint32_t lane_offset(uint32_t c, uint32_t &total)
+{
+    uint32_t excl = 0u;
+    total = 0u;
+#pragma unroll
+    for (int bit = 0; bit < 3; ++bit) {
+        const uint64_t m = __ballot((c >> bit) & 1u);
+        excl += (uint32_t)lanes_below(m) << bit;
+        total += (uint32_t)__builtin_popcountll(m) << bit;
+    }
+    return excl;
+}
+
+constexpr int kMaxSurvivors = 256;
+
+// One wave (one workgroup) per query block; grid (nb, H, B).  Lane l loads
+// key blocks 256 r + 4 l .. 256 r + 4 l + 3 with one 16-byte load per r and
+// keeps their keys in registers.  A radix select over four 8-bit digits, most
+// significant first, finds the keep-th largest key T and how many keys equal
+// to T are kept (LDS histogram of the keys still matching the chosen prefix,
+// then a suffix scan across lanes).  After two digits the few keys that still
+// match are compacted into LDS and the last two digits count only those.  The
+// kept blocks -- every key above T and the lowest-indexed keys equal to T --
+// are written in ascending order, each lane's offset taken from ballots.
+template <int RV>
 __global__ __launch_bounds__(kWave) void subblock_topk_kernel(const float *__restrict__ scores,
                                                               int32_t *__restrict__ kept, int nb, int ld, int keep,
                                                               int H)
 {
     __shared__ __align__(16) uint32_t hist[256];
+    __shared__ uint32_t survivors[kMaxSurvivors];
     const int lane = threadIdx.x;
     const size_t row = ((size_t)blockIdx.z * H + blockIdx.y) * nb + blockIdx.x;
     const float *s = scores + row * ld;
     int32_t *out = kept + row * keep;
 
-    uint32_t key[R];
+    uint32_t key[RV][4];
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-        const int j = lane + kWave * r;
-        key[r] = j < nb ? score_key(__builtin_nontemporal_load(s + j)) : 0u;
+    for (int r = 0; r < RV; ++r) {
+        const int j0 = 256 * r + 4 * lane;
+        f32x4 v = {0.f, 0.f, 0.f, 0.f};
+        if (j0 < nb) // the row is 16-byte aligned and ld >= nb rounded up to 4
+            v = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(s + j0));
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            key[r][e] = score_key(v[e]);
     }
+    auto valid = [&](int r, int e) { return 256 * r + 4 * lane + e < nb; };
 
-    uint32_t prefix = 0u, mask = 0u;
-    uint32_t need = (uint32_t)keep;
+    RadixState st = {0u, 0u, (uint32_t)keep, 0u};
+    auto count_registers = [&](int shift) {
+#pragma unroll
+        for (int r = 0; r < RV; ++r)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (valid(r, e) && (key[r][e] & st.mask) == st.prefix)
+                    atomicAdd(&hist[(key[r][e] >> shift) & 0xffu], 1u);
+    };
 #pragma unroll 1
-    for (int pass = 0; pass < 4; ++pass) {
+    for (int pass = 0; pass < 2; ++pass) {
         const int shift = 24 - 8 * pass;
         reinterpret_cast<uint4 *>(hist)[lane] = make_uint4(0u, 0u, 0u, 0u);
         __syncthreads();
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const int j = lane + kWave * r;
-            if (j < nb && (key[r] & mask) == prefix)
-                atomicAdd(&hist[(key[r] >> shift) & 0xffu], 1u);
-        }
+        count_registers(shift);
         __syncthreads();
-        const uint4 h4 = reinterpret_cast<const uint4 *>(hist)[lane]; // digits 4l .. 4l+3
-        const uint32_t c = h4.x + h4.y + h4.z + h4.w;
-        uint32_t suffix = c; // keys of digits >= 4l
-#pragma unroll
-        for (int off = 1; off < kWave; off <<= 1) {
-            const uint32_t o = __shfl_down(suffix, off, kWave);
-            suffix += (lane + off < kWave) ? o : 0u;
-        }
-        const uint32_t above = suffix - c;
-        const bool mine = above < need && need <= suffix; // exactly one lane
-        uint32_t digit = 4u * lane, greater = above;
-        if (mine) {
-            if (above + h4.w >= need) {
-                digit += 3u;
-            } else if (above + h4.w + h4.z >= need) {
-                digit += 2u, greater += h4.w;
-            } else if (above + h4.w + h4.z + h4.y >= need) {
-                digit += 1u, greater += h4.w + h4.z;
-            } else {
-                greater += h4.w + h4.z + h4.y;
-            }
-        }
-        const int src = __builtin_ctzll(__ballot(mine));
-        digit = __builtin_amdgcn_readlane(digit, src);
-        greater = __builtin_amdgcn_readlane(greater, src);
-        prefix |= digit << shift;
-        mask |= 0xffu << shift;
-        need -= greater;
+        choose_digit(hist, lane, shift, st);
         __syncthreads(); // every lane has read the histogram before it is cleared
     }
+    const bool compact = st.in_bin <= (uint32_t)kMaxSurvivors; // wave-uniform
+    uint32_t n_surv = 0u;
+    if (compact) {
+#pragma unroll
+        for (int r = 0; r < RV; ++r)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const bool m = valid(r, e) && (key[r][e] & st.mask) == st.prefix;
+                const uint64_t mm = __ballot(m);
+                const uint32_t at = n_surv + (uint32_t)lanes_below(mm);
+                if (m && at < (uint32_t)kMaxSurvivors) // exactly in_bin keys match; the bound guards the store
+                    survivors[at] = key[r][e];
+                n_surv += (uint32_t)__builtin_popcountll(mm);
+            }
+    }
+#pragma unroll 1
+    for (int pass = 2; pass < 4; ++pass) {
+        const int shift = 24 - 8 * pass;
+        reinterpret_cast<uint4 *>(hist)[lane] = make_uint4(0u, 0u, 0u, 0u);
+        __syncthreads();
+        if (compact) {
+            for (uint32_t c = lane; c < n_surv; c += kWave) {
+                const uint32_t k = survivors[c];
+                if ((k & st.mask) == st.prefix)
+                    atomicAdd(&hist[(k >> shift) & 0xffu], 1u);
+            }
+        } else {
+            count_registers(shift);
+        }
+        __syncthreads();
+        choose_digit(hist, lane, shift, st);
+        __syncthreads();
+    }
 
-    // prefix is now the keep-th largest key; `need` keys equal to it are kept.
+    // st.prefix is now the keep-th largest key T; st.in_bin keys equal T and
+    // st.need of them are kept.  Exactly keep blocks are selected; the bound
+    // on `at` only guards the stores.
+    const uint32_t T = st.prefix;
+    const bool all_ties = st.need == st.in_bin; // wave-uniform
     uint32_t written = 0u, ties = 0u;
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-        const int j = lane + kWave * r;
-        const bool valid = j < nb;
-        const bool eq = valid && key[r] == prefix;
-        const uint64_t eq_mask = __ballot(eq);
-        const bool sel = (valid && key[r] > prefix) || (eq && ties + (uint32_t)lanes_below(eq_mask) < need);
-        const uint64_t sel_mask = __ballot(sel);
-        const uint32_t at = written + (uint32_t)lanes_below(sel_mask);
-        if (sel && at < (uint32_t)keep) // exactly keep are selected; the bound only guards the store
-            out[at] = j;
-        written += (uint32_t)__builtin_popcountll(sel_mask);
-        ties += (uint32_t)__builtin_popcountll(eq_mask);
+    for (int r = 0; r < RV; ++r) {
+        bool sel[4];
+        uint32_t c = 0u;
+        if (all_ties) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                sel[e] = valid(r, e) && key[r][e] >= T;
+                c += sel[e] ? 1u : 0u;
+            }
+        } else {
+            bool eq[4];
+            uint32_t c_eq = 0u, eq_total;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                eq[e] = valid(r, e) && key[r][e] == T;
+                c_eq += eq[e] ? 1u : 0u;
+            }
+            uint32_t rank = ties + lane_offset(c_eq, eq_total); // tie rank of this lane's first tie
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                sel[e] = (valid(r, e) && key[r][e] > T) || (eq[e] && rank < st.need);
+                rank += eq[e] ? 1u : 0u;
+                c += sel[e] ? 1u : 0u;
+            }
+            ties += eq_total;
+        }
+        uint32_t total;
+        uint32_t at = written + lane_offset(c, total);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (sel[e]) {
+                if (at < (uint32_t)keep)
+                    out[at] = 256 * r + 4 * lane + e;
+                ++at;
+            }
+        written += total;
     }
 }
 
-template <int R>
-void launch_topk_r(const float *scores, int32_t *kept, int nb, int ld, int keep, int H, int B, hipStream_t stream)
+template <int RV>
+void launch_topk_rv(const float *scores, int32_t *kept, int nb, int ld, int keep, int H, int B, hipStream_t stream)
 {
-    hipLaunchKernelGGL(subblock_topk_kernel<R>, dim3((unsigned)nb, (unsigned)H, (unsigned)B), dim3(kWave), 0, stream,
+    hipLaunchKernelGGL(subblock_topk_kernel<RV>, dim3((unsigned)nb, (unsigned)H, (unsigned)B), dim3(kWave), 0, stream,
                        scores, kept, nb, ld, keep, H);
 }
 
@@ -401,13 +518,11 @@ hipError_t launch_subblock_route(const float *q_pooled, const float *k_pooled, f
     if (keep == 0)
         return hipGetLastError();
     const int kp = (int)keep;
-    if (n <= 64) launch_topk_r<1>(scores, kept, n, l, kp, h, b, stream);
-    else if (n <= 128) launch_topk_r<2>(scores, kept, n, l, kp, h, b, stream);
-    else if (n <= 256) launch_topk_r<4>(scores, kept, n, l, kp, h, b, stream);
-    else if (n <= 512) launch_topk_r<8>(scores, kept, n, l, kp, h, b, stream);
-    else if (n <= 1024) launch_topk_r<16>(scores, kept, n, l, kp, h, b, stream);
-    else if (n <= 2048) launch_topk_r<32>(scores, kept, n, l, kp, h, b, stream);
-    else launch_topk_r<64>(scores, kept, n, l, kp, h, b, stream);
+    if (n <= 256) launch_topk_rv<1>(scores, kept, n, l, kp, h, b, stream);
+    else if (n <= 512) launch_topk_rv<2>(scores, kept, n, l, kp, h, b, stream);
+    else if (n <= 1024) launch_topk_rv<4>(scores, kept, n, l, kp, h, b, stream);
+    else if (n <= 2048) launch_topk_rv<8>(scores, kept, n, l, kp, h, b, stream);
+    else launch_topk_rv<16>(scores, kept, n, l, kp, h, b, stream);
     return hipGetLastError();
 }
 
