@@ -55,21 +55,53 @@ KERNEL_SOURCES = {
     "residual": "residual.hip",
     "swiglu": "swiglu.hip",
     "qk": "qk_rope.hip",
+    "residual_adaln": "residual_adaln.hip",
+    "qk_layout": "qk_rope.hip",
+    "change": "residual_change.hip",
+    "change_final": "residual_change.hip",
+    "pool": "subblock.hip",
+    "pool_hm": "subblock.hip",
+    "scores": "subblock.hip",
+    "topk": "subblock.hip",
     "copy": "copy.hip",
 }
+# Kernels of the next rows, measured after the chain (see main()).
+NEXT_OPS = ("residual_adaln", "qk_layout", "change", "change_final", "pool", "pool_hm", "scores", "topk")
+ROUTE_SPARSITY = 0.75
 COUNTER_SUMMARY = os.path.join(ROOT, "profiles", "{op}_{workload}_counters.md")
 
 
-def op_bytes(wl) -> dict:
-    """Compulsory HBM bytes of one launch of each op on workload ``wl``."""
+def op_bytes(wl, next_rows: bool = False) -> dict:
+    """Compulsory HBM bytes of one launch of each op on workload ``wl`` (the chain's five, and with
+    ``next_rows`` the kernels of the next rows as the benchmark runs them)."""
     B, N, R, D, F, H, Dh = wl.B, wl.N, wl.R, wl.D, wl.F, wl.H, wl.Dh
-    return {
+    out = {
         "positions": 12 * N,                                   # write (t, h, w) int32
         "adaln": 2 * R * D * 2 + 2 * B * D * 2,                # x in, y out, shift + scale
         "residual": 3 * R * D * 2 + B * D * 2,                 # x, y in, out, gate
         "swiglu": R * 2 * F * 2 + R * F * 2,                   # [a|b] in, out
         "qk": 4 * R * H * Dh * 2 + 12 * N + 2 * Dh * 2,        # q, k in, q', k' out, pos, wq, wk
     }
+    if next_rows:
+        nb = -(-N // 64)
+        keep = dit_keep(nb)
+        pooled = 2 * B * H * nb * Dh * 4
+        out.update({
+            "residual_adaln": 4 * R * D * 2 + 3 * B * D * 2,   # x, y in, x_out, z out, gate + shift + scale
+            "qk_layout": out["qk"],                            # same bytes, strided in, head-major out
+            "change": 2 * R * D * 2,                           # r, r_cached in (partials: 16 B per 2048 vectors)
+            "pool": 2 * R * H * Dh * 2 + pooled,               # q', k' in, fp32 block means out
+            "pool_hm": 2 * R * H * Dh * 2 + pooled,
+            "scores": pooled + B * H * nb * nb * 4,            # means in, fp32 scores out
+            "topk": B * H * nb * nb * 4 + B * H * nb * keep * 4,  # scores in, kept indices out
+        })
+    return out
+
+
+def dit_keep(nb: int) -> int:
+    from video_diffusion_transformer_dit_amd import dit_subblock_keep
+
+    return dit_subblock_keep(nb, ROUTE_SPARSITY)
 
 
 def source_digest(op: str) -> str:
@@ -225,7 +257,8 @@ def main(argv=None) -> int:
              "GB_s": round(fused_bytes / (fused_ms * 1e-3) / 1e9, 1),
              "pct_of_peak": round(100.0 * fused_bytes / (fused_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
              "unfused_ms": round(unfused_ms, 5), "unfused_bytes": nbytes["residual"] + nbytes["adaln"],
-             "time_saved_pct": round(100.0 * (1.0 - fused_ms / unfused_ms), 1)}
+             "time_saved_pct": round(100.0 * (1.0 - fused_ms / unfused_ms), 1),
+             "traffic": committed_traffic("residual_adaln", wl.name)}
 
     # QK with the layouts around attention: q and k read straight out of a fused
     # [B, N, 3*H*Dh] projection buffer, q' and k' written head-major [B, H, N, Dh].
@@ -252,7 +285,8 @@ def main(argv=None) -> int:
               "pct_of_peak": round(100.0 * nbytes["qk"] / (layout_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
               "token_major_ms": ops["qk"]["avg_ms"],
               "passes_avoided": "splitting q, k out of the QKV buffer and transposing q', k' to head-major: "
-                                "each a further read and write of q and k (2 x 4.1 GB here)"}
+                                "each a further read and write of q and k (2 x 4.1 GB here)",
+              "traffic": committed_traffic("qk_layout", wl.name)}
 
     # Cache-DiT residual-change statistic over the packed sequence (the two
     # residual inputs stand in for the current and cached boundary residuals).
@@ -271,7 +305,8 @@ def main(argv=None) -> int:
     change_ms = sum(a.elapsed_time(b) for a, b in cev) / args.steps
     change = {"op": "dit_residual_change (two launches: partials, fixed-order reduce)", "avg_ms": round(change_ms, 5),
               "bytes": change_bytes, "GB_s": round(change_bytes / (change_ms * 1e-3) / 1e9, 1),
-              "pct_of_peak": round(100.0 * change_bytes / (change_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2)}
+              "pct_of_peak": round(100.0 * change_bytes / (change_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
+              "traffic_partial_kernel": committed_traffic("change", wl.name)}
 
     # SubBlock routing front-end on the chain's q', k' at sparsity 0.75: block
     # means (both input layouts), block scores alone (keep = 0 runs only the
@@ -287,11 +322,12 @@ def main(argv=None) -> int:
         torch.cuda.synchronize()
         return sum(a.elapsed_time(b) for a, b in ev) / args.steps
 
-    def rate(nbytes_, ms):
+    def rate(nbytes_, ms, op):
         return {"avg_ms": round(ms, 5), "bytes": nbytes_, "GB_s": round(nbytes_ / (ms * 1e-3) / 1e9, 1),
-                "pct_of_peak": round(100.0 * nbytes_ / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2)}
+                "pct_of_peak": round(100.0 * nbytes_ / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
+                "traffic": committed_traffic(op, wl.name)}
 
-    sparsity = 0.75
+    sparsity = ROUTE_SPARSITY
     nb = -(-wl.N // 64)
     keep = dit.dit_subblock_keep(nb, sparsity)
     ld = dit.dit_subblock_scores_ld(nb)
@@ -318,11 +354,12 @@ def main(argv=None) -> int:
     topk_ms = route_ms - scores_ms
     subblock = {
         "sparsity": sparsity, "blocks": nb, "keep": keep,
-        "pool": rate(pool_bytes, pool_ms),
-        "pool_head_major": rate(pool_bytes, pool_hm_ms),
-        "scores": {**rate(scores_bytes, scores_ms), "TFLOP_s": round(score_flops / (scores_ms * 1e-3) / 1e12, 1),
+        "pool": rate(pool_bytes, pool_ms, "pool"),
+        "pool_head_major": rate(pool_bytes, pool_hm_ms, "pool_hm"),
+        "scores": {**rate(scores_bytes, scores_ms, "scores"),
+                   "TFLOP_s": round(score_flops / (scores_ms * 1e-3) / 1e12, 1),
                    "pct_of_bf16_mfma_peak": round(100.0 * score_flops / (scores_ms * 1e-3) / 2.5e15, 2)},
-        "topk": rate(topk_bytes, topk_ms),
+        "topk": rate(topk_bytes, topk_ms, "topk"),
         "total_ms": round(pool_ms + route_ms, 5),
     }
     del qp_s, kp_s, sc, kept, kept0
@@ -522,14 +559,23 @@ def cpu_baseline(wl, ins, outs, target_s: float) -> dict:
 
 # --------------------------------------------------------------------------- rocprofv3 summaries
 
-KERNEL_OPS = {
-    "packed_positions_kernel": "positions",
-    "adaln_modulate_kernel": "adaln",
-    "gated_residual_kernel": "residual",
-    "swiglu_kernel": "swiglu",
-    "qk_rmsnorm_rope3d_kernel": "qk",
-    "copy16_kernel": "copy",
-}
+# Kernel name pattern -> op, most specific first (names carry template arguments).
+KERNEL_OPS = (
+    (r"gated_residual_adaln_kernel", "residual_adaln"),
+    (r"adaln_modulate_kernel", "adaln"),
+    (r"gated_residual_kernel", "residual"),
+    (r"swiglu_kernel", "swiglu"),
+    (r"qk_rmsnorm_rope3d_kernel<\d+, true>", "qk_layout"),
+    (r"qk_rmsnorm_rope3d_kernel", "qk"),
+    (r"residual_change_partial_kernel", "change"),
+    (r"residual_change_final_kernel", "change_final"),
+    (r"subblock_pool_token_major_kernel", "pool"),
+    (r"subblock_pool_head_major_kernel", "pool_hm"),
+    (r"subblock_scores_kernel", "scores"),
+    (r"subblock_topk_kernel", "topk"),
+    (r"packed_positions_kernel", "positions"),
+    (r"copy16_kernel", "copy"),
+)
 
 PROFILE_COMMANDS = """\
 cd /tmp && export TMPDIR=/tmp
@@ -543,8 +589,8 @@ cd $REPO && python bench.py --workload {wl} --summarize-rocprof gpurun_out/prof_
 
 
 def _kernel_op(name: str):
-    for key, op in KERNEL_OPS.items():
-        if key in name:
+    for pattern, op in KERNEL_OPS:
+        if re.search(pattern, name):
             return op
     return None
 
@@ -574,7 +620,7 @@ def summarize_rocprof(trace_dir: str, fetch_dir: str, write_dir: str, workload: 
     import synthetic_inputs as si
 
     wl = si.WORKLOADS[workload]
-    nbytes = op_bytes(wl)
+    nbytes = op_bytes(wl, next_rows=True)
     out_dir = os.path.join(ROOT, "profiles")
     os.makedirs(out_dir, exist_ok=True)
     commands = PROFILE_COMMANDS.format(wl=workload)
@@ -604,13 +650,13 @@ def summarize_rocprof(trace_dir: str, fetch_dir: str, write_dir: str, workload: 
     factor = {k: (v[0] / v[1] if v[1] else None) for k, v in calib.items()}
 
     lines = [f"# Kernel durations: {wl.description}", "",
-             "rocprofv3 kernel trace of the benchmark step (10 timed + 2 warm-up steps, plus the copy-ceiling "
-             "copies). Bytes are the compulsory (algorithmic) HBM bytes of one launch; GB/s uses the average "
-             "duration.", "", "Commands (from the repository root on the GPU host, REPO=$PWD):", "", "```",
+             "rocprofv3 kernel trace of the benchmark (10 timed + 2 warm-up steps of the chain, then the same "
+             "counts of each next-row kernel and the copy-ceiling copies). Bytes are the compulsory "
+             "(algorithmic) HBM bytes of one launch; GB/s uses the average duration.", "", "Commands (from the repository root on the GPU host, REPO=$PWD):", "", "```",
              commands, "```", "",
              "| kernel | calls | avg us | min us | max us | algorithmic bytes | GB/s at avg | % of 8 TB/s |",
              "|---|---|---|---|---|---|---|---|"]
-    for op in ("positions", "adaln", "residual", "swiglu", "qk", "copy"):
+    for op in (*OPS, *NEXT_OPS, "copy"):
         if op not in stats:
             continue
         st = stats[op]
@@ -622,8 +668,8 @@ def summarize_rocprof(trace_dir: str, fetch_dir: str, write_dir: str, workload: 
     with open(os.path.join(out_dir, f"kernels_{workload}_trace.md"), "w", encoding="utf-8") as fh:
         fh.write("\n".join(lines) + "\n")
 
-    for op in ("adaln", "residual", "swiglu", "qk"):
-        if op not in counters["FETCH_SIZE"] or op not in counters["WRITE_SIZE"]:
+    for op in (*OPS[1:], *NEXT_OPS):
+        if op not in counters["FETCH_SIZE"] or op not in counters["WRITE_SIZE"] or op not in nbytes:
             continue
         f_kib = sum(counters["FETCH_SIZE"][op]) / len(counters["FETCH_SIZE"][op])
         w_kib = sum(counters["WRITE_SIZE"][op]) / len(counters["WRITE_SIZE"][op])
