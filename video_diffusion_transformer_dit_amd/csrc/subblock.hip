@@ -338,13 +338,16 @@ constexpr int kMaxSurvivors = 256;
 // match are compacted into LDS and the last two digits count only those.  The
 // kept blocks -- every key above T and the lowest-indexed keys equal to T --
 // are written in ascending order, each lane's offset taken from ballots.
+// Counting never branches: a key that does not count adds to its lane's own
+// trash slot after the 256 bins (and a survivor past the bound to a trash
+// slot after the list), so the waves issue no exec-mask bookkeeping per key.
 template <int RV>
 __global__ __launch_bounds__(kWave) void subblock_topk_kernel(const float *__restrict__ scores,
                                                               int32_t *__restrict__ kept, int nb, int ld, int keep,
                                                               int H)
 {
-    __shared__ __align__(16) uint32_t hist[256];
-    __shared__ uint32_t survivors[kMaxSurvivors];
+    __shared__ __align__(16) uint32_t hist[256 + kWave]; // 256 digits, then one trash slot per lane
+    __shared__ uint32_t survivors[kMaxSurvivors + kWave]; // then one trash slot per lane
     const int lane = threadIdx.x;
     const size_t row = ((size_t)blockIdx.z * H + blockIdx.y) * nb + blockIdx.x;
     const float *s = scores + row * ld;
@@ -361,27 +364,38 @@ __global__ __launch_bounds__(kWave) void subblock_topk_kernel(const float *__res
         for (int e = 0; e < 4; ++e)
             key[r][e] = score_key(v[e]);
     }
-    auto valid = [&](int r, int e) { return 256 * r + 4 * lane + e < nb; };
+    const int limit = nb - 4 * lane; // key (r, e) is a real block when 256 r + e < limit
+    auto valid = [&](int r, int e) { return 256 * r + e < limit; };
 
     RadixState st = {0u, 0u, (uint32_t)keep, 0u};
+    // Every key adds to a bin without branching: keys that do not count go to
+    // the lane's own trash slot.
     auto count_registers = [&](int shift) {
 #pragma unroll
         for (int r = 0; r < RV; ++r)
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                if (valid(r, e) && (key[r][e] & st.mask) == st.prefix)
-                    atomicAdd(&hist[(key[r][e] >> shift) & 0xffu], 1u);
+            for (int e = 0; e < 4; ++e) {
+                const bool counts = valid(r, e) && (key[r][e] & st.mask) == st.prefix;
+                atomicAdd(&hist[counts ? (key[r][e] >> shift) & 0xffu : 256u + lane], 1u);
+            }
     };
-#pragma unroll 1
-    for (int pass = 0; pass < 2; ++pass) {
-        const int shift = 24 - 8 * pass;
-        reinterpret_cast<uint4 *>(hist)[lane] = make_uint4(0u, 0u, 0u, 0u);
-        __syncthreads();
-        count_registers(shift);
-        __syncthreads();
-        choose_digit(hist, lane, shift, st);
-        __syncthreads(); // every lane has read the histogram before it is cleared
-    }
+    // first digit: every valid key counts
+    reinterpret_cast<uint4 *>(hist)[lane] = make_uint4(0u, 0u, 0u, 0u);
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < RV; ++r)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            atomicAdd(&hist[valid(r, e) ? key[r][e] >> 24 : 256u + lane], 1u);
+    __syncthreads();
+    choose_digit(hist, lane, 24, st);
+    __syncthreads();
+    reinterpret_cast<uint4 *>(hist)[lane] = make_uint4(0u, 0u, 0u, 0u);
+    __syncthreads();
+    count_registers(16);
+    __syncthreads();
+    choose_digit(hist, lane, 16, st);
+    __syncthreads();
     const bool compact = st.in_bin <= (uint32_t)kMaxSurvivors; // wave-uniform
     uint32_t n_surv = 0u;
     if (compact) {
@@ -392,8 +406,8 @@ __global__ __launch_bounds__(kWave) void subblock_topk_kernel(const float *__res
                 const bool m = valid(r, e) && (key[r][e] & st.mask) == st.prefix;
                 const uint64_t mm = __ballot(m);
                 const uint32_t at = n_surv + (uint32_t)lanes_below(mm);
-                if (m && at < (uint32_t)kMaxSurvivors) // exactly in_bin keys match; the bound guards the store
-                    survivors[at] = key[r][e];
+                // exactly in_bin keys match; the bound only guards the store
+                survivors[(m && at < (uint32_t)kMaxSurvivors) ? at : kMaxSurvivors + lane] = key[r][e];
                 n_surv += (uint32_t)__builtin_popcountll(mm);
             }
     }
