@@ -235,7 +235,7 @@ def test_end_to_end_small(head_major):
     assert agree > 0.95
 
 
-@pytest.mark.parametrize("name", ["lowres", "full5s", "full10s"])
+@pytest.mark.parametrize("name", ["lowres", "full5s", "full10s", "batch2"])
 def test_end_to_end_workload(name):
     wl = WORKLOADS[name]
     nb = -(-wl.N // 64)
