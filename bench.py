@@ -579,13 +579,13 @@ KERNEL_OPS = (
 
 PROFILE_COMMANDS = """\
 cd /tmp && export TMPDIR=/tmp
-rocprofv3 --kernel-trace --stats --output-format csv -d $REPO/gpurun_out/prof_trace -o trace -- \\
+rocprofv3 --kernel-trace --stats --output-format csv -d $OUT/prof_trace -o trace -- \\
     python $REPO/bench.py --workload {wl} --steps 10 --warmup 2 --no-cpu-baseline
-rocprofv3 --pmc FETCH_SIZE --output-format csv -d $REPO/gpurun_out/prof_fetch -o fetch -- \\
+rocprofv3 --pmc FETCH_SIZE --output-format csv -d $OUT/prof_fetch -o fetch -- \\
     python $REPO/bench.py --workload {wl} --steps 2 --warmup 1 --no-cpu-baseline --copy-calibration
-rocprofv3 --pmc WRITE_SIZE --output-format csv -d $REPO/gpurun_out/prof_write -o write -- \\
+rocprofv3 --pmc WRITE_SIZE --output-format csv -d $OUT/prof_write -o write -- \\
     python $REPO/bench.py --workload {wl} --steps 2 --warmup 1 --no-cpu-baseline --copy-calibration
-cd $REPO && python bench.py --workload {wl} --summarize-rocprof gpurun_out/prof_trace gpurun_out/prof_fetch gpurun_out/prof_write"""
+cd $REPO && python bench.py --workload {wl} --summarize-rocprof $OUT/prof_trace $OUT/prof_fetch $OUT/prof_write"""
 
 
 def _kernel_op(name: str):
@@ -652,7 +652,7 @@ def summarize_rocprof(trace_dir: str, fetch_dir: str, write_dir: str, workload: 
     lines = [f"# Kernel durations: {wl.description}", "",
              "rocprofv3 kernel trace of the benchmark (10 timed + 2 warm-up steps of the chain, then the same "
              "counts of each next-row kernel and the copy-ceiling copies). Bytes are the compulsory "
-             "(algorithmic) HBM bytes of one launch; GB/s uses the average duration.", "", "Commands (from the repository root on the GPU host, REPO=$PWD):", "", "```",
+             "(algorithmic) HBM bytes of one launch; GB/s uses the average duration.", "", "Commands (REPO = the repository root, OUT = an output directory for the raw rocprofv3 files):", "", "```",
              commands, "```", "",
              "| kernel | calls | avg us | min us | max us | algorithmic bytes | GB/s at avg | % of 8 TB/s |",
              "|---|---|---|---|---|---|---|---|"]
@@ -679,7 +679,7 @@ def summarize_rocprof(trace_dir: str, fetch_dir: str, write_dir: str, workload: 
             "rocprofv3 counters, one counter per run (FETCH_SIZE, then WRITE_SIZE), KiB per dispatch averaged "
             "over the timed and warm-up launches of the run; each scaled by the same counter's reading for "
             "dit_copy16 calls of known size in the same run.", "",
-            "Commands (from the repository root on the GPU host, REPO=$PWD):", "", "```", commands, "```", "",
+            "Commands (REPO = the repository root, OUT = an output directory for the raw rocprofv3 files):", "", "```", commands, "```", "",
             f"- dispatches: {len(counters['FETCH_SIZE'][op])} (FETCH_SIZE run), "
             f"{len(counters['WRITE_SIZE'][op])} (WRITE_SIZE run)",
             f"- FETCH_SIZE per launch: {f_kib:.1f} KiB (raw)",
