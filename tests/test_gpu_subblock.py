@@ -52,6 +52,7 @@ POOL_SHAPES = [
     (1, 1, 4, 128),     # one token
     (1, 100, 5, 128),   # 80 vectors per token: a partial second column chunk
     (2, 1000, 4, 32),
+    (1, 4096 * 64, 1, 16),  # the largest sequence: 4096 blocks
 ]
 
 
@@ -97,6 +98,7 @@ ROUTE_SHAPES = [
     (1, 1, 130, 256),
     (1, 2, 700, 128),
     (1, 1, 2100, 64),   # more than 2048 blocks
+    (1, 1, 4096, 16),   # the largest block count
 ]
 
 
