@@ -236,6 +236,63 @@ def main(argv=None) -> int:
                 "frac": round(achieved / HBM_PEAK_GBPS, 4),
                 "traffic": traffic, "algorithmic_bytes": nbytes[dominant]}
 
+    # Per-op medians under a flush protocol: every timed call is preceded,
+    # outside its events, by a 1 GiB scratch write that evicts the 4 MB L2 of
+    # each XCD and the 256 MB last-level cache, so no op starts with warm data.
+    flush_buf = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    flushed = {}
+    reps = max(20, args.steps)
+    for op in OPS:
+        pairs = []
+        for i in range(args.warmup + reps):
+            flush_buf.zero_()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            launch(op)
+            e1.record(stream)
+            if i >= args.warmup:
+                pairs.append((e0, e1))
+        torch.cuda.synchronize()
+        t = sorted(a.elapsed_time(b) for a, b in pairs)
+        med = t[len(t) // 2]
+        flushed[op] = {"median_ms": round(med, 5), "min_ms": round(t[0], 5),
+                       "GB_s_median": round(nbytes[op] / (med * 1e-3) / 1e9, 1),
+                       "pct_of_peak_median": round(100.0 * nbytes[op] / (med * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2)}
+    del flush_buf
+
+    # One GPU's share of an 8-way sequence split (row-local ops: each GPU runs
+    # this same chain on N/8 tokens, with the matching slice of the positions).
+    share = None
+    if wl.B == 1:
+        ns = wl.N // 8
+        sl = {"x_mod": ins["x_mod"][:, :ns], "res_x": ins["res_x"][:, :ns], "res_y": ins["res_y"][:, :ns],
+              "swiglu_in": ins["swiglu_in"][:ns], "q": ins["q"][:, :ns], "k": ins["k"][:, :ns]}
+        outs_s = {"y": y[:, :ns], "out": out[:, :ns], "sw": sw[:ns], "qo": qo[:, :ns], "ko": ko[:, :ns]}
+        pos_s = pos[:ns]
+
+        def share_step():
+            dit.dit_adaln_modulate(sl["x_mod"], ins["shift"], ins["scale"], y=outs_s["y"], eps=wl.eps, stream=stream)
+            dit.dit_gated_residual(sl["res_x"], sl["res_y"], ins["gate"], out=outs_s["out"], stream=stream)
+            dit.dit_swiglu(sl["swiglu_in"], out=outs_s["sw"], stream=stream)
+            dit.dit_qk_rmsnorm_rope3d(sl["q"], sl["k"], ins["wq"], ins["wk"], pos_s, wl.bands, q_out=outs_s["qo"],
+                                      k_out=outs_s["ko"], theta=wl.theta, eps=wl.eps, stream=stream)
+
+        for _ in range(args.warmup):
+            share_step()
+        torch.cuda.synchronize()
+        t_s0 = time.perf_counter()
+        for _ in range(args.steps):
+            share_step()
+        torch.cuda.synchronize()
+        share_ms = (time.perf_counter() - t_s0) * 1e3 / args.steps
+        share_bytes = (chain_bytes - nbytes["positions"]) * ns // wl.N
+        share = {"rows": ns, "of": "1/8 of the tokens (sequence split), positions sliced, not rebuilt",
+                 "ms_per_step": round(share_ms, 4), "bytes": share_bytes,
+                 "GB_s": round(share_bytes / (share_ms * 1e-3) / 1e9, 1),
+                 "pct_of_peak": round(100.0 * share_bytes / (share_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
+                 "tokens_per_s": round(ns / (share_ms * 1e-3))}
+        # (the slices receive the same values the full chain wrote there: same inputs, per-row kernels)
+
     # The next fusion, measured on its own after the chain: gated residual ->
     # AdaLN in one kernel (x and y read once, x_out and z written once).
     fused_bytes = 4 * wl.R * wl.D * 2 + 3 * wl.B * wl.D * 2
@@ -378,8 +435,19 @@ def main(argv=None) -> int:
     e1.record(stream)
     torch.cuda.synchronize()
     copy_ms = e0.elapsed_time(e1) / reps
+    # the runtime's device-to-device copy of the same buffers (torch issues hipMemcpyAsync for it)
+    for _ in range(3):
+        dst.copy_(src)
+    e0.record(stream)
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    memcpy_ms = e0.elapsed_time(e1) / reps
     copy_ceiling = {"bytes": 2 * cbytes, "avg_ms": round(copy_ms, 4),
-                    "GB_s": round(2 * cbytes / (copy_ms * 1e-3) / 1e9, 1)}
+                    "GB_s": round(2 * cbytes / (copy_ms * 1e-3) / 1e9, 1),
+                    "memcpy_dtod_ms": round(memcpy_ms, 4),
+                    "memcpy_dtod_GB_s": round(2 * cbytes / (memcpy_ms * 1e-3) / 1e9, 1)}
     del src, dst
 
     mix_ms = 2 * ops["adaln"]["avg_ms"] + ops["qk"]["avg_ms"] + 2 * ops["residual"]["avg_ms"] + ops["swiglu"]["avg_ms"]
@@ -429,6 +497,7 @@ def main(argv=None) -> int:
         "chain_bytes": chain_bytes,
         "kernel_ms_sum": round(kernel_ms, 4),
         "ops": ops,
+        "ops_flushed": flushed,
         "roofline": roofline,
         "copy_ceiling": copy_ceiling,
         "block_mix": block_mix,
@@ -438,6 +507,7 @@ def main(argv=None) -> int:
         "next_subblock_routing": subblock,
         "block_mix_fused": block_mix_fused,
         "next_consistency": consistency,
+        "one_gpu_share_of_8": share,
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, ins, {"y": y, "out": out, "sw": sw, "qo": qo, "ko": ko,
@@ -482,8 +552,10 @@ def cpu_baseline(wl, ins, outs, target_s: float) -> dict:
     shift, scale, gate = bits(ins["shift"]), bits(ins["scale"]), bits(ins["gate"])
     wq, wk = bits(ins["wq"]), bits(ins["wk"])
 
-    def run_oracle(rows, host):
-        """All four ops on the given rows (each row is one token of one sample)."""
+    op_seconds = {"adaln": 0.0, "residual": 0.0, "swiglu": 0.0, "qk": 0.0}
+
+    def run_oracle(rows, host, nthreads=threads, timing=op_seconds):
+        """All four ops on the given rows (each row is one token of one sample); per-op oracle time into timing."""
         res = {"y": [], "out": [], "sw": [], "qo": [], "ko": []}
         samples = np.asarray(rows) // N
         tokens = np.asarray(rows) % N
@@ -492,17 +564,26 @@ def cpu_baseline(wl, ins, outs, target_s: float) -> dict:
             if sel.size == 0:
                 continue
             n = sel.size
+            t0 = time.perf_counter()
             res["y"].append((sel, oracle.adaln_modulate(host["x"][sel].reshape(1, n, -1), shift[b:b + 1],
-                                                        scale[b:b + 1], eps=wl.eps, threads=threads).reshape(n, -1)))
+                                                        scale[b:b + 1], eps=wl.eps, threads=nthreads).reshape(n, -1)))
+            t1 = time.perf_counter()
             res["out"].append((sel, oracle.gated_residual(host["rx"][sel].reshape(1, n, -1),
                                                           host["ry"][sel].reshape(1, n, -1), gate[b:b + 1],
-                                                          threads=threads).reshape(n, -1)))
+                                                          threads=nthreads).reshape(n, -1)))
+            t2 = time.perf_counter()
             qr, kr = oracle.qk_rmsnorm_rope3d(host["q"][sel].reshape(1, n, wl.H, wl.Dh),
                                               host["k"][sel].reshape(1, n, wl.H, wl.Dh), wq, wk,
-                                              pos_ref[tokens[sel]], wl.bands, wl.theta, wl.eps, threads=threads)
+                                              pos_ref[tokens[sel]], wl.bands, wl.theta, wl.eps, threads=nthreads)
+            t3 = time.perf_counter()
+            timing["adaln"] += t1 - t0
+            timing["residual"] += t2 - t1
+            timing["qk"] += t3 - t2
             res["qo"].append((sel, qr.reshape(n, -1)))
             res["ko"].append((sel, kr.reshape(n, -1)))
-        res["sw"].append((np.arange(len(rows)), oracle.swiglu(host["sw"], threads=threads)))
+        t0 = time.perf_counter()
+        res["sw"].append((np.arange(len(rows)), oracle.swiglu(host["sw"], threads=nthreads)))
+        timing["swiglu"] += time.perf_counter() - t0
         return res
 
     def fused_check(rows, host, gpu):
@@ -543,6 +624,19 @@ def cpu_baseline(wl, ins, outs, target_s: float) -> dict:
         if elapsed >= target_s:
             break
     tokens_per_s = done / elapsed
+    # the same oracle on one thread, over one chunk of the same tokens
+    rows = np.sort(order[:chunk]).tolist()
+    host, _ = chunk_rows(rows)
+    single = {k: 0.0 for k in op_seconds}
+    t = time.perf_counter()
+    run_oracle(rows, host, nthreads=1, timing=single)
+    single_tokens_per_s = len(rows) / (time.perf_counter() - t)
+    cpu_model = ""
+    try:
+        with open("/proc/cpuinfo", encoding="utf-8") as fh:
+            cpu_model = next((ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")), "")
+    except OSError:
+        pass
     return {
         "value": round(tokens_per_s * per_token / 1e9, 4),
         "unit": "GB/s",
@@ -552,6 +646,11 @@ def cpu_baseline(wl, ins, outs, target_s: float) -> dict:
         "sample": f"{done} of {R} tokens (seeded uniform random rows) of the {wl.name} workload; all four ops "
                   f"in the fp64 C oracle on {threads} host threads; {elapsed:.1f} s of oracle time (the same "
                   f"tokens' GPU outputs, and the fused residual->AdaLN z, are checked against it)",
+        "tokens_per_s_per_op": {k: round(done / v, 1) for k, v in op_seconds.items() if v > 0},
+        "single_thread_tokens_per_s": round(single_tokens_per_s, 1),
+        "single_thread_tokens_per_s_per_op": {k: round(len(rows) / v, 1) for k, v in single.items() if v > 0},
+        "host_cpu": cpu_model,
+        "host_logical_cpus": os.cpu_count(),
         "parity_rows_checked": done,
         "parity_max_err_over_bound": round(max_ratio, 4),
         "parity_ok": bool(max_ratio <= 1.0),
