@@ -88,6 +88,11 @@ def _bind(lib):
     lib.dit_oracle_subblock_keep.restype = _c_i64
     lib.dit_oracle_subblock_topk.argtypes = [_c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64]
     lib.dit_oracle_subblock_topk.restype = ctypes.c_int
+    lib.dit_oracle_qk_rmsnorm_rope3d_pool.argtypes = [
+        _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p,
+        _c_i64, _c_i64, _c_i64, _c_i64, _c_i32, _c_i32, _c_i32, _c_dbl, _c_dbl, _c_i64,
+    ]
+    lib.dit_oracle_qk_rmsnorm_rope3d_pool.restype = ctypes.c_int
     return lib
 
 
@@ -401,3 +406,26 @@ def subblock_route(q, k, sparsity: float, block: int = SUBBLOCK_TOKENS, lib=None
     s = subblock_scores(qp, kp, lib=lib)
     idx = subblock_topk(s, subblock_keep(qp.shape[2], sparsity, lib=lib), lib=lib)
     return qp, kp, s, idx
+
+
+def qk_rmsnorm_rope3d_pool(q, k, wq, wk, pos, bands, theta: float = 1e4, eps: float = 1e-6,
+                           block: int = SUBBLOCK_TOKENS, lib=None):
+    """QK RMSNorm + 3D RoPE and the block means of its bf16-stored outputs.
+
+    q, k [B,N,H,Dh], wq/wk [Dh] (bf16 bits), pos [N,3] -> (q', k' [B,N,H,Dh], q_pooled, k_pooled [B,H,nb,Dh]).
+    """
+    lib = lib or load()
+    q, k, wq, wk = _bits(q), _bits(k), _bits(wq), _bits(wk)
+    pos = np.ascontiguousarray(pos, dtype=np.int32)
+    B, N, H, Dh = q.shape
+    assert k.shape == q.shape and wq.shape == (Dh,) and wk.shape == (Dh,) and pos.shape == (N, 3)
+    nb = -(-N // block)
+    qo = np.empty(q.shape, dtype=np.float64)
+    ko = np.empty(k.shape, dtype=np.float64)
+    qp = np.empty((B, H, nb, Dh), dtype=np.float64)
+    kp = np.empty((B, H, nb, Dh), dtype=np.float64)
+    d_t, d_h, d_w = (int(b) for b in bands)
+    _check(lib.dit_oracle_qk_rmsnorm_rope3d_pool(
+        _ptr(q), _ptr(k), _ptr(wq), _ptr(wk), _ptr(pos), _ptr(qo), _ptr(ko), _ptr(qp), _ptr(kp),
+        B, N, H, Dh, d_t, d_h, d_w, theta, eps, block), "qk_rmsnorm_rope3d_pool")
+    return qo, ko, qp, kp

@@ -623,3 +623,44 @@ int dit_oracle_subblock_topk(const double *s, int32_t *idx, int64_t B, int64_t H
     free(row); free(kept);
     return status;
 }
+
+/*
+ * QK RMSNorm + 3D RoPE with the SubBlock block means of its outputs.
+ * Cited: the xhh.club Q&A (QK RMSNorm fused with 3D RoPE) and the
+ * stamatios.com summary, "De onde vêm os ganhos" (SubBlock routing over
+ * 64-token blocks); the Sol-H3 abstract describes searching over such kernel
+ * fusions.
+ * Reading: the routing pools q' and k' as stored, i.e. rounded to bf16, as it
+ * does when it reads them back from memory; so this is the QK op, one bf16
+ * rounding of each output, then dit_oracle_subblock_pool.
+ * q, k: [B][N][H][Dh] bf16 bits; q_out, k_out: [B][N][H][Dh] unrounded;
+ * q_pooled, k_pooled: [B][H][nb][Dh], nb = ceil(N / block).
+ */
+int dit_oracle_qk_rmsnorm_rope3d_pool(const uint16_t *q, const uint16_t *k,
+                                      const uint16_t *wq, const uint16_t *wk,
+                                      const int32_t *pos, double *q_out, double *k_out,
+                                      double *q_pooled, double *k_pooled, int64_t B,
+                                      int64_t N, int64_t H, int64_t Dh, int32_t d_t,
+                                      int32_t d_h, int32_t d_w, double theta, double eps,
+                                      int64_t block)
+{
+    if (!q_pooled || !k_pooled || block <= 0)
+        return ORACLE_BAD_ARG;
+    int status = dit_oracle_qk_rmsnorm_rope3d(q, k, wq, wk, pos, q_out, k_out, B, N, H, Dh,
+                                              d_t, d_h, d_w, theta, eps);
+    if (status != ORACLE_OK)
+        return status;
+    const int64_t n_el = B * N * H * Dh;
+    uint16_t *stored = malloc(sizeof(uint16_t) * (size_t)(n_el > 0 ? n_el : 1));
+    if (!stored)
+        return ORACLE_BAD_ARG;
+    for (int which = 0; which < 2 && status == ORACLE_OK; ++which) {
+        const double *u = which == 0 ? q_out : k_out;
+        for (int64_t e = 0; e < n_el; ++e)
+            stored[e] = dit_oracle_bf16_encode(u[e]);
+        status = dit_oracle_subblock_pool(stored, which == 0 ? q_pooled : k_pooled, B, N, H, Dh,
+                                          block);
+    }
+    free(stored);
+    return status;
+}

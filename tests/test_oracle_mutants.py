@@ -105,6 +105,11 @@ MUTANTS = {
                          "            if (kept[j])\n                idx[r * keep + at++] = (int32_t)j;",
                          "        for (int64_t t = 0; t < keep; ++t)\n"
                          "            idx[r * keep + t] = (int32_t)row[t].index;"),
+    # QK + block means of the stored outputs
+    "qk_pool_unrounded_store": ("stored[e] = dit_oracle_bf16_encode(u[e]);",
+                                "{ float f = (float)u[e]; uint32_t w; memcpy(&w, &f, 4); stored[e] = (uint16_t)(w >> 16); }"),
+    "qk_pool_k_into_q": ("status = dit_oracle_subblock_pool(stored, which == 0 ? q_pooled : k_pooled, B, N, H, Dh,",
+                         "status = dit_oracle_subblock_pool(stored, q_pooled, B, N, H, Dh,"),
     # bf16 decode
     "decode_wrong_shift": ("uint32_t word = (uint32_t)bits << 16;", "uint32_t word = (uint32_t)bits << 15;"),
 }

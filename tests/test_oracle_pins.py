@@ -660,6 +660,34 @@ def pin_subblock_route_structured(lib):
     assert idx[0, 0].tolist() == [[0, 2], [1, 3], [0, 3], [0, 3]]
 
 
+def pin_qk_pool_hand_cases(lib):
+    for case in cases("qk_pool_hand.txt"):
+        n_tok = int(case["tokens"][0])
+        v = b16(values(case["v"]) * n_tok, (1, n_tok, 1, 2))
+        w = b16(values(case["w"]))
+        pos = np.zeros((n_tok, 3), dtype=np.int32)
+        qo, ko, qp, kp = oracle.qk_rmsnorm_rope3d_pool(v, v, w, w, pos, (2, 0, 0), 1e4, 1e-6, lib=lib)
+        assert close(qo[0, 0, 0], values(case["exact"]), rel=1e-15), (case, qo)
+        assert qp.reshape(-1).tolist() == values(case["pooled"]), (case, qp)
+        assert np.array_equal(qp, kp)
+
+
+def pin_qk_pool_is_the_pipeline(lib):
+    # the fused oracle equals QK, then the oracle's bf16 store, then block pooling
+    B, N, H, Dh = 2, 130, 2, 64
+    q = rand_bf16((B, N, H, Dh), seed=211)
+    k = rand_bf16((B, N, H, Dh), seed=212, scale=3.0)
+    wq, wk = _weights(Dh, 213), _weights(Dh, 214)
+    pos = np.array([[n // 20, (n // 5) % 4, n % 5] for n in range(N)], dtype=np.int32)
+    qo, ko, qp, kp = oracle.qk_rmsnorm_rope3d_pool(bits(q), bits(k), bits(wq), bits(wk), pos, BANDS, lib=lib)
+    qr, kr = oracle.qk_rmsnorm_rope3d(bits(q), bits(k), bits(wq), bits(wk), pos, BANDS, lib=lib)
+    assert np.array_equal(qo, qr) and np.array_equal(ko, kr)
+    encode = np.vectorize(lambda x: oracle.bf16_encode(x, lib=lib), otypes=[np.uint16])
+    assert np.array_equal(qp, oracle.subblock_pool(encode(qr), lib=lib))
+    assert np.array_equal(kp, oracle.subblock_pool(encode(kr), lib=lib))
+    assert not np.array_equal(qp, kp)
+
+
 # --------------------------------------------------------------------------- argument checks and threading
 
 def pin_rope_rejects_bad_bands(lib):
