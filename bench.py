@@ -59,6 +59,7 @@ KERNEL_SOURCES = {
     "qk_layout": "qk_rope.hip",
     "change": "residual_change.hip",
     "change_final": "residual_change.hip",
+    "qk_pool": "qk_rope.hip",
     "pool": "subblock.hip",
     "pool_hm": "subblock.hip",
     "scores": "subblock.hip",
@@ -66,7 +67,7 @@ KERNEL_SOURCES = {
     "copy": "copy.hip",
 }
 # Kernels of the next rows, measured after the chain (see main()).
-NEXT_OPS = ("residual_adaln", "qk_layout", "change", "change_final", "pool", "pool_hm", "scores", "topk")
+NEXT_OPS = ("residual_adaln", "qk_layout", "change", "change_final", "qk_pool", "pool", "pool_hm", "scores", "topk")
 ROUTE_SPARSITY = 0.75
 COUNTER_SUMMARY = os.path.join(ROOT, "profiles", "{op}_{workload}_counters.md")
 
@@ -90,6 +91,7 @@ def op_bytes(wl, next_rows: bool = False) -> dict:
             "residual_adaln": 4 * R * D * 2 + 3 * B * D * 2,   # x, y in, x_out, z out, gate + shift + scale
             "qk_layout": out["qk"],                            # same bytes, strided in, head-major out
             "change": 2 * R * D * 2,                           # r, r_cached in (partials: 16 B per 2048 vectors)
+            "qk_pool": out["qk"] + pooled,                     # QK's bytes plus the block means out
             "pool": 2 * R * H * Dh * 2 + pooled,               # q', k' in, fp32 block means out
             "pool_hm": 2 * R * H * Dh * 2 + pooled,
             "scores": pooled + B * H * nb * nb * 4,            # means in, fp32 scores out
@@ -399,9 +401,15 @@ def main(argv=None) -> int:
     ko_as_hm = ko.view(wl.B, wl.H, wl.N, wl.Dh)
     pool_hm_ms = timed(lambda: dit.dit_subblock_pool(qo_as_hm, ko_as_hm, head_major=True, q_pooled=qp_s,
                                                      k_pooled=kp_s, stream=stream))
-    dit.dit_subblock_pool(qo, ko, q_pooled=qp_s, k_pooled=kp_s, stream=stream)
     scores_ms = timed(lambda: dit.dit_subblock_route(qp_s, kp_s, keep=0, scores=sc, kept=kept0, stream=stream))
     route_ms = timed(lambda: dit.dit_subblock_route(qp_s, kp_s, keep=keep, scores=sc, kept=kept, stream=stream))
+    # QK RMSNorm + RoPE that also writes the block means (no second read of q', k')
+    qo_f, ko_f = torch.empty_like(qo), torch.empty_like(ko)
+    qk_pool_ms = timed(lambda: dit.dit_qk_rmsnorm_rope3d_pool(ins["q"], ins["k"], ins["wq"], ins["wk"], pos, wl.bands,
+                                                              q_out=qo_f, k_out=ko_f, q_pooled=qp_s, k_pooled=kp_s,
+                                                              theta=wl.theta, eps=wl.eps, stream=stream))
+    del qo_f, ko_f
+    dit.dit_subblock_pool(qo, ko, q_pooled=qp_s, k_pooled=kp_s, stream=stream)
     pooled_bytes = 2 * wl.B * wl.H * nb * wl.Dh * 4
     score_elems = wl.B * wl.H * nb * nb
     pool_bytes = 2 * wl.R * wl.H * wl.Dh * 2 + pooled_bytes
@@ -413,11 +421,15 @@ def main(argv=None) -> int:
         "sparsity": sparsity, "blocks": nb, "keep": keep,
         "pool": rate(pool_bytes, pool_ms, "pool"),
         "pool_head_major": rate(pool_bytes, pool_hm_ms, "pool_hm"),
+        "qk_with_pool": {**rate(nbytes["qk"] + pooled_bytes, qk_pool_ms, "qk_pool"),
+                         "op": "dit_qk_rmsnorm_rope3d_pool (QK writing the block means too)",
+                         "separate_ms": round(ops["qk"]["avg_ms"] + pool_ms, 5)},
         "scores": {**rate(scores_bytes, scores_ms, "scores"),
                    "TFLOP_s": round(score_flops / (scores_ms * 1e-3) / 1e12, 1),
                    "pct_of_bf16_mfma_peak": round(100.0 * score_flops / (scores_ms * 1e-3) / 2.5e15, 2)},
         "topk": rate(topk_bytes, topk_ms, "topk"),
         "total_ms": round(pool_ms + route_ms, 5),
+        "total_after_fused_qk_ms": round(qk_pool_ms - ops["qk"]["avg_ms"] + route_ms, 5),
     }
     del qp_s, kp_s, sc, kept, kept0
 
@@ -664,6 +676,7 @@ KERNEL_OPS = (
     (r"adaln_modulate_kernel", "adaln"),
     (r"gated_residual_kernel", "residual"),
     (r"swiglu_kernel", "swiglu"),
+    (r"qk_rmsnorm_rope3d_pool_kernel", "qk_pool"),
     (r"qk_rmsnorm_rope3d_kernel<\d+, true>", "qk_layout"),
     (r"qk_rmsnorm_rope3d_kernel", "qk"),
     (r"residual_change_partial_kernel", "change"),

@@ -301,6 +301,33 @@ dit_status dit_subblock_pool(const dit_bf16 *q, const dit_bf16 *k,
                              void *stream);
 
 /*
+ * QK RMSNorm + 3D RoPE fused with the block means of its outputs: q_out, k_out
+ * are exactly those of dit_qk_rmsnorm_rope3d, and q_pooled, k_pooled exactly
+ * those dit_subblock_pool computes from the stored q_out, k_out
+ * (DIT_QK_TOKEN_MAJOR), without reading them back from memory.
+ * Cited: xhh.club Q&A ("QK RMSNorm fused with 3D RoPE"); stamatios.com
+ * summary, "De onde vêm os ganhos" (SubBlock 64-token blocks); Sol-H3
+ * abstract (search over kernel fusions).  Reading: the routing pools q', k' as
+ * stored in bf16.
+ *   q, k, q_out, k_out   bf16 [B][N][H][Dh]; q_out == q and k_out == k allowed,
+ *                        any other overlap DIT_ERR_ARG
+ *   wq, wk, pos          as for dit_qk_rmsnorm_rope3d
+ *   q_pooled, k_pooled   fp32 [B][H][ceil(N/64)][Dh], 16-byte aligned, overlapping
+ *                        nothing else (DIT_ERR_ARG)
+ *   Dh in {16, 32, 64, 128, 256}, bands as for dit_qk_rmsnorm_rope3d, H*Dh <=
+ *   65536 (else DIT_ERR_SHAPE); N <= 262,144 and B <= 65535 (else DIT_ERR_ARG).
+ * B == 0 or N == 0 is a no-op.
+ */
+dit_status dit_qk_rmsnorm_rope3d_pool(const dit_bf16 *q, const dit_bf16 *k,
+                                      dit_bf16 *q_out, dit_bf16 *k_out,
+                                      const dit_bf16 *wq, const dit_bf16 *wk,
+                                      const int32_t *pos, float *q_pooled,
+                                      float *k_pooled, int64_t B, int64_t N,
+                                      int64_t H, int64_t Dh, int32_t d_t,
+                                      int32_t d_h, int32_t d_w, float theta,
+                                      float eps, void *stream);
+
+/*
  * Block scores and the kept key blocks of every query block:
  *   scores[b][h][i][j] = sum_d bf16(q_pooled[b][h][i][d]) *
  *                               bf16(k_pooled[b][h][j][d])

@@ -242,6 +242,27 @@ def test_subblock_pool_validation(lib):
     assert f(q=0, k=0, qp=0, kp=0, B=0) == DIT_OK
 
 
+def test_qk_pool_validation(lib):
+    # B=1, N=128, H=2, Dh=16 (bands 4/6/6): q, k 8 KiB each, pooled 2*2*16 floats
+    def f(q=P, k=Q, qo=R, ko=S, wq=T, wk=T + 64, pos=U, qp=V, kp=V + 4096, B=1, N=128, H=2, Dh=16, bands=(4, 6, 6),
+          theta=1e4, eps=1e-6):
+        return lib.dit_qk_rmsnorm_rope3d_pool(q, k, qo, ko, wq, wk, pos, qp, kp, B, N, H, Dh, *bands, theta, eps, None)
+
+    assert f(B=-1, qp=0) == DIT_ERR_ARG
+    assert f(N=4096 * 64 + 1, qp=0) == DIT_ERR_ARG
+    assert f(Dh=8, bands=(2, 2, 4), qp=0) == DIT_ERR_SHAPE  # pooling needs Dh >= 16
+    assert f(bands=(4, 6, 4), qp=0) == DIT_ERR_SHAPE and f(bands=(5, 5, 6), qp=0) == DIT_ERR_SHAPE
+    assert f(eps=0.0, qp=0) == DIT_ERR_ARG and f(theta=1.0, qp=0) == DIT_ERR_ARG
+    assert f(qp=0) == DIT_ERR_NULL and f(pos=0) == DIT_ERR_NULL
+    assert f(kp=V + 4) == DIT_ERR_ALIGN and f(q=P + 8) == DIT_ERR_ALIGN
+    assert f(qp=P + 64) == DIT_ERR_ARG  # pooled q over q
+    assert f(kp=V + 64) == DIT_ERR_ARG  # the two pooled outputs overlap
+    assert f(kp=R) == DIT_ERR_ARG  # pooled k over q_out
+    assert f(qo=P + 16) == DIT_ERR_ARG  # q_out partly over q
+    assert f(ko=P) == DIT_ERR_ARG  # k_out over q
+    assert f(q=0, k=0, qo=0, ko=0, wq=0, wk=0, pos=0, qp=0, kp=0, N=0) == DIT_OK
+
+
 def test_subblock_route_validation(lib):
     # B=1, H=2, nb=5, Dh=16: pooled 640 B each, scores 2*5*8 floats, kept 2*5*keep ints
     def f(qp=P, kp=Q, sc=R, kept=S, B=1, H=2, nb=5, Dh=16, keep=2):

@@ -28,9 +28,10 @@ import torch
 
 import oracle
 import video_diffusion_transformer_dit_amd as dit
+from parity_util import assert_close
 from subblock_checks import (check_kept_lists, check_top_set_of_own_scores, check_valid_against_oracle,
                              flip_room, pool_bound, score_bound, set_agreement)
-from synthetic_inputs import WORKLOADS, bits, correlated_heads
+from synthetic_inputs import WORKLOADS, bits, correlated_heads, make_inputs
 
 pytestmark = pytest.mark.gpu
 
@@ -247,3 +248,82 @@ def test_end_to_end_workload(name):
     agree = end_to_end(wl.B, wl.N, wl.H, wl.Dh, 0.75, seed=71, sample_rows=rows)
     print(f"[subblock] {name}: kept-set agreement with the oracle {agree:.4f}", flush=True)
     assert agree > 0.95
+
+
+# --------------------------------------------------------------------------- QK RMSNorm + RoPE fused with pooling
+
+QK_POOL_SHAPES = [
+    # B, N, H, Dh, bands
+    (1, 200, 2, 64, (16, 24, 24)),
+    (2, 321, 3, 16, (4, 6, 6)),        # ragged last block of 1 token
+    (1, 130, 2, 256, (32, 112, 112)),  # 128 rotary pairs: two per lane
+    (1, 64, 1, 32, (8, 12, 12)),
+    (1, 1, 4, 128, (16, 56, 56)),
+    (1, 100, 5, 128, (16, 56, 56)),    # a partial second column chunk
+]
+
+
+def qk_pool_inputs(B, N, H, Dh, seed):
+    g = torch.Generator().manual_seed(seed)
+    q = (torch.randn((B, N, H, Dh), generator=g) * 1.5).to(torch.bfloat16).to(DEV)
+    k = (torch.randn((B, N, H, Dh), generator=g) * 0.7).to(torch.bfloat16).to(DEV)
+    wq = (1.0 + 0.02 * torch.randn(Dh, generator=g)).to(torch.bfloat16).to(DEV)
+    wk = (1.0 + 0.02 * torch.randn(Dh, generator=g)).to(torch.bfloat16).to(DEV)
+    grid = (max(1, N // 30), 5, 6)
+    extra = N - grid[0] * 30 if N >= 30 else N
+    if N < 30:
+        grid = (0, 5, 6)
+    pos = dit.dit_packed_positions(*grid, extra, device=DEV)
+    return q, k, wq, wk, pos
+
+
+@pytest.mark.parametrize("shape", QK_POOL_SHAPES, ids=lambda s: "x".join(map(str, s[:4])))
+def test_qk_pool_matches_parts_and_oracle(shape):
+    B, N, H, Dh, bands = shape
+    q, k, wq, wk, pos = qk_pool_inputs(B, N, H, Dh, seed=N + Dh)
+    qo, ko, qp, kp = dit.dit_qk_rmsnorm_rope3d_pool(q, k, wq, wk, pos, bands)
+    qr, kr = dit.dit_qk_rmsnorm_rope3d(q, k, wq, wk, pos, bands)
+    qpr, kpr = dit.dit_subblock_pool(qr, kr)
+    torch.cuda.synchronize()
+    # the same outputs as the two separate kernels, bit for bit
+    assert torch.equal(qo, qr) and torch.equal(ko, kr)
+    assert torch.equal(qp, qpr) and torch.equal(kp, kpr)
+    # Against the oracle: outputs within the bf16 bound.  The oracle's means are
+    # of bf16(exact q'), the kernel's of its stored q' (each within
+    # 1e-2 + 8e-3|q'| of exact q'), and bf16 rounding moves a value by at most
+    # 2^-9 of it, so each mean is within 1e-2 + (8e-3 + 2^-9) * mean|q'|, plus
+    # the fp32 sum's own error.
+    o_q, o_k, o_qp, o_kp = oracle.qk_rmsnorm_rope3d_pool(bits(q), bits(k), bits(wq), bits(wk), to_host(pos), bands)
+    assert_close(qo, o_q, "q'")
+    assert_close(ko, o_k, "k'")
+    for got, ref_out, ref in ((qp, o_q, o_qp), (kp, o_k, o_kp)):
+        mean_abs = oracle.subblock_pool(bits(torch.from_numpy(np.abs(ref_out)).float().to(torch.bfloat16)))
+        bound = 1e-2 + (8e-3 + 2.0 ** -9) * 1.01 * mean_abs + 64 * 2.0 ** -24 * mean_abs
+        err = np.abs(to_host(got).astype(np.float64) - ref)
+        assert np.all(err <= bound), f"pooled: worst err/bound {(err / bound).max():.3g}"
+
+
+def test_qk_pool_in_place():
+    B, N, H, Dh, bands = 1, 257, 4, 128, (16, 56, 56)
+    q, k, wq, wk, pos = qk_pool_inputs(B, N, H, Dh, seed=3)
+    qr, kr, qpr, kpr = dit.dit_qk_rmsnorm_rope3d_pool(q, k, wq, wk, pos, bands)
+    qi, ki = q.clone(), k.clone()
+    dit.dit_qk_rmsnorm_rope3d_pool(qi, ki, wq, wk, pos, bands, q_out=qi, k_out=ki)
+    torch.cuda.synchronize()
+    assert torch.equal(qi, qr) and torch.equal(ki, kr)
+
+
+@pytest.mark.parametrize("name", ["full5s", "full10s"])
+def test_qk_pool_full_workload_equals_parts(name):
+    wl = WORKLOADS[name]
+    ins = make_inputs(wl, device=DEV, names=("q", "k", "wq", "wk"))
+    pos = dit.dit_packed_positions(*wl.grid, wl.n_extra, device=DEV)
+    qo, ko, qp, kp = dit.dit_qk_rmsnorm_rope3d_pool(ins["q"], ins["k"], ins["wq"], ins["wk"], pos, wl.bands,
+                                                    theta=wl.theta, eps=wl.eps)
+    qr, kr = dit.dit_qk_rmsnorm_rope3d(ins["q"], ins["k"], ins["wq"], ins["wk"], pos, wl.bands, theta=wl.theta,
+                                       eps=wl.eps)
+    assert torch.equal(qo, qr) and torch.equal(ko, kr)
+    del ins
+    qpr, kpr = dit.dit_subblock_pool(qr, kr)
+    torch.cuda.synchronize()
+    assert torch.equal(qp, qpr) and torch.equal(kp, kpr)

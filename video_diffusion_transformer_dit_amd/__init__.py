@@ -12,6 +12,7 @@ hand-written HIP kernels (``csrc/``; declarations in ``include/dit_ops.h``):
                           writing head-major outputs
   dit_residual_change     Cache-DiT statistic: sum |r - r_cached| / sum |r_cached| per sample
   dit_subblock_pool       SubBlock routing: means of each 64-token block of q' and k'
+  dit_qk_rmsnorm_rope3d_pool  QK RMSNorm + RoPE that also writes those block means
   dit_subblock_route      SubBlock routing: block scores and the kept key blocks per query block
   dit_packed_positions    (t, h, w) coordinates of a packed token sequence
   dit_copy16              plain 16-byte-vector copy (bandwidth ceiling)
@@ -40,6 +41,7 @@ from ._binding import (  # noqa: F401
     dit_packed_positions,
     dit_qk_rmsnorm_rope3d,
     dit_qk_rmsnorm_rope3d_layout,
+    dit_qk_rmsnorm_rope3d_pool,
     dit_residual_change,
     dit_residual_change_workspace_bytes,
     dit_status_str,

@@ -37,6 +37,8 @@ SIGNATURES = {
     "dit_subblock_scores_ld": ([_I64], ctypes.c_int64),
     "dit_subblock_pool": ([_P, _P, _P, _P, _I64, _I64, _I64, _I64, _I32, _P], ctypes.c_int),
     "dit_subblock_route": ([_P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _P], ctypes.c_int),
+    "dit_qk_rmsnorm_rope3d_pool": ([_P, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I32, _I32, _I32,
+                                    _F32, _F32, _P], ctypes.c_int),
     "dit_packed_positions": ([_P, _I64, _I64, _I64, _I64, _P], ctypes.c_int),
     "dit_copy16": ([_P, _P, _I64, _P], ctypes.c_int),
 }
@@ -308,6 +310,38 @@ def dit_subblock_pool(q, k, head_major: bool = False, q_pooled=None, k_pooled=No
             q.data_ptr(), k.data_ptr(), q_pooled.data_ptr(), k_pooled.data_ptr(), B, N, H, Dh,
             DIT_QK_HEAD_MAJOR if head_major else DIT_QK_TOKEN_MAJOR, _stream(stream, dev)))
     return q_pooled, k_pooled
+
+
+def dit_qk_rmsnorm_rope3d_pool(q, k, wq, wk, pos, bands, q_out=None, k_out=None, q_pooled=None, k_pooled=None,
+                               theta: float = 1e4, eps: float = 1e-6, stream=None):
+    """dit_qk_rmsnorm_rope3d plus the 64-token block means of its stored outputs.
+
+    q, k [B,N,H,Dh] bf16 -> (q_out, k_out [B,N,H,Dh] bf16, q_pooled, k_pooled [B,H,nb,Dh] fp32).
+    """
+    _tensor(q, "q", ndim=4)
+    B, N, H, Dh = q.shape
+    _shape(_tensor(k, "k"), "k", (B, N, H, Dh))
+    _shape(_tensor(wq, "wq"), "wq", (Dh,))
+    _shape(_tensor(wk, "wk"), "wk", (Dh,))
+    _shape(_tensor(pos, "pos", dtype=torch.int32), "pos", (N, 3))
+    q_out = torch.empty_like(q) if q_out is None else q_out
+    k_out = torch.empty_like(k) if k_out is None else k_out
+    _shape(_tensor(q_out, "q_out"), "q_out", (B, N, H, Dh))
+    _shape(_tensor(k_out, "k_out"), "k_out", (B, N, H, Dh))
+    nb = -(-N // DIT_SUBBLOCK_TOKENS)
+    pshape = (B, H, nb, Dh)
+    q_pooled = torch.empty(pshape, dtype=torch.float32, device=q.device) if q_pooled is None else q_pooled
+    k_pooled = torch.empty(pshape, dtype=torch.float32, device=q.device) if k_pooled is None else k_pooled
+    _shape(_tensor(q_pooled, "q_pooled", dtype=torch.float32), "q_pooled", pshape)
+    _shape(_tensor(k_pooled, "k_pooled", dtype=torch.float32), "k_pooled", pshape)
+    d_t, d_h, d_w = (int(b) for b in bands)
+    dev = _same_device(q, k, wq, wk, pos, q_out, k_out, q_pooled, k_pooled)
+    with torch.cuda.device(dev):
+        _check("dit_qk_rmsnorm_rope3d_pool", load_library().dit_qk_rmsnorm_rope3d_pool(
+            q.data_ptr(), k.data_ptr(), q_out.data_ptr(), k_out.data_ptr(), wq.data_ptr(), wk.data_ptr(),
+            pos.data_ptr(), q_pooled.data_ptr(), k_pooled.data_ptr(), B, N, H, Dh, d_t, d_h, d_w, float(theta),
+            float(eps), _stream(stream, dev)))
+    return q_out, k_out, q_pooled, k_pooled
 
 
 def dit_subblock_route(q_pooled, k_pooled, sparsity: float | None = None, keep: int | None = None, scores=None,

@@ -140,6 +140,164 @@ __global__ __launch_bounds__(kQKThreads) void qk_rmsnorm_rope3d_kernel(
         store_stream((which ? k_out : q_out) + dst, o);
 }
 
+// Per channel pair: turns per unit coordinate and band axis, from (Dh, bands,
+// theta), evaluated once on the host in double.
+RotaryPlan make_rotary_plan(int64_t Dh, int d_t, int d_h, int d_w, float theta)
+{
+    RotaryPlan plan = {};
+    const double log2_theta = log2((double)theta);
+    for (int i = 0; i < (int)Dh / 2; ++i) {
+        const int ch = 2 * i;
+        int axis, lo, width;
+        if (ch < d_t) {
+            axis = 0, lo = 0, width = d_t;
+        } else if (ch < d_t + d_h) {
+            axis = 1, lo = d_t, width = d_h;
+        } else {
+            axis = 2, lo = d_t + d_h, width = d_w;
+        }
+        plan.axis[i] = axis;
+        plan.turns_per_unit[i] = exp2(-(double)(ch - lo) / (double)width * log2_theta) / (2.0 * M_PI);
+    }
+    (void)d_w;
+    return plan;
+}
+
+// QK RMSNorm + RoPE fused with the SubBlock block means of its outputs
+// (token-major in and out).  grid (chunks * nb, 2 (q then k), B), 512
+// threads.  A workgroup covers one 64-token block and one chunk of 64 vector
+// columns (64 * 8 / Dh heads): wave w handles tokens w, w+8, ..., w+56 of the
+// block, each across its 64 columns just as the QK kernel handles a token (a
+// head is LPH adjacent lanes), stores every normalised, rotated vector, and
+// adds the stored bf16 values into eight fp32 sums per lane.  Wave 0 then adds
+// the other waves' sums in order and writes the means -- the order of the
+// standalone pooling kernel, so the means equal pooling the stored q', k'
+// bit for bit, and q', k' equal the QK kernel's bit for bit (same rotary
+// arithmetic, same norm_rotate).  The token's (cos, sin) pairs are computed
+// once per wave and token, pair p by lane p % 64, and fetched with lane
+// shuffles.  Pooling this way costs no HBM traffic beyond QK's own.
+constexpr int kQKPoolWaves = 8;
+constexpr int kQKPoolTokens = 64; // SubBlock block size
+
+template <int LPH>
+__global__ __launch_bounds__(kQKPoolWaves * kWave) void qk_rmsnorm_rope3d_pool_kernel(
+    const u32x4 *q, const u32x4 *k, u32x4 *q_out, u32x4 *k_out, const u32x4 *__restrict__ wq,
+    const u32x4 *__restrict__ wk, const int32_t *__restrict__ pos, float *__restrict__ qp, float *__restrict__ kp,
+    int N, int nb, int C, int chunks, float inv_dh, float eps, const RotaryPlan plan)
+{
+    constexpr int kPerWave = kQKPoolTokens / kQKPoolWaves;
+    constexpr int kPairs = 4 * LPH;                       // channel pairs per head
+    constexpr int kPairSlots = kPairs > kWave ? kPairs / kWave : 1; // pairs computed per lane
+    __shared__ float4 part[kQKPoolWaves - 1][2][kWave];
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    const int chunk = blockIdx.x % chunks, blk = blockIdx.x / chunks;
+    const int which = blockIdx.y; // 0: q, 1: k
+    const size_t b = blockIdx.z;
+    const u32x4 *src = which ? k : q;
+    u32x4 *dst = which ? k_out : q_out;
+    const int c = chunk * kWave + lane;
+    const bool valid = c < C;
+    const int n0 = blk * kQKPoolTokens;
+    const int count = min(kQKPoolTokens, N - n0);
+    const int slot = lane % LPH; // chunks start on head boundaries: c % LPH == lane % LPH
+
+    float w[8];
+    unpack8(load_cached((which ? wk : wq) + slot), w);
+    double tpu[kPairSlots];
+    int axis[kPairSlots];
+#pragma unroll
+    for (int m = 0; m < kPairSlots; ++m) {
+        const int pr = (lane + kWave * m) % kPairs;
+        tpu[m] = plan.turns_per_unit[pr];
+        axis[m] = plan.axis[pr];
+    }
+
+    const size_t row0 = (size_t)b * N + n0;
+    u32x4 raw[kPerWave];
+#pragma unroll
+    for (int t = 0; t < kPerWave; ++t) {
+        const int n = wave + kQKPoolWaves * t; // wave-uniform
+        raw[t] = (valid && n < count) ? load_stream(src + (row0 + n) * C + c) : u32x4{0u, 0u, 0u, 0u};
+    }
+
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < kPerWave; ++t) {
+        const int n = wave + kQKPoolWaves * t;
+        if (n < count) { // wave-uniform
+            const int32_t *p = pos + 3 * (size_t)(n0 + n);
+            const int p_t = p[0], p_h = p[1], p_w = p[2];
+            float2 mine[kPairSlots];
+#pragma unroll
+            for (int m = 0; m < kPairSlots; ++m) {
+                const int coord = axis[m] == 0 ? p_t : (axis[m] == 1 ? p_h : p_w);
+                const double turns = (double)coord * tpu[m];
+                const float r = (float)(turns - rint(turns));
+                mine[m] = make_float2(__builtin_amdgcn_cosf(r), __builtin_amdgcn_sinf(r));
+            }
+            float cs[4], sn[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int pr = 4 * slot + j;
+                const int from = pr % kWave;
+                float cj = __shfl(mine[0].x, from, kWave), sj = __shfl(mine[0].y, from, kWave);
+#pragma unroll
+                for (int m = 1; m < kPairSlots; ++m) {
+                    const float cm = __shfl(mine[m].x, from, kWave), sm = __shfl(mine[m].y, from, kWave);
+                    cj = pr / kWave == m ? cm : cj;
+                    sj = pr / kWave == m ? sm : sj;
+                }
+                cs[j] = cj;
+                sn[j] = sj;
+            }
+            const u32x4 o = norm_rotate<LPH>(raw[t], w, cs, sn, inv_dh, eps);
+            if (valid)
+                store_stream(dst + (row0 + n) * C + c, o);
+            float f[8];
+            unpack8(o, f);
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                acc[i] += valid ? f[i] : 0.f;
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                acc[i] += 0.f; // the standalone pooling adds the zero vectors of absent tokens
+        }
+    }
+    if (wave > 0) {
+        part[wave - 1][0][lane] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+        part[wave - 1][1][lane] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+    }
+    __syncthreads();
+    if (wave == 0 && valid) {
+#pragma unroll
+        for (int v = 0; v < kQKPoolWaves - 1; ++v) {
+            const float4 lo = part[v][0][lane], hi = part[v][1][lane];
+            acc[0] += lo.x, acc[1] += lo.y, acc[2] += lo.z, acc[3] += lo.w;
+            acc[4] += hi.x, acc[5] += hi.y, acc[6] += hi.z, acc[7] += hi.w;
+        }
+        const int H = C / LPH, h = c / LPH, Dh = 8 * LPH;
+        float *o = (which ? kp : qp) + (((size_t)b * H + h) * nb + blk) * Dh + slot * 8;
+        float4 *o4 = reinterpret_cast<float4 *>(o);
+        const float cnt = (float)count;
+        o4[0] = make_float4(acc[0] / cnt, acc[1] / cnt, acc[2] / cnt, acc[3] / cnt);
+        o4[1] = make_float4(acc[4] / cnt, acc[5] / cnt, acc[6] / cnt, acc[7] / cnt);
+    }
+}
+
+template <int LPH>
+hipError_t launch_pool_lph(const u32x4 *q, const u32x4 *k, u32x4 *qo, u32x4 *ko, const u32x4 *wq, const u32x4 *wk,
+                           const int32_t *pos, float *qp, float *kp, int B, int N, int C, float inv_dh, float eps,
+                           const RotaryPlan &plan, hipStream_t stream)
+{
+    const int nb = (N + kQKPoolTokens - 1) / kQKPoolTokens;
+    const int chunks = (C + kWave - 1) / kWave;
+    hipLaunchKernelGGL((qk_rmsnorm_rope3d_pool_kernel<LPH>), dim3((unsigned)(chunks * nb), 2u, (unsigned)B),
+                       dim3(kQKPoolWaves * kWave), 0, stream, q, k, qo, ko, wq, wk, pos, qp, kp, N, nb, C, chunks,
+                       inv_dh, eps, plan);
+    return hipGetLastError();
+}
+
 template <int LPH>
 hipError_t launch_lph(const u32x4 *q, const u32x4 *k, u32x4 *qo, u32x4 *ko, const u32x4 *wq, const u32x4 *wk,
                       const int32_t *pos, int rows, int N, int H, int VPR, int64_t in_stride, bool head_major,
@@ -174,21 +332,7 @@ hipError_t launch_qk_rmsnorm_rope3d(const void *q, const void *k, void *q_out, v
     const float inv_dh = 1.f / (float)Dh;
     const int r = (int)rows, n = (int)N, h = (int)H;
 
-    RotaryPlan plan = {};
-    const double log2_theta = log2((double)theta);
-    for (int i = 0; i < (int)Dh / 2; ++i) {
-        const int ch = 2 * i;
-        int axis, lo, width;
-        if (ch < d_t) {
-            axis = 0, lo = 0, width = d_t;
-        } else if (ch < d_t + d_h) {
-            axis = 1, lo = d_t, width = d_h;
-        } else {
-            axis = 2, lo = d_t + d_h, width = d_w;
-        }
-        plan.axis[i] = axis;
-        plan.turns_per_unit[i] = exp2(-(double)(ch - lo) / (double)width * log2_theta) / (2.0 * M_PI);
-    }
+    const RotaryPlan plan = make_rotary_plan(Dh, d_t, d_h, d_w, theta);
 #define DIT_QK_LAUNCH(L) launch_lph<L>(qv, kv, qo, ko, wqv, wkv, pos, r, n, h, VPR, in_stride, head_major, inv_dh, eps, plan, stream)
     switch (Dh) {
     case 8: return DIT_QK_LAUNCH(1);
@@ -200,6 +344,33 @@ hipError_t launch_qk_rmsnorm_rope3d(const void *q, const void *k, void *q_out, v
     default: return hipErrorInvalidValue;
     }
 #undef DIT_QK_LAUNCH
+}
+
+hipError_t launch_qk_rmsnorm_rope3d_pool(const void *q, const void *k, void *q_out, void *k_out, const void *wq,
+                                         const void *wk, const int32_t *pos, float *q_pooled, float *k_pooled,
+                                         int64_t B, int64_t N, int64_t H, int64_t Dh, int d_t, int d_h, int d_w,
+                                         float theta, float eps, hipStream_t stream)
+{
+    const auto *qv = static_cast<const u32x4 *>(q);
+    const auto *kv = static_cast<const u32x4 *>(k);
+    auto *qo = static_cast<u32x4 *>(q_out);
+    auto *ko = static_cast<u32x4 *>(k_out);
+    const auto *wqv = static_cast<const u32x4 *>(wq);
+    const auto *wkv = static_cast<const u32x4 *>(wk);
+    const int C = (int)(H * Dh / 8);
+    const float inv_dh = 1.f / (float)Dh;
+    const RotaryPlan plan = make_rotary_plan(Dh, d_t, d_h, d_w, theta);
+    const int b = (int)B, n = (int)N;
+#define DIT_QK_POOL_LAUNCH(L) launch_pool_lph<L>(qv, kv, qo, ko, wqv, wkv, pos, q_pooled, k_pooled, b, n, C, inv_dh, eps, plan, stream)
+    switch (Dh) {
+    case 16: return DIT_QK_POOL_LAUNCH(2);
+    case 32: return DIT_QK_POOL_LAUNCH(4);
+    case 64: return DIT_QK_POOL_LAUNCH(8);
+    case 128: return DIT_QK_POOL_LAUNCH(16);
+    case 256: return DIT_QK_POOL_LAUNCH(32);
+    default: return hipErrorInvalidValue;
+    }
+#undef DIT_QK_POOL_LAUNCH
 }
 
 } // namespace dit
