@@ -737,13 +737,26 @@ def summarize_rocprof(trace_dir: str, fetch_dir: str, write_dir: str, workload: 
     os.makedirs(out_dir, exist_ok=True)
     commands = PROFILE_COMMANDS.format(wl=workload)
 
+    # Per-dispatch durations; each op keeps only its full-size launches (the
+    # largest grid it ran with): the benchmark also runs the chain's kernels on
+    # one GPU's share of the tokens, and those smaller launches are left out.
+    by_grid = {}
+    for r in _csv_rows(trace_dir, "kernel_trace.csv"):
+        op = _kernel_op(r["Kernel_Name"])
+        if not op:
+            continue
+        grid = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
+        us = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        m = re.search(r"::(\w+(?:<[^()]*>)?)\(", r["Kernel_Name"])
+        entry = by_grid.setdefault(op, {}).setdefault(grid, {"name": m.group(1) if m else r["Kernel_Name"][:60],
+                                                             "us": []})
+        entry["us"].append(us)
     stats = {}
-    for r in _csv_rows(trace_dir, "kernel_stats.csv"):
-        op = _kernel_op(r["Name"])
-        if op:
-            m = re.search(r"::(\w+(?:<[^()]*>)?)\(", r["Name"])
-            stats[op] = {"name": m.group(1) if m else r["Name"][:60], "calls": int(r["Calls"]), "avg_us": float(r["AverageNs"]) / 1e3,
-                         "min_us": float(r["MinNs"]) / 1e3, "max_us": float(r["MaxNs"]) / 1e3}
+    for op, grids in by_grid.items():
+        full = grids[max(grids)]
+        t = full["us"]
+        stats[op] = {"name": full["name"], "calls": len(t), "avg_us": sum(t) / len(t), "min_us": min(t),
+                     "max_us": max(t), "smaller_launches": sum(len(g["us"]) for g in grids.values()) - len(t)}
 
     counters = {"FETCH_SIZE": {}, "WRITE_SIZE": {}}
     calib = {"FETCH_SIZE": [0.0, 0.0], "WRITE_SIZE": [0.0, 0.0]}  # known bytes, counter bytes
@@ -758,16 +771,20 @@ def summarize_rocprof(trace_dir: str, fetch_dir: str, write_dir: str, workload: 
                 calib[name][0] += 16.0 * int(r["Grid_Size"])
                 calib[name][1] += kib * 1024.0
             else:
-                counters[name].setdefault(op, []).append(kib)
+                counters[name].setdefault(op, {}).setdefault(int(r["Grid_Size"]), []).append(kib)
+    for name in counters:  # full-size launches only, as for the durations
+        counters[name] = {op: grids[max(grids)] for op, grids in counters[name].items()}
     factor = {k: (v[0] / v[1] if v[1] else None) for k, v in calib.items()}
 
     lines = [f"# Kernel durations: {wl.description}", "",
-             "rocprofv3 kernel trace of the benchmark (10 timed + 2 warm-up steps of the chain, then the same "
-             "counts of each next-row kernel and the copy-ceiling copies). Bytes are the compulsory "
-             "(algorithmic) HBM bytes of one launch; GB/s uses the average duration.", "", "Commands (REPO = the repository root, OUT = an output directory for the raw rocprofv3 files):", "", "```",
+             "rocprofv3 kernel trace of the benchmark (10 timed + 2 warm-up steps of the chain, then the "
+             "flushed per-op calls, the same counts of each next-row kernel and the copy-ceiling copies). "
+             "Each kernel's figures cover its full-size launches only; `smaller` counts the launches on one "
+             "GPU's share of the tokens, left out. Bytes are the compulsory (algorithmic) HBM bytes of one "
+             "launch; GB/s uses the average duration.", "", "Commands (REPO = the repository root, OUT = an output directory for the raw rocprofv3 files):", "", "```",
              commands, "```", "",
-             "| kernel | calls | avg us | min us | max us | algorithmic bytes | GB/s at avg | % of 8 TB/s |",
-             "|---|---|---|---|---|---|---|---|"]
+             "| kernel | calls | smaller | avg us | min us | max us | algorithmic bytes | GB/s at avg | % of 8 TB/s |",
+             "|---|---|---|---|---|---|---|---|---|"]
     for op in (*OPS, *NEXT_OPS, "copy"):
         if op not in stats:
             continue
@@ -775,8 +792,8 @@ def summarize_rocprof(trace_dir: str, fetch_dir: str, write_dir: str, workload: 
         b = nbytes.get(op)
         gbs = f"{b / (st['avg_us'] * 1e-6) / 1e9:.1f}" if b else "-"
         pct = f"{100 * b / (st['avg_us'] * 1e-6) / 1e9 / HBM_PEAK_GBPS:.1f}" if b else "-"
-        lines.append(f"| `{st['name']}` | {st['calls']} | {st['avg_us']:.2f} | {st['min_us']:.2f} | {st['max_us']:.2f} "
-                     f"| {b if b else '-'} | {gbs} | {pct} |")
+        lines.append(f"| `{st['name']}` | {st['calls']} | {st['smaller_launches']} | {st['avg_us']:.2f} "
+                     f"| {st['min_us']:.2f} | {st['max_us']:.2f} | {b if b else '-'} | {gbs} | {pct} |")
     with open(os.path.join(out_dir, f"kernels_{workload}_trace.md"), "w", encoding="utf-8") as fh:
         fh.write("\n".join(lines) + "\n")
 
