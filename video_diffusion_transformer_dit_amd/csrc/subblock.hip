@@ -18,6 +18,8 @@
 //   scores are a batched 1953 x 1953 x 128 product per head (31 GFLOP, bf16
 //   matrix cores) whose cost is writing 488 MB of fp32 scores;
 //   selection reads the scores once and writes the kept indices.
+// The pooling can instead be done by the QK kernel while it writes q', k'
+// (qk_rmsnorm_rope3d_pool_kernel, qk_rope.hip), which spares the read.
 #include "device_common.hpp"
 #include "launch.hpp"
 
