@@ -60,6 +60,7 @@ KERNEL_SOURCES = {
     "change": "residual_change.hip",
     "change_final": "residual_change.hip",
     "qk_pool": "qk_rope.hip",
+    "qk_pool_layout": "qk_rope.hip",
     "pool": "subblock.hip",
     "pool_hm": "subblock.hip",
     "scores": "subblock.hip",
@@ -67,7 +68,8 @@ KERNEL_SOURCES = {
     "copy": "copy.hip",
 }
 # Kernels of the next rows, measured after the chain (see main()).
-NEXT_OPS = ("residual_adaln", "qk_layout", "change", "change_final", "qk_pool", "pool", "pool_hm", "scores", "topk")
+NEXT_OPS = ("residual_adaln", "qk_layout", "qk_pool_layout", "change", "change_final", "qk_pool", "pool", "pool_hm",
+            "scores", "topk")
 ROUTE_SPARSITY = 0.75
 COUNTER_SUMMARY = os.path.join(ROOT, "profiles", "{op}_{workload}_counters.md")
 
@@ -92,6 +94,7 @@ def op_bytes(wl, next_rows: bool = False) -> dict:
             "qk_layout": out["qk"],                            # same bytes, strided in, head-major out
             "change": 2 * R * D * 2,                           # r, r_cached in (partials: 16 B per 2048 vectors)
             "qk_pool": out["qk"] + pooled,                     # QK's bytes plus the block means out
+            "qk_pool_layout": out["qk"] + pooled,              # the same from a fused QKV buffer, head-major out
             "pool": 2 * R * H * Dh * 2 + pooled,               # q', k' in, fp32 block means out
             "pool_hm": 2 * R * H * Dh * 2 + pooled,
             "scores": pooled + B * H * nb * nb * 4,            # means in, fp32 scores out
@@ -337,15 +340,38 @@ def main(argv=None) -> int:
         if i >= args.warmup:
             lev[i - args.warmup][1].record(stream)
     torch.cuda.synchronize()
-    del qkv
     layout_ms = sum(a.elapsed_time(b) for a, b in lev) / args.steps
+    # the same, also writing the SubBlock block means (one pass prepares attention and routing)
+    nb_r = -(-wl.N // 64)
+    qo_hm2, ko_hm2 = torch.empty_like(qo_hm), torch.empty_like(ko_hm)
+    qp_r = torch.empty((wl.B, wl.H, nb_r, wl.Dh), dtype=torch.float32, device=dev)
+    kp_r = torch.empty_like(qp_r)
+    pev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for i in range(args.warmup + args.steps):
+        if i >= args.warmup:
+            pev[i - args.warmup][0].record(stream)
+        dit.dit_qk_rmsnorm_rope3d_pool(qkv, None, ins["wq"], ins["wk"], pos, wl.bands, head_major=True,
+                                       heads=(wl.H, wl.Dh), q_out=qo_hm2, k_out=ko_hm2, q_pooled=qp_r, k_pooled=kp_r,
+                                       theta=wl.theta, eps=wl.eps, stream=stream)
+        if i >= args.warmup:
+            pev[i - args.warmup][1].record(stream)
+    torch.cuda.synchronize()
+    layout_pool_ms = sum(a.elapsed_time(b) for a, b in pev) / args.steps
+    layout_pool_same = bool(torch.equal(qo_hm2, qo_hm) and torch.equal(ko_hm2, ko_hm))
+    del qkv, qo_hm2, ko_hm2, qp_r, kp_r
+    layout_pool_bytes = nbytes["qk"] + 2 * wl.B * wl.H * nb_r * wl.Dh * 4
     layout = {"op": "dit_qk_rmsnorm_rope3d_layout (fused QKV in, head-major out)", "avg_ms": round(layout_ms, 5),
               "bytes": nbytes["qk"], "GB_s": round(nbytes["qk"] / (layout_ms * 1e-3) / 1e9, 1),
               "pct_of_peak": round(100.0 * nbytes["qk"] / (layout_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
               "token_major_ms": ops["qk"]["avg_ms"],
               "passes_avoided": "splitting q, k out of the QKV buffer and transposing q', k' to head-major: "
                                 "each a further read and write of q and k (2 x 4.1 GB here)",
-              "traffic": committed_traffic("qk_layout", wl.name)}
+              "traffic": committed_traffic("qk_layout", wl.name),
+              "with_block_means": {
+                  "op": "dit_qk_rmsnorm_rope3d_pool (same layouts, also the SubBlock block means)",
+                  "avg_ms": round(layout_pool_ms, 5), "bytes": layout_pool_bytes,
+                  "GB_s": round(layout_pool_bytes / (layout_pool_ms * 1e-3) / 1e9, 1),
+                  "pct_of_peak": round(100.0 * layout_pool_bytes / (layout_pool_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2)}}
 
     # Cache-DiT residual-change statistic over the packed sequence (the two
     # residual inputs stand in for the current and cached boundary residuals).
@@ -479,6 +505,7 @@ def main(argv=None) -> int:
     # ones transposed (the oracle check below covers the fused z).
     consistency = {
         "fused_x_out_equals_residual": bool(torch.equal(fused_x, out)),
+        "fused_pool_head_major_equals_layout_qk": layout_pool_same,
         "head_major_equals_token_major": bool(
             torch.equal(qo_hm.permute(0, 2, 1, 3), qo.view(wl.B, wl.N, wl.H, wl.Dh))
             and torch.equal(ko_hm.permute(0, 2, 1, 3), ko.view(wl.B, wl.N, wl.H, wl.Dh))),
@@ -676,6 +703,7 @@ KERNEL_OPS = (
     (r"adaln_modulate_kernel", "adaln"),
     (r"gated_residual_kernel", "residual"),
     (r"swiglu_kernel", "swiglu"),
+    (r"qk_rmsnorm_rope3d_pool_kernel<\d+, true>", "qk_pool_layout"),
     (r"qk_rmsnorm_rope3d_pool_kernel", "qk_pool"),
     (r"qk_rmsnorm_rope3d_kernel<\d+, true>", "qk_layout"),
     (r"qk_rmsnorm_rope3d_kernel", "qk"),

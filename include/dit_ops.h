@@ -302,18 +302,25 @@ dit_status dit_subblock_pool(const dit_bf16 *q, const dit_bf16 *k,
 
 /*
  * QK RMSNorm + 3D RoPE fused with the block means of its outputs: q_out, k_out
- * are exactly those of dit_qk_rmsnorm_rope3d, and q_pooled, k_pooled exactly
- * those dit_subblock_pool computes from the stored q_out, k_out
- * (DIT_QK_TOKEN_MAJOR), without reading them back from memory.
+ * are exactly those of dit_qk_rmsnorm_rope3d_layout with the same strides and
+ * layout, and q_pooled, k_pooled exactly those dit_subblock_pool computes from
+ * the stored q_out, k_out, without reading them back from memory.  With a
+ * fused QKV projection as input and head-major outputs this prepares q', k'
+ * for attention and the means for SubBlock routing in one pass.
  * Cited: xhh.club Q&A ("QK RMSNorm fused with 3D RoPE"); stamatios.com
  * summary, "De onde vêm os ganhos" (SubBlock 64-token blocks); Sol-H3
- * abstract (search over kernel fusions).  Reading: the routing pools q', k' as
- * stored in bf16.
- *   q, k, q_out, k_out   bf16 [B][N][H][Dh]; q_out == q and k_out == k allowed,
- *                        any other overlap DIT_ERR_ARG
- *   wq, wk, pos          as for dit_qk_rmsnorm_rope3d
- *   q_pooled, k_pooled   fp32 [B][H][ceil(N/64)][Dh], 16-byte aligned, overlapping
- *                        nothing else (DIT_ERR_ARG)
+ * abstract (search over kernel fusions and memory layouts).  Reading: the
+ * routing pools q', k' as stored in bf16.
+ *   q, k             bf16; token (b, n), head h at (b*N + n)*in_token_stride +
+ *                    h*Dh; in_token_stride a multiple of 8, >= H*Dh, at most
+ *                    2^24 (else DIT_ERR_SHAPE / DIT_ERR_ARG); may share a buffer
+ *   q_out, k_out     bf16 [B][N][H][Dh] (DIT_QK_TOKEN_MAJOR) or [B][H][N][Dh]
+ *                    (DIT_QK_HEAD_MAJOR; else DIT_ERR_ARG); q_out == q and
+ *                    k_out == k only when in_token_stride == H*Dh and the output
+ *                    is token-major; any other overlap DIT_ERR_ARG
+ *   wq, wk, pos      as for dit_qk_rmsnorm_rope3d
+ *   q_pooled, k_pooled  fp32 [B][H][ceil(N/64)][Dh], 16-byte aligned,
+ *                    overlapping nothing else (DIT_ERR_ARG)
  *   Dh in {16, 32, 64, 128, 256}, bands as for dit_qk_rmsnorm_rope3d, H*Dh <=
  *   65536 (else DIT_ERR_SHAPE); N <= 262,144 and B <= 65535 (else DIT_ERR_ARG).
  * B == 0 or N == 0 is a no-op.
@@ -323,7 +330,9 @@ dit_status dit_qk_rmsnorm_rope3d_pool(const dit_bf16 *q, const dit_bf16 *k,
                                       const dit_bf16 *wq, const dit_bf16 *wk,
                                       const int32_t *pos, float *q_pooled,
                                       float *k_pooled, int64_t B, int64_t N,
-                                      int64_t H, int64_t Dh, int32_t d_t,
+                                      int64_t H, int64_t Dh,
+                                      int64_t in_token_stride,
+                                      int32_t out_layout, int32_t d_t,
                                       int32_t d_h, int32_t d_w, float theta,
                                       float eps, void *stream);
 

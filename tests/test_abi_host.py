@@ -244,9 +244,10 @@ def test_subblock_pool_validation(lib):
 
 def test_qk_pool_validation(lib):
     # B=1, N=128, H=2, Dh=16 (bands 4/6/6): q, k 8 KiB each, pooled 2*2*16 floats
-    def f(q=P, k=Q, qo=R, ko=S, wq=T, wk=T + 64, pos=U, qp=V, kp=V + 4096, B=1, N=128, H=2, Dh=16, bands=(4, 6, 6),
-          theta=1e4, eps=1e-6):
-        return lib.dit_qk_rmsnorm_rope3d_pool(q, k, qo, ko, wq, wk, pos, qp, kp, B, N, H, Dh, *bands, theta, eps, None)
+    def f(q=P, k=Q, qo=R, ko=S, wq=T, wk=T + 64, pos=U, qp=V, kp=V + 4096, B=1, N=128, H=2, Dh=16, stride=32,
+          layout=0, bands=(4, 6, 6), theta=1e4, eps=1e-6):
+        return lib.dit_qk_rmsnorm_rope3d_pool(q, k, qo, ko, wq, wk, pos, qp, kp, B, N, H, Dh, stride, layout, *bands,
+                                              theta, eps, None)
 
     assert f(B=-1, qp=0) == DIT_ERR_ARG
     assert f(N=4096 * 64 + 1, qp=0) == DIT_ERR_ARG
@@ -260,6 +261,11 @@ def test_qk_pool_validation(lib):
     assert f(kp=R) == DIT_ERR_ARG  # pooled k over q_out
     assert f(qo=P + 16) == DIT_ERR_ARG  # q_out partly over q
     assert f(ko=P) == DIT_ERR_ARG  # k_out over q
+    assert f(stride=24, qp=0) == DIT_ERR_SHAPE  # stride below H*Dh
+    assert f(stride=36, qp=0) == DIT_ERR_SHAPE  # stride not a multiple of 8
+    assert f(layout=2, qp=0) == DIT_ERR_ARG
+    assert f(layout=1, qo=P) == DIT_ERR_ARG  # head-major output over its own input is not in place
+    assert f(stride=96, qo=P + 64 * 200, k=P + 64) == DIT_ERR_ARG  # inside the strided input's extent
     assert f(q=0, k=0, qo=0, ko=0, wq=0, wk=0, pos=0, qp=0, kp=0, N=0) == DIT_OK
 
 

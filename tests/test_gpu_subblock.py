@@ -327,3 +327,22 @@ def test_qk_pool_full_workload_equals_parts(name):
     qpr, kpr = dit.dit_subblock_pool(qr, kr)
     torch.cuda.synchronize()
     assert torch.equal(qp, qpr) and torch.equal(kp, kpr)
+
+
+@pytest.mark.parametrize("head_major", [False, True], ids=["token_major", "head_major"])
+@pytest.mark.parametrize("shape", [QK_POOL_SHAPES[0], QK_POOL_SHAPES[1], QK_POOL_SHAPES[2], QK_POOL_SHAPES[5]],
+                         ids=lambda s: "x".join(map(str, s[:4])))
+def test_qk_pool_from_fused_projection(shape, head_major):
+    # q and k read out of a fused [B, N, 3*H*Dh] projection, q', k' in either layout: the same
+    # outputs as the layout QK kernel and the same means as the contiguous token-major call
+    B, N, H, Dh, bands = shape
+    q, k, wq, wk, pos = qk_pool_inputs(B, N, H, Dh, seed=7 + N)
+    HD = H * Dh
+    qkv = torch.cat([q.reshape(B, N, HD), k.reshape(B, N, HD), torch.full((B, N, HD), float("nan"), device=DEV,
+                                                                          dtype=torch.bfloat16)], dim=-1).contiguous()
+    qo, ko, qp, kp = dit.dit_qk_rmsnorm_rope3d_pool(qkv, None, wq, wk, pos, bands, head_major=head_major, heads=(H, Dh))
+    ql, kl = dit.dit_qk_rmsnorm_rope3d_layout(qkv, H, Dh, wq, wk, pos, bands, head_major=head_major)
+    _, _, qp_ref, kp_ref = dit.dit_qk_rmsnorm_rope3d_pool(q, k, wq, wk, pos, bands)
+    torch.cuda.synchronize()
+    assert torch.equal(qo, ql) and torch.equal(ko, kl)
+    assert torch.equal(qp, qp_ref) and torch.equal(kp, kp_ref)

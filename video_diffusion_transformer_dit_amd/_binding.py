@@ -37,8 +37,8 @@ SIGNATURES = {
     "dit_subblock_scores_ld": ([_I64], ctypes.c_int64),
     "dit_subblock_pool": ([_P, _P, _P, _P, _I64, _I64, _I64, _I64, _I32, _P], ctypes.c_int),
     "dit_subblock_route": ([_P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _P], ctypes.c_int),
-    "dit_qk_rmsnorm_rope3d_pool": ([_P, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I32, _I32, _I32,
-                                    _F32, _F32, _P], ctypes.c_int),
+    "dit_qk_rmsnorm_rope3d_pool": ([_P, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I32, _I32,
+                                    _I32, _I32, _F32, _F32, _P], ctypes.c_int),
     "dit_packed_positions": ([_P, _I64, _I64, _I64, _I64, _P], ctypes.c_int),
     "dit_copy16": ([_P, _P, _I64, _P], ctypes.c_int),
 }
@@ -312,22 +312,38 @@ def dit_subblock_pool(q, k, head_major: bool = False, q_pooled=None, k_pooled=No
     return q_pooled, k_pooled
 
 
-def dit_qk_rmsnorm_rope3d_pool(q, k, wq, wk, pos, bands, q_out=None, k_out=None, q_pooled=None, k_pooled=None,
-                               theta: float = 1e4, eps: float = 1e-6, stream=None):
-    """dit_qk_rmsnorm_rope3d plus the 64-token block means of its stored outputs.
+def dit_qk_rmsnorm_rope3d_pool(q, k, wq, wk, pos, bands, head_major: bool = False, q_out=None, k_out=None,
+                               q_pooled=None, k_pooled=None, heads=None, theta: float = 1e4, eps: float = 1e-6,
+                               stream=None):
+    """QK RMSNorm + 3D RoPE plus the 64-token block means of its stored outputs.
 
-    q, k [B,N,H,Dh] bf16 -> (q_out, k_out [B,N,H,Dh] bf16, q_pooled, k_pooled [B,H,nb,Dh] fp32).
+    Inputs: q, k bf16 [B,N,H,Dh]; or, with ``k=None`` and ``heads=(H, Dh)``, q is a fused projection
+    [B,N,S] holding q at [0, H*Dh) and k at [H*Dh, 2*H*Dh) of each token.  Outputs q', k' are
+    [B,N,H,Dh], or [B,H,N,Dh] with ``head_major=True``; the means are fp32 [B,H,nb,Dh], nb = ceil(N/64).
+    Returns (q_out, k_out, q_pooled, k_pooled).
     """
-    _tensor(q, "q", ndim=4)
-    B, N, H, Dh = q.shape
-    _shape(_tensor(k, "k"), "k", (B, N, H, Dh))
+    if k is None:
+        _tensor(q, "qkv", ndim=3)
+        if heads is None:
+            raise ValueError("a fused projection needs heads=(H, Dh)")
+        B, N, S = q.shape
+        H, Dh = (int(v) for v in heads)
+        if S < 2 * H * Dh:
+            raise ValueError(f"the projection's last dimension {S} cannot hold q and k of {H}x{Dh}")
+        stride, q_ptr, k_ptr, src = S, q.data_ptr(), q.data_ptr() + H * Dh * q.element_size(), (q,)
+    else:
+        _tensor(q, "q", ndim=4)
+        B, N, H, Dh = q.shape
+        _shape(_tensor(k, "k"), "k", (B, N, H, Dh))
+        stride, q_ptr, k_ptr, src = H * Dh, q.data_ptr(), k.data_ptr(), (q, k)
     _shape(_tensor(wq, "wq"), "wq", (Dh,))
     _shape(_tensor(wk, "wk"), "wk", (Dh,))
     _shape(_tensor(pos, "pos", dtype=torch.int32), "pos", (N, 3))
-    q_out = torch.empty_like(q) if q_out is None else q_out
-    k_out = torch.empty_like(k) if k_out is None else k_out
-    _shape(_tensor(q_out, "q_out"), "q_out", (B, N, H, Dh))
-    _shape(_tensor(k_out, "k_out"), "k_out", (B, N, H, Dh))
+    shape = (B, H, N, Dh) if head_major else (B, N, H, Dh)
+    q_out = torch.empty(shape, dtype=torch.bfloat16, device=q.device) if q_out is None else q_out
+    k_out = torch.empty(shape, dtype=torch.bfloat16, device=q.device) if k_out is None else k_out
+    _shape(_tensor(q_out, "q_out"), "q_out", shape)
+    _shape(_tensor(k_out, "k_out"), "k_out", shape)
     nb = -(-N // DIT_SUBBLOCK_TOKENS)
     pshape = (B, H, nb, Dh)
     q_pooled = torch.empty(pshape, dtype=torch.float32, device=q.device) if q_pooled is None else q_pooled
@@ -335,12 +351,13 @@ def dit_qk_rmsnorm_rope3d_pool(q, k, wq, wk, pos, bands, q_out=None, k_out=None,
     _shape(_tensor(q_pooled, "q_pooled", dtype=torch.float32), "q_pooled", pshape)
     _shape(_tensor(k_pooled, "k_pooled", dtype=torch.float32), "k_pooled", pshape)
     d_t, d_h, d_w = (int(b) for b in bands)
-    dev = _same_device(q, k, wq, wk, pos, q_out, k_out, q_pooled, k_pooled)
+    dev = _same_device(*src, wq, wk, pos, q_out, k_out, q_pooled, k_pooled)
     with torch.cuda.device(dev):
         _check("dit_qk_rmsnorm_rope3d_pool", load_library().dit_qk_rmsnorm_rope3d_pool(
-            q.data_ptr(), k.data_ptr(), q_out.data_ptr(), k_out.data_ptr(), wq.data_ptr(), wk.data_ptr(),
-            pos.data_ptr(), q_pooled.data_ptr(), k_pooled.data_ptr(), B, N, H, Dh, d_t, d_h, d_w, float(theta),
-            float(eps), _stream(stream, dev)))
+            q_ptr, k_ptr, q_out.data_ptr(), k_out.data_ptr(), wq.data_ptr(), wk.data_ptr(), pos.data_ptr(),
+            q_pooled.data_ptr(), k_pooled.data_ptr(), B, N, H, Dh, stride,
+            DIT_QK_HEAD_MAJOR if head_major else DIT_QK_TOKEN_MAJOR, d_t, d_h, d_w, float(theta), float(eps),
+            _stream(stream, dev)))
     return q_out, k_out, q_pooled, k_pooled
 
 

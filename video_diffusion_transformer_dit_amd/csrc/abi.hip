@@ -315,13 +315,17 @@ dit_status dit_subblock_pool(const dit_bf16 *q, const dit_bf16 *k, float *q_pool
 
 dit_status dit_qk_rmsnorm_rope3d_pool(const dit_bf16 *q, const dit_bf16 *k, dit_bf16 *q_out, dit_bf16 *k_out,
                                       const dit_bf16 *wq, const dit_bf16 *wk, const int32_t *pos, float *q_pooled,
-                                      float *k_pooled, int64_t B, int64_t N, int64_t H, int64_t Dh, int32_t d_t,
-                                      int32_t d_h, int32_t d_w, float theta, float eps, void *stream)
+                                      float *k_pooled, int64_t B, int64_t N, int64_t H, int64_t Dh,
+                                      int64_t in_token_stride, int32_t out_layout, int32_t d_t, int32_t d_h,
+                                      int32_t d_w, float theta, float eps, void *stream)
 {
-    if (B < 0 || N < 0 || H < 0 || Dh < 0 || B > kMaxSamples || N > kMaxSubBlocks * DIT_SUBBLOCK_TOKENS)
+    if (B < 0 || N < 0 || H < 0 || Dh < 0 || B > kMaxSamples || N > kMaxSubBlocks * DIT_SUBBLOCK_TOKENS ||
+        in_token_stride < 0 || in_token_stride > kMaxWidth)
+        return DIT_ERR_ARG;
+    if (out_layout != DIT_QK_TOKEN_MAJOR && out_layout != DIT_QK_HEAD_MAJOR)
         return DIT_ERR_ARG;
     if (!subblock_head_ok(H, Dh) || d_t < 0 || d_h < 0 || d_w < 0 || (d_t | d_h | d_w) & 1 ||
-        (int64_t)d_t + d_h + d_w != Dh)
+        (int64_t)d_t + d_h + d_w != Dh || in_token_stride % 8 != 0 || in_token_stride < H * Dh)
         return DIT_ERR_SHAPE;
     if (!(eps > 0.f) || !isfinite(eps) || !(theta > 1.f) || !isfinite(theta))
         return DIT_ERR_ARG;
@@ -332,30 +336,33 @@ dit_status dit_qk_rmsnorm_rope3d_pool(const dit_bf16 *q, const dit_bf16 *k, dit_
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(q_out, 16) || !aligned(k_out, 16) || !aligned(wq, 16) ||
         !aligned(wk, 16) || !aligned(pos, 4) || !aligned(q_pooled, 16) || !aligned(k_pooled, 16))
         return DIT_ERR_ALIGN;
+    const int64_t rows = B * N;
     const int64_t nb = (N + DIT_SUBBLOCK_TOKENS - 1) / DIT_SUBBLOCK_TOKENS;
-    const int64_t nt = B * N * H * Dh * 2, npool = B * H * nb * Dh * 4, nw = Dh * 2, np = N * 12;
-    // q' may overwrite q and k' k exactly (each vector is read before it is written); nothing else overlaps.
-    if (bad_alias(q_out, q, nt) || bad_alias(k_out, k, nt) || overlap(q_out, nt, k, nt) || overlap(k_out, nt, q, nt) ||
-        overlap(k_out, nt, q_out, nt))
+    const int64_t nt = rows * H * Dh * 2;                          // bytes of each output
+    const int64_t ni = ((rows - 1) * in_token_stride + H * Dh) * 2; // byte extent of each input
+    const int64_t npool = B * H * nb * Dh * 4, nw = Dh * 2, np = N * 12;
+    // q' may overwrite q and k' k exactly, where the two layouts coincide; the
+    // inputs may share a buffer (fused QKV); nothing else overlaps.
+    const bool same_layout = in_token_stride == H * Dh && out_layout == DIT_QK_TOKEN_MAJOR;
+    const bool q_bad = same_layout ? bad_alias(q_out, q, nt) : overlap(q_out, nt, q, ni);
+    const bool k_bad = same_layout ? bad_alias(k_out, k, nt) : overlap(k_out, nt, k, ni);
+    if (q_bad || k_bad || overlap(q_out, nt, k, ni) || overlap(k_out, nt, q, ni) || overlap(k_out, nt, q_out, nt))
         return DIT_ERR_ARG;
     const void *rd[5] = {q, k, wq, wk, pos};
-    const int64_t rd_n[5] = {nt, nt, nw, nw, np};
+    const int64_t rd_n[5] = {ni, ni, nw, nw, np};
     const void *wr[4] = {q_out, k_out, q_pooled, k_pooled};
     const int64_t wr_n[4] = {nt, nt, npool, npool};
-    for (int i = 2; i < 4; ++i) {
-        for (int j = 0; j < 5; ++j)
+    for (int i = 0; i < 4; ++i) {
+        for (int j = i < 2 ? 2 : 0; j < 5; ++j) // q_out, k_out against q, k are checked above
             if (overlap(wr[i], wr_n[i], rd[j], rd_n[j]))
                 return DIT_ERR_ARG;
-        for (int j = 0; j < 4; ++j)
+        for (int j = 2; j < 4; ++j)
             if (j != i && overlap(wr[i], wr_n[i], wr[j], wr_n[j]))
                 return DIT_ERR_ARG;
     }
-    for (int i = 0; i < 2; ++i)
-        for (int j = 2; j < 5; ++j)
-            if (overlap(wr[i], wr_n[i], rd[j], rd_n[j]))
-                return DIT_ERR_ARG;
     return launched(dit::launch_qk_rmsnorm_rope3d_pool(q, k, q_out, k_out, wq, wk, pos, q_pooled, k_pooled, B, N, H,
-                                                       Dh, d_t, d_h, d_w, theta, eps, (hipStream_t)stream));
+                                                       Dh, in_token_stride, out_layout == DIT_QK_HEAD_MAJOR, d_t, d_h,
+                                                       d_w, theta, eps, (hipStream_t)stream));
 }
 
 dit_status dit_subblock_route(const float *q_pooled, const float *k_pooled, float *scores, int32_t *kept, int64_t B,

@@ -41,12 +41,14 @@ int64_t residual_change_tiles(int64_t N, int64_t D);
 hipError_t launch_residual_change(const void *r, const void *r_cached, double *out, void *workspace, int64_t B,
                                   int64_t N, int64_t D, hipStream_t stream);
 
-// QK RMSNorm + 3D RoPE (token-major in and out) and the means of each 64-token block of the stored
-// q', k': [B][H][ceil(N/64)][Dh] fp32.  Dh in {16,...,256}, power of two.
+// QK RMSNorm + 3D RoPE and the means of each 64-token block of the stored q', k':
+// [B][H][ceil(N/64)][Dh] fp32.  Inputs with in_token_stride elements between tokens; outputs
+// [B][N][H][Dh] or [B][H][N][Dh] (head_major).  Dh in {16,...,256}, power of two.
 hipError_t launch_qk_rmsnorm_rope3d_pool(const void *q, const void *k, void *q_out, void *k_out, const void *wq,
                                          const void *wk, const int32_t *pos, float *q_pooled, float *k_pooled,
-                                         int64_t B, int64_t N, int64_t H, int64_t Dh, int d_t, int d_h, int d_w,
-                                         float theta, float eps, hipStream_t stream);
+                                         int64_t B, int64_t N, int64_t H, int64_t Dh, int64_t in_token_stride,
+                                         bool head_major, int d_t, int d_h, int d_w, float theta, float eps,
+                                         hipStream_t stream);
 
 // Means of each 64-token block of q and of k, per sample and head: [B][H][ceil(N/64)][Dh] fp32.
 // Inputs [B][N][H][Dh] (token-major) or [B][H][N][Dh] (head_major); Dh in {16,...,256}, power of two.

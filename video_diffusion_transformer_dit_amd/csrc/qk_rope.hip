@@ -163,8 +163,8 @@ RotaryPlan make_rotary_plan(int64_t Dh, int d_t, int d_h, int d_w, float theta)
     return plan;
 }
 
-// QK RMSNorm + RoPE fused with the SubBlock block means of its outputs
-// (token-major in and out).  grid (chunks * nb, 2 (q then k), B), 512
+// QK RMSNorm + RoPE fused with the SubBlock block means of its outputs.
+// grid (chunks * nb, 2 (q then k), B), 512
 // threads.  A workgroup covers one 64-token block and one chunk of 64 vector
 // columns (64 * 8 / Dh heads): wave w handles tokens w, w+8, ..., w+56 of the
 // block, each across its 64 columns just as the QK kernel handles a token (a
@@ -179,11 +179,15 @@ RotaryPlan make_rotary_plan(int64_t Dh, int d_t, int d_h, int d_w, float theta)
 constexpr int kQKPoolWaves = 8;
 constexpr int kQKPoolTokens = 64; // SubBlock block size
 
-template <int LPH>
+// in_stride = vectors from one token's q (or k) to the next token's (C for
+// contiguous inputs, more for q and k inside a fused QKV projection).
+// HEAD_MAJOR: q', k' written [B][H][N][Dh]; the workgroup's 64 tokens of a head
+// are then 64 * Dh contiguous values of its plane.
+template <int LPH, bool HEAD_MAJOR>
 __global__ __launch_bounds__(kQKPoolWaves * kWave) void qk_rmsnorm_rope3d_pool_kernel(
     const u32x4 *q, const u32x4 *k, u32x4 *q_out, u32x4 *k_out, const u32x4 *__restrict__ wq,
     const u32x4 *__restrict__ wk, const int32_t *__restrict__ pos, float *__restrict__ qp, float *__restrict__ kp,
-    int N, int nb, int C, int chunks, float inv_dh, float eps, const RotaryPlan plan)
+    int N, int nb, int C, int64_t in_stride, int chunks, float inv_dh, float eps, const RotaryPlan plan)
 {
     constexpr int kPerWave = kQKPoolTokens / kQKPoolWaves;
     constexpr int kPairs = 4 * LPH;                       // channel pairs per head
@@ -213,11 +217,15 @@ __global__ __launch_bounds__(kQKPoolWaves * kWave) void qk_rmsnorm_rope3d_pool_k
     }
 
     const size_t row0 = (size_t)b * N + n0;
+    const int H = C / LPH, h = c / LPH;
+    // output vector of token n0 + n: token-major row, or the head's plane
+    const size_t out0 = HEAD_MAJOR ? (((size_t)b * H + h) * N + n0) * LPH + slot : row0 * C + c;
+    const size_t out_step = HEAD_MAJOR ? LPH : C;
     u32x4 raw[kPerWave];
 #pragma unroll
     for (int t = 0; t < kPerWave; ++t) {
         const int n = wave + kQKPoolWaves * t; // wave-uniform
-        raw[t] = (valid && n < count) ? load_stream(src + (row0 + n) * C + c) : u32x4{0u, 0u, 0u, 0u};
+        raw[t] = (valid && n < count) ? load_stream(src + (row0 + n) * in_stride + c) : u32x4{0u, 0u, 0u, 0u};
     }
 
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
@@ -252,7 +260,7 @@ __global__ __launch_bounds__(kQKPoolWaves * kWave) void qk_rmsnorm_rope3d_pool_k
             }
             const u32x4 o = norm_rotate<LPH>(raw[t], w, cs, sn, inv_dh, eps);
             if (valid)
-                store_stream(dst + (row0 + n) * C + c, o);
+                store_stream(dst + out0 + (size_t)n * out_step, o);
             float f[8];
             unpack8(o, f);
 #pragma unroll
@@ -276,7 +284,7 @@ __global__ __launch_bounds__(kQKPoolWaves * kWave) void qk_rmsnorm_rope3d_pool_k
             acc[0] += lo.x, acc[1] += lo.y, acc[2] += lo.z, acc[3] += lo.w;
             acc[4] += hi.x, acc[5] += hi.y, acc[6] += hi.z, acc[7] += hi.w;
         }
-        const int H = C / LPH, h = c / LPH, Dh = 8 * LPH;
+        const int Dh = 8 * LPH;
         float *o = (which ? kp : qp) + (((size_t)b * H + h) * nb + blk) * Dh + slot * 8;
         float4 *o4 = reinterpret_cast<float4 *>(o);
         const float cnt = (float)count;
@@ -287,14 +295,18 @@ __global__ __launch_bounds__(kQKPoolWaves * kWave) void qk_rmsnorm_rope3d_pool_k
 
 template <int LPH>
 hipError_t launch_pool_lph(const u32x4 *q, const u32x4 *k, u32x4 *qo, u32x4 *ko, const u32x4 *wq, const u32x4 *wk,
-                           const int32_t *pos, float *qp, float *kp, int B, int N, int C, float inv_dh, float eps,
-                           const RotaryPlan &plan, hipStream_t stream)
+                           const int32_t *pos, float *qp, float *kp, int B, int N, int C, int64_t in_stride,
+                           bool head_major, float inv_dh, float eps, const RotaryPlan &plan, hipStream_t stream)
 {
     const int nb = (N + kQKPoolTokens - 1) / kQKPoolTokens;
     const int chunks = (C + kWave - 1) / kWave;
-    hipLaunchKernelGGL((qk_rmsnorm_rope3d_pool_kernel<LPH>), dim3((unsigned)(chunks * nb), 2u, (unsigned)B),
-                       dim3(kQKPoolWaves * kWave), 0, stream, q, k, qo, ko, wq, wk, pos, qp, kp, N, nb, C, chunks,
-                       inv_dh, eps, plan);
+    const dim3 grid((unsigned)(chunks * nb), 2u, (unsigned)B), block(kQKPoolWaves * kWave);
+    if (head_major)
+        hipLaunchKernelGGL((qk_rmsnorm_rope3d_pool_kernel<LPH, true>), grid, block, 0, stream, q, k, qo, ko, wq, wk,
+                           pos, qp, kp, N, nb, C, in_stride, chunks, inv_dh, eps, plan);
+    else
+        hipLaunchKernelGGL((qk_rmsnorm_rope3d_pool_kernel<LPH, false>), grid, block, 0, stream, q, k, qo, ko, wq, wk,
+                           pos, qp, kp, N, nb, C, in_stride, chunks, inv_dh, eps, plan);
     return hipGetLastError();
 }
 
@@ -348,8 +360,9 @@ hipError_t launch_qk_rmsnorm_rope3d(const void *q, const void *k, void *q_out, v
 
 hipError_t launch_qk_rmsnorm_rope3d_pool(const void *q, const void *k, void *q_out, void *k_out, const void *wq,
                                          const void *wk, const int32_t *pos, float *q_pooled, float *k_pooled,
-                                         int64_t B, int64_t N, int64_t H, int64_t Dh, int d_t, int d_h, int d_w,
-                                         float theta, float eps, hipStream_t stream)
+                                         int64_t B, int64_t N, int64_t H, int64_t Dh, int64_t in_token_stride,
+                                         bool head_major, int d_t, int d_h, int d_w, float theta, float eps,
+                                         hipStream_t stream)
 {
     const auto *qv = static_cast<const u32x4 *>(q);
     const auto *kv = static_cast<const u32x4 *>(k);
@@ -361,7 +374,10 @@ hipError_t launch_qk_rmsnorm_rope3d_pool(const void *q, const void *k, void *q_o
     const float inv_dh = 1.f / (float)Dh;
     const RotaryPlan plan = make_rotary_plan(Dh, d_t, d_h, d_w, theta);
     const int b = (int)B, n = (int)N;
-#define DIT_QK_POOL_LAUNCH(L) launch_pool_lph<L>(qv, kv, qo, ko, wqv, wkv, pos, q_pooled, k_pooled, b, n, C, inv_dh, eps, plan, stream)
+    const int64_t in_stride = in_token_stride / 8;
+#define DIT_QK_POOL_LAUNCH(L)                                                                                        \
+    launch_pool_lph<L>(qv, kv, qo, ko, wqv, wkv, pos, q_pooled, k_pooled, b, n, C, in_stride, head_major, inv_dh, eps, \
+                       plan, stream)
     switch (Dh) {
     case 16: return DIT_QK_POOL_LAUNCH(2);
     case 32: return DIT_QK_POOL_LAUNCH(4);
