@@ -346,3 +346,37 @@ def test_qk_pool_from_fused_projection(shape, head_major):
     torch.cuda.synchronize()
     assert torch.equal(qo, ql) and torch.equal(ko, kl)
     assert torch.equal(qp, qp_ref) and torch.equal(kp, kp_ref)
+
+
+def test_every_entry_point_accepts_empty_inputs():
+    # zero tokens (or zero samples) is a no-op for every entry point, through the binding
+    bf = dict(dtype=torch.bfloat16, device=DEV)
+    D, H, Dh, bands = 256, 4, 64, (16, 24, 24)
+    x = torch.empty((1, 0, D), **bf)
+    v = torch.zeros((1, D), **bf)
+    w = torch.ones((Dh,), **bf)
+    pos = torch.empty((0, 3), dtype=torch.int32, device=DEV)
+    q = torch.empty((1, 0, H, Dh), **bf)
+    assert dit.dit_adaln_modulate(x, v, v).shape == (1, 0, D)
+    assert dit.dit_gated_residual(x, x, v).shape == (1, 0, D)
+    xo, z = dit.dit_gated_residual_adaln(x, x, v, v, v)
+    assert xo.shape == z.shape == (1, 0, D)
+    assert dit.dit_swiglu(torch.empty((0, 2 * D), **bf)).shape == (0, D)
+    qo, ko = dit.dit_qk_rmsnorm_rope3d(q, q, w, w, pos, bands)
+    assert qo.shape == (1, 0, H, Dh)
+    ql, kl = dit.dit_qk_rmsnorm_rope3d_layout(torch.empty((1, 0, 3 * H * Dh), **bf), H, Dh, w, w, pos, bands)
+    assert ql.shape == (1, H, 0, Dh)
+    assert dit.dit_packed_positions(0, 4, 4, 0, device=DEV).shape == (0, 3)
+    qp, kp = dit.dit_subblock_pool(q, q)
+    assert qp.shape == (1, H, 0, Dh)
+    kept, scores = dit.dit_subblock_route(qp, kp, sparsity=0.75)
+    assert kept.shape == (1, H, 0, 0)
+    outs = dit.dit_qk_rmsnorm_rope3d_pool(q, q, w, w, pos, bands)
+    assert outs[2].shape == (1, H, 0, Dh)
+    change = dit.dit_residual_change(x, x)
+    dit.dit_copy16(torch.empty(0, dtype=torch.uint8, device=DEV), torch.empty(0, dtype=torch.uint8, device=DEV))
+    # zero samples
+    qp0, kp0 = dit.dit_subblock_pool(torch.empty((0, 100, H, Dh), **bf), torch.empty((0, 100, H, Dh), **bf))
+    assert qp0.shape == (0, H, 2, Dh)
+    torch.cuda.synchronize()
+    assert torch.all(change == 0)
