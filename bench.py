@@ -547,6 +547,8 @@ def main(argv=None) -> int:
         "block_mix_fused": block_mix_fused,
         "next_consistency": consistency,
         "one_gpu_share_of_8": share,
+        "env": {"torch": torch.__version__, "hip": getattr(torch.version, "hip", None),
+                "device": torch.cuda.get_device_name(dev)},
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, ins, {"y": y, "out": out, "sw": sw, "qo": qo, "ko": ko,
