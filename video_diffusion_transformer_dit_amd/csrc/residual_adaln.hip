@@ -13,11 +13,11 @@
 // values actually stored in x_out, so the result equals the unfused pipeline.
 //
 // Mapping (gfx950) as in adaln.hip: one wave per row, four rows per
-// workgroup, the row held in registers (here the stored residual), row
-// statistics from per-lane (count, mean, M2) partials combined across the
-// wave with the parallel-variance identity, and the per-sample vectors (gate,
-// 1 + scale, shift) staged once per workgroup in LDS as fp32 for rows up to
-// 4096 wide (48 KiB).
+// workgroup, the row's loads issued first, the row held in registers (here
+// the stored residual), row statistics from per-lane (count, mean, M2)
+// partials combined across the wave with the parallel-variance identity, and
+// the per-sample vectors (gate, 1 + scale, shift) staged once per workgroup
+// in LDS as fp32 for rows up to 4096 wide (48 KiB).
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -47,6 +47,22 @@ __global__ __launch_bounds__(256) void gated_residual_adaln_kernel(
     const int row0 = blockIdx.x * kRowsPerBlock;
     const int row = row0 + (threadIdx.x / kWave);
     const int b0 = row0 / N;
+    // The row's loads go out before the staging below: they do not depend on
+    // it, so the HBM latency of x and y overlaps the cached reads of the
+    // modulation vectors and the barrier (measured 3% faster at 4096 wide).
+    // A wave past the last row loads nothing and leaves after the barrier.
+    const size_t base = (size_t)row * C;
+    u32x4 xr[VPL], yr[VPL];
+#pragma unroll
+    for (int k = 0; k < VPL; ++k) {
+        const int c = lane + kWave * k;
+        xr[k] = yr[k] = u32x4{0u, 0u, 0u, 0u};
+        if (row < rows && (FULL || c < C)) {
+            xr[k] = load_stream(x + base + c);
+            yr[k] = load_stream(y + base + c);
+        }
+    }
+
     if constexpr (STAGE) {
         for (int c = threadIdx.x; c < C; c += blockDim.x) {
             float g[8], s[8], t[8];
@@ -66,21 +82,9 @@ __global__ __launch_bounds__(256) void gated_residual_adaln_kernel(
     if (row >= rows) // wave-uniform
         return;
 
-    const size_t base = (size_t)row * C;
     const int b = row / N;
     const bool staged = STAGE && b == b0; // wave-uniform
     const u32x4 *gv = gate + (size_t)b * C;
-
-    u32x4 xr[VPL], yr[VPL];
-#pragma unroll
-    for (int k = 0; k < VPL; ++k) {
-        const int c = lane + kWave * k;
-        xr[k] = yr[k] = u32x4{0u, 0u, 0u, 0u};
-        if (FULL || c < C) {
-            xr[k] = load_stream(x + base + c);
-            yr[k] = load_stream(y + base + c);
-        }
-    }
 
     // Residual update: round once to bf16, store, and keep the stored values.
     float v[VPL][8];
