@@ -707,7 +707,7 @@ KERNEL_OPS = (
     (r"swiglu_kernel", "swiglu"),
     (r"qk_rmsnorm_rope3d_pool_kernel<\d+, true>", "qk_pool_layout"),
     (r"qk_rmsnorm_rope3d_pool_kernel", "qk_pool"),
-    (r"qk_rmsnorm_rope3d_kernel<\d+, true>", "qk_layout"),
+    (r"qk_rmsnorm_rope3d_head_major_kernel", "qk_layout"),
     (r"qk_rmsnorm_rope3d_kernel", "qk"),
     (r"residual_change_partial_kernel", "change"),
     (r"residual_change_final_kernel", "change_final"),
