@@ -577,6 +577,14 @@ def test_full_workload_sampled(name):
                                                  pos_ref[n:n + 1], wl.bands, 1, 1, wl.H, wl.Dh, S, 1, wl.theta, wl.eps)
         assert_close(qo[b, :, n], qr[0, :, 0], f"{name} q head-major row {r}")
         assert_close(ko[b, :, n], kr[0, :, 0], f"{name} k head-major row {r}")
+    # Every element: the head-major outputs are the token-major ones of the
+    # same buffer, transposed (same arithmetic per element, another layout).
+    qt, kt = dit.dit_qk_rmsnorm_rope3d_layout(qkv, wl.H, wl.Dh, ins["wq"], ins["wk"], pos, wl.bands,
+                                              head_major=False, theta=wl.theta, eps=wl.eps)
+    sync()
+    assert torch.equal(qo.permute(0, 2, 1, 3), qt), f"{name} head-major q differs from token-major q transposed"
+    assert torch.equal(ko.permute(0, 2, 1, 3), kt), f"{name} head-major k differs from token-major k transposed"
+    del qt, kt
     del ins, qo, ko, qkv, qkv_rows
     torch.cuda.empty_cache()
     # Rows of a sample are the same computation for every sample: the same
