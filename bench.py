@@ -784,6 +784,7 @@ KERNEL_OPS = (
     (r"residual_change_final_kernel", "change_final"),
     (r"subblock_pool_token_major_kernel", "pool"),
     (r"subblock_pool_head_major_kernel", "pool_hm"),
+    (r"subblock_scores_persistent_kernel", "scores"),
     (r"subblock_scores_kernel", "scores"),
     (r"subblock_topk_kernel", "topk"),
     (r"packed_positions_kernel", "positions"),

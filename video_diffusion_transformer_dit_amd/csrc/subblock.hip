@@ -166,8 +166,9 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // grid (tiles * tiles, H, B), 4 * TILE threads; tiles = ceil(nb / TILE), the
 // (head, tile) pairs renumbered per XCD (below).  A workgroup computes a
-// TILE x TILE tile of one head's score matrix (TILE = 128 for Dh <= 128, 64
-// for Dh = 256, where two 128-row operand tiles would fill most of the LDS):
+// TILE x TILE tile of one head's score matrix.  The route runs it for
+// Dh = 256 with TILE = 64 (two 128-row operand tiles would fill most of the
+// LDS); smaller heads take the persistent form below, whose tiles are 128:
 // both TILE-row operand tiles are rounded to bf16 into LDS (rows padded by 4
 // values so the 16 rows one MFMA reads fall in different banks).  The waves
 // form a 4 x (TILE/64) grid; each multiplies TILE/64 strips of 16 query rows
@@ -271,6 +272,126 @@ __global__ __launch_bounds__(4 * TILE) void subblock_scores_kernel(const float *
         if (row < q_rows && 4 * c4 < k_rows) // columns up to nb rounded up to 4, all inside ld
             __builtin_nontemporal_store(*reinterpret_cast<const f32x4 *>(&lds_s[row * kOutRow + 4 * c4]),
                                         reinterpret_cast<f32x4 *>(out + (size_t)row * ld + 4 * c4));
+    }
+}
+
+// Persistent form of the 128 x 128 tile for Dh <= 128 (what the route runs):
+// one 512-thread workgroup per resident slot, each walking a run of tiles.
+// The XCD of workgroup w (w % 8, dispatch is round-robin) takes the (w % 8)-th
+// contiguous eighth of the (head, tile) list, and its workgroups interleave
+// over that range, so each XCD's L2 again holds one head's means at a time.
+// After a tile's operands are staged in LDS, the next tile's fp32 operands
+// are loaded into registers; those loads are in flight while the current
+// tile is multiplied, staged out through LDS and stored, which overlaps the
+// score stores with the next tile's loads (the short-lived workgroups of
+// subblock_scores_kernel store only at their end).  The arithmetic per tile
+// is that kernel's, so the scores are the same bit for bit; measured 15%
+// faster at 1953 blocks (115-121 against 135-138 us).  The registers holding
+// the prefetch leave room for one workgroup per CU at Dh = 128.
+template <int DH>
+__global__ __launch_bounds__(512) void subblock_scores_persistent_kernel(const float *__restrict__ qp,
+                                                                         const float *__restrict__ kp,
+                                                                         float *__restrict__ scores, int nb, int ld,
+                                                                         int tiles, unsigned total)
+{
+    constexpr int TILE = 128, kThreads = 512, kStrips = 2;
+    constexpr int kRow = DH + 4; // bf16 per padded LDS row
+    constexpr int kF4PerRow = DH / 4;
+    constexpr int kLoads = TILE * kF4PerRow / kThreads; // float4 per thread and operand
+    constexpr int kOutRow = TILE + 4;
+    constexpr int kOperandBytes = 2 * TILE * kRow * 2, kOutBytes = TILE * kOutRow * 4;
+    __shared__ __align__(16) unsigned char lds_raw[kOperandBytes > kOutBytes ? kOperandBytes : kOutBytes];
+    uint16_t *lds_q = reinterpret_cast<uint16_t *>(lds_raw);
+    uint16_t *lds_k = lds_q + TILE * kRow;
+    float *lds_s = reinterpret_cast<float *>(lds_raw);
+
+    // gridDim.x is a multiple of 8; items [first, last) belong to this XCD
+    const unsigned per = gridDim.x / 8, xcd = blockIdx.x % 8, j = blockIdx.x / 8;
+    const unsigned span = (total + 7) / 8;
+    const unsigned first = xcd * span, last = min(total, first + span);
+    const unsigned per_head = (unsigned)(tiles * tiles);
+
+    float4 qr[kLoads], kr[kLoads];
+    auto load = [&](unsigned it) {
+        const size_t bh = it / per_head;
+        const int tile = (int)(it % per_head), ti = tile / tiles, tj = tile % tiles;
+        const float4 *qa = reinterpret_cast<const float4 *>(qp + (bh * nb + (size_t)ti * TILE) * DH);
+        const float4 *kb = reinterpret_cast<const float4 *>(kp + (bh * nb + (size_t)tj * TILE) * DH);
+        const int q_rows = min(TILE, nb - ti * TILE), k_rows = min(TILE, nb - tj * TILE);
+#pragma unroll
+        for (int m = 0; m < kLoads; ++m) {
+            const int e = threadIdx.x + kThreads * m;
+            const int r = e / kF4PerRow;
+            qr[m] = r < q_rows ? qa[e] : make_float4(0.f, 0.f, 0.f, 0.f);
+            kr[m] = r < k_rows ? kb[e] : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+    };
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    const int r16 = lane & 15, quad = lane >> 4;
+    const int row0 = 16 * kStrips * (wave / kStrips), col0 = 64 * (wave % kStrips);
+
+    unsigned item = first + j;
+    if (item < last)
+        load(item);
+    for (; item < last; item += per) { // the same trip count for the whole workgroup
+        const size_t bh = item / per_head;
+        const int tile = (int)(item % per_head), ti = tile / tiles, tj = tile % tiles;
+        const int q_rows = min(TILE, nb - ti * TILE), k_rows = min(TILE, nb - tj * TILE);
+        __syncthreads(); // the previous tile's scores have left LDS
+#pragma unroll
+        for (int m = 0; m < kLoads; ++m) {
+            const int e = threadIdx.x + kThreads * m;
+            const int r = e / kF4PerRow, c4 = e % kF4PerRow;
+            uint2 pa, pc;
+            pa.x = pack_bf16x2(qr[m].x, qr[m].y), pa.y = pack_bf16x2(qr[m].z, qr[m].w);
+            pc.x = pack_bf16x2(kr[m].x, kr[m].y), pc.y = pack_bf16x2(kr[m].z, kr[m].w);
+            *reinterpret_cast<uint2 *>(&lds_q[r * kRow + 4 * c4]) = pa;
+            *reinterpret_cast<uint2 *>(&lds_k[r * kRow + 4 * c4]) = pc;
+        }
+        __syncthreads();
+        if (item + per < last)
+            load(item + per); // in flight during the products and the stores below
+
+        f32x4 acc[kStrips][4];
+#pragma unroll
+        for (int i = 0; i < kStrips; ++i)
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                acc[i][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < DH / 16; ++s) {
+            const int kof = 16 * s + 4 * quad;
+            s16x4 a[kStrips];
+#pragma unroll
+            for (int i = 0; i < kStrips; ++i)
+                a[i] = *reinterpret_cast<const s16x4 *>(&lds_q[(row0 + 16 * i + r16) * kRow + kof]);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const s16x4 bv = *reinterpret_cast<const s16x4 *>(&lds_k[(col0 + 16 * t + r16) * kRow + kof]);
+#pragma unroll
+                for (int i = 0; i < kStrips; ++i)
+                    acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a[i], bv, acc[i][t], 0, 0, 0);
+            }
+        }
+
+        __syncthreads(); // every wave has finished reading the operand tiles
+#pragma unroll
+        for (int i = 0; i < kStrips; ++i)
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    lds_s[(row0 + 16 * i + 4 * quad + e) * kOutRow + col0 + 16 * t + r16] = acc[i][t][e];
+        __syncthreads();
+        float *out = scores + (bh * nb + (size_t)ti * TILE) * ld + (size_t)tj * TILE;
+#pragma unroll
+        for (int m = 0; m < TILE * TILE / 4 / kThreads; ++m) {
+            const int idx = threadIdx.x + kThreads * m;
+            const int row = idx / (TILE / 4), c4 = idx % (TILE / 4);
+            if (row < q_rows && 4 * c4 < k_rows) // columns up to nb rounded up to 4, all inside ld
+                __builtin_nontemporal_store(*reinterpret_cast<const f32x4 *>(&lds_s[row * kOutRow + 4 * c4]),
+                                            reinterpret_cast<f32x4 *>(out + (size_t)row * ld + 4 * c4));
+        }
     }
 }
 
@@ -505,10 +626,32 @@ template <int DH>
 void launch_scores_dh(const float *qp, const float *kp, float *scores, int nb, int ld, int H, int B,
                       hipStream_t stream)
 {
-    constexpr int kTile = DH <= 128 ? 128 : 64;
-    const int tiles = (nb + kTile - 1) / kTile;
-    hipLaunchKernelGGL((subblock_scores_kernel<DH, kTile>), dim3((unsigned)(tiles * tiles), (unsigned)H, (unsigned)B),
-                       dim3(4 * kTile), 0, stream, qp, kp, scores, nb, ld, tiles, H);
+    if constexpr (DH <= 128) {
+        // as many workgroups as the device holds at once (a multiple of 8 for
+        // the per-XCD ranges), no more than there are tiles (rounded up to 8)
+        const int tiles = (nb + 127) / 128;
+        const unsigned total = (unsigned)(tiles * tiles) * (unsigned)(H * B);
+        int dev = 0, cus = 0, per_cu = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 8) {
+            (void)hipGetLastError(); // a failed query: fall back to the MI355X's 256 CUs
+            cus = 256;
+        }
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, subblock_scores_persistent_kernel<DH>, 512, 0) !=
+                hipSuccess || per_cu < 1) {
+            (void)hipGetLastError();
+            per_cu = 1;
+        }
+        const unsigned resident = (unsigned)(cus * per_cu) / 8 * 8, need = (total + 7) / 8 * 8;
+        hipLaunchKernelGGL(subblock_scores_persistent_kernel<DH>, dim3(resident < need ? resident : need), dim3(512),
+                           0, stream, qp, kp, scores, nb, ld, tiles, total);
+    } else {
+        constexpr int kTile = 64;
+        const int tiles = (nb + kTile - 1) / kTile;
+        hipLaunchKernelGGL((subblock_scores_kernel<DH, kTile>),
+                           dim3((unsigned)(tiles * tiles), (unsigned)H, (unsigned)B), dim3(4 * kTile), 0, stream, qp,
+                           kp, scores, nb, ld, tiles, H);
+    }
 }
 
 template <int VPT>
