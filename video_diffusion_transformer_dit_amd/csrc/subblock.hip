@@ -626,6 +626,16 @@ template <int DH>
 void launch_scores_dh(const float *qp, const float *kp, float *scores, int nb, int ld, int H, int B,
                       hipStream_t stream)
 {
+    const uint64_t tiles128 = (uint64_t)((nb + 127) / 128);
+    if (DH <= 128 && tiles128 * tiles128 * (uint64_t)H * (uint64_t)B > 0x7fffffffull) {
+        // beyond the persistent kernel's 32-bit tile count: one workgroup per tile
+        constexpr int kTile = 128;
+        const int tiles = (nb + kTile - 1) / kTile;
+        hipLaunchKernelGGL((subblock_scores_kernel<DH, kTile>),
+                           dim3((unsigned)(tiles * tiles), (unsigned)H, (unsigned)B), dim3(4 * kTile), 0, stream, qp,
+                           kp, scores, nb, ld, tiles, H);
+        return;
+    }
     if constexpr (DH <= 128) {
         // as many workgroups as the device holds at once (a multiple of 8 for
         // the per-XCD ranges), no more than there are tiles (rounded up to 8)
