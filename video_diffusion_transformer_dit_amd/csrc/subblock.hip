@@ -276,18 +276,22 @@ __global__ __launch_bounds__(4 * TILE) void subblock_scores_kernel(const float *
 }
 
 // Persistent form of the 128 x 128 tile for Dh <= 128 (what the route runs):
-// one 512-thread workgroup per resident slot, each walking a run of tiles.
-// The XCD of workgroup w (w % 8, dispatch is round-robin) takes the (w % 8)-th
-// contiguous eighth of the (head, tile) list, and its workgroups interleave
-// over that range, so each XCD's L2 again holds one head's means at a time.
-// After a tile's operands are staged in LDS, the next tile's fp32 operands
-// are loaded into registers; those loads are in flight while the current
-// tile is multiplied, staged out through LDS and stored, which overlaps the
-// score stores with the next tile's loads (the short-lived workgroups of
-// subblock_scores_kernel store only at their end).  The arithmetic per tile
-// is that kernel's, so the scores are the same bit for bit; measured 15%
-// faster at 1953 blocks (115-121 against 135-138 us).  The registers holding
-// the prefetch leave room for one workgroup per CU at Dh = 128.
+// one 512-thread workgroup per resident slot, each walking a contiguous run of
+// tiles.  The XCD of workgroup w (w % 8, dispatch is round-robin) takes the
+// (w % 8)-th contiguous eighth of the (head, tile) list and splits it into
+// one run per workgroup, so each XCD's L2 holds one head's means at a time.
+// Tiles are numbered query-tile-major, so consecutive tiles of a run share
+// their query tile: it stays in LDS (bf16) and is loaded again only when the
+// run moves to the next query tile, about once per nb/128 tiles.  The key
+// tile is prefetched: once the current one is in LDS, the next one's fp32
+// values are loaded into registers, in flight while the current tile is
+// multiplied, staged out through its own LDS buffer and stored.  The score
+// stores thus overlap the next tile's loads, which the short-lived
+// workgroups of subblock_scores_kernel (storing only at their end) could not
+// do.  The arithmetic per tile is that kernel's, so the scores are the same
+// bit for bit.  At 1953 blocks: 102 us, against 121 us with both operands
+// prefetched per tile and 135 us with one workgroup per tile.  Registers and
+// the three LDS tiles (135 KB at Dh = 128) leave one workgroup per CU.
 template <int DH>
 __global__ __launch_bounds__(512) void subblock_scores_persistent_kernel(const float *__restrict__ qp,
                                                                          const float *__restrict__ kp,
@@ -299,58 +303,68 @@ __global__ __launch_bounds__(512) void subblock_scores_persistent_kernel(const f
     constexpr int kF4PerRow = DH / 4;
     constexpr int kLoads = TILE * kF4PerRow / kThreads; // float4 per thread and operand
     constexpr int kOutRow = TILE + 4;
-    constexpr int kOperandBytes = 2 * TILE * kRow * 2, kOutBytes = TILE * kOutRow * 4;
-    __shared__ __align__(16) unsigned char lds_raw[kOperandBytes > kOutBytes ? kOperandBytes : kOutBytes];
-    uint16_t *lds_q = reinterpret_cast<uint16_t *>(lds_raw);
-    uint16_t *lds_k = lds_q + TILE * kRow;
-    float *lds_s = reinterpret_cast<float *>(lds_raw);
+    __shared__ __align__(16) uint16_t lds_q[TILE * kRow];
+    __shared__ __align__(16) uint16_t lds_k[TILE * kRow];
+    __shared__ __align__(16) float lds_s[TILE * kOutRow];
 
-    // gridDim.x is a multiple of 8; items [first, last) belong to this XCD
+    // gridDim.x is a multiple of 8; items [first, last) belong to this XCD and
+    // [begin, end) to this workgroup
     const unsigned per = gridDim.x / 8, xcd = blockIdx.x % 8, j = blockIdx.x / 8;
     const unsigned span = (total + 7) / 8;
     const unsigned first = xcd * span, last = min(total, first + span);
+    const unsigned run = (span + per - 1) / per;
+    const unsigned begin = min(last, first + j * run), end = min(last, begin + run);
     const unsigned per_head = (unsigned)(tiles * tiles);
 
-    float4 qr[kLoads], kr[kLoads];
-    auto load = [&](unsigned it) {
+    float4 kr[kLoads];
+    auto load_k = [&](unsigned it) {
         const size_t bh = it / per_head;
-        const int tile = (int)(it % per_head), ti = tile / tiles, tj = tile % tiles;
-        const float4 *qa = reinterpret_cast<const float4 *>(qp + (bh * nb + (size_t)ti * TILE) * DH);
+        const int tj = (int)(it % per_head) % tiles;
         const float4 *kb = reinterpret_cast<const float4 *>(kp + (bh * nb + (size_t)tj * TILE) * DH);
-        const int q_rows = min(TILE, nb - ti * TILE), k_rows = min(TILE, nb - tj * TILE);
+        const int k_rows = min(TILE, nb - tj * TILE);
 #pragma unroll
         for (int m = 0; m < kLoads; ++m) {
             const int e = threadIdx.x + kThreads * m;
-            const int r = e / kF4PerRow;
-            qr[m] = r < q_rows ? qa[e] : make_float4(0.f, 0.f, 0.f, 0.f);
-            kr[m] = r < k_rows ? kb[e] : make_float4(0.f, 0.f, 0.f, 0.f);
+            kr[m] = e / kF4PerRow < k_rows ? kb[e] : make_float4(0.f, 0.f, 0.f, 0.f);
         }
     };
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
     const int r16 = lane & 15, quad = lane >> 4;
     const int row0 = 16 * kStrips * (wave / kStrips), col0 = 64 * (wave % kStrips);
 
-    unsigned item = first + j;
-    if (item < last)
-        load(item);
-    for (; item < last; item += per) { // the same trip count for the whole workgroup
+    if (begin < end)
+        load_k(begin);
+    size_t held_bh = ~(size_t)0; // the (head, query tile) whose operand is in lds_q
+    int held_ti = -1;
+    for (unsigned item = begin; item < end; ++item) { // the same trip count for the whole workgroup
         const size_t bh = item / per_head;
         const int tile = (int)(item % per_head), ti = tile / tiles, tj = tile % tiles;
         const int q_rows = min(TILE, nb - ti * TILE), k_rows = min(TILE, nb - tj * TILE);
-        __syncthreads(); // the previous tile's scores have left LDS
+        __syncthreads(); // the previous tile's operand and score reads are over
+        if (bh != held_bh || ti != held_ti) { // workgroup-uniform
+            const float4 *qa = reinterpret_cast<const float4 *>(qp + (bh * nb + (size_t)ti * TILE) * DH);
+#pragma unroll
+            for (int m = 0; m < kLoads; ++m) {
+                const int e = threadIdx.x + kThreads * m;
+                const int r = e / kF4PerRow, c4 = e % kF4PerRow;
+                const float4 a = r < q_rows ? qa[e] : make_float4(0.f, 0.f, 0.f, 0.f);
+                uint2 pa;
+                pa.x = pack_bf16x2(a.x, a.y), pa.y = pack_bf16x2(a.z, a.w);
+                *reinterpret_cast<uint2 *>(&lds_q[r * kRow + 4 * c4]) = pa;
+            }
+            held_bh = bh, held_ti = ti;
+        }
 #pragma unroll
         for (int m = 0; m < kLoads; ++m) {
             const int e = threadIdx.x + kThreads * m;
             const int r = e / kF4PerRow, c4 = e % kF4PerRow;
-            uint2 pa, pc;
-            pa.x = pack_bf16x2(qr[m].x, qr[m].y), pa.y = pack_bf16x2(qr[m].z, qr[m].w);
+            uint2 pc;
             pc.x = pack_bf16x2(kr[m].x, kr[m].y), pc.y = pack_bf16x2(kr[m].z, kr[m].w);
-            *reinterpret_cast<uint2 *>(&lds_q[r * kRow + 4 * c4]) = pa;
             *reinterpret_cast<uint2 *>(&lds_k[r * kRow + 4 * c4]) = pc;
         }
         __syncthreads();
-        if (item + per < last)
-            load(item + per); // in flight during the products and the stores below
+        if (item + 1 < end)
+            load_k(item + 1); // in flight during the products and the stores below
 
         f32x4 acc[kStrips][4];
 #pragma unroll
@@ -374,7 +388,8 @@ __global__ __launch_bounds__(512) void subblock_scores_persistent_kernel(const f
             }
         }
 
-        __syncthreads(); // every wave has finished reading the operand tiles
+        // lds_s has its own space; the barrier at the loop top ordered the
+        // previous tile's reads of it before these writes
 #pragma unroll
         for (int i = 0; i < kStrips; ++i)
 #pragma unroll
