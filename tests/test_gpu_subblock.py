@@ -154,6 +154,40 @@ def test_route_exact_scores_and_ties_bit_exact(nb):
         assert np.array_equal(to_host(kept), oracle.subblock_topk(s_ref, keep)), sparsity
 
 
+@pytest.mark.parametrize("nb", [300, 1953, 2100])
+@pytest.mark.parametrize("first_rare", [False, True])
+def test_route_crowded_first_digit_bit_exact(nb, first_rare):
+    # Scores crowded into the magnitudes [0.5, 2) with both signs, i.e. one
+    # first-digit bin and its mirror, on a 1/64 grid (exact in bf16 means and
+    # fp32 sums).  With the first key in the crowded pair the top-k counts that
+    # pair by ballots; with a rare first key (magnitude 8) it counts every key
+    # by atomics.  Either way the lists must equal the oracle's.
+    B, H, Dh = 1, 2, 16
+    rng = np.random.default_rng(1000 + nb + first_rare)
+    qp = np.zeros((B, H, nb, Dh))
+    qp[..., 0] = rng.choice([-1.0, 1.0], size=(B, H, nb))
+    qp[..., 1] = rng.choice([0.0, 0.125], size=(B, H, nb))
+    kp = np.zeros((B, H, nb, Dh))
+    crowd = rng.integers(4, 16, size=(B, H, nb)) / 8.0 * rng.choice([-1.0, 1.0], size=(B, H, nb))
+    spread = rng.choice([0.0, 0.0625, 0.25, 4.0, -3.0], size=(B, H, nb))
+    kp[..., 0] = np.where(rng.random((B, H, nb)) < 0.8, crowd, spread)
+    kp[..., 1] = rng.integers(-2, 3, size=(B, H, nb)) / 8.0
+    kp[..., 2:] = rng.integers(-8, 9, size=(B, H, nb, Dh - 2)) / 8.0  # multiplied by the zero q means
+    if first_rare:
+        kp[:, :, 0, 0] = 8.0
+    else:
+        kp[:, :, 0, 0] = 1.0
+    s_ref = oracle.subblock_scores(qp, kp)
+    qd = torch.from_numpy(qp).float().to(DEV)
+    kd = torch.from_numpy(kp).float().to(DEV)
+    for sparsity in (0.5, 0.75, 0.95):
+        keep = oracle.subblock_keep(nb, sparsity)
+        kept, scores = dit.dit_subblock_route(qd, kd, sparsity=sparsity)
+        torch.cuda.synchronize()
+        assert np.array_equal(to_host(scores)[..., :nb].astype(np.float64), s_ref)
+        assert np.array_equal(to_host(kept), oracle.subblock_topk(s_ref, keep)), sparsity
+
+
 def test_route_special_values():
     # all-zero means: every score is +0 or -0, all tie, the lowest indices are kept
     B, H, nb, Dh = 1, 1, 9, 16

@@ -494,7 +494,9 @@ constexpr int kMaxSurvivors = 256;
 // are written in ascending order, each lane's offset taken from ballots.
 // Counting never branches: a key that does not count adds to its lane's own
 // trash slot after the 256 bins (and a survivor past the bound to a trash
-// slot after the list), so the waves issue no exec-mask bookkeeping per key.
+// slot after the list), so the waves issue no exec-mask bookkeeping per key;
+// when the first digit's likeliest crowded bin pair holds most keys, that pair
+// is counted by ballots instead.
 template <int RV>
 __global__ __launch_bounds__(kWave) void subblock_topk_kernel(const float *__restrict__ scores,
                                                               int32_t *__restrict__ kept, int nb, int ld, int keep,
@@ -533,14 +535,54 @@ __global__ __launch_bounds__(kWave) void subblock_topk_kernel(const float *__res
                 atomicAdd(&hist[counts ? (key[r][e] >> shift) & 0xffu : 256u + lane], 1u);
             }
     };
-    // first digit: every valid key counts
+    // First digit: every valid key counts.  The first digit is the sign and
+    // the top of the exponent, so a row's keys can crowd into a few bins, and
+    // LDS atomics on one address serialise.  The candidate crowded bin is the
+    // first key's, paired with its mirror 255 - it (the key of -x is the
+    // bitwise inverse of the key of x, so that bin holds the same magnitudes
+    // with the other sign).  When the pair holds more than half of the first
+    // 256 keys (a wave-uniform test), the keys in it are counted with one
+    // ballot per bin and key slot and added once, and only the others go to
+    // the atomics.  Otherwise the ballots would cost more than the conflicts
+    // they remove, and every key adds to its bin.  The counts, and so the
+    // selection, are the same either way.
     reinterpret_cast<uint4 *>(hist)[lane] = make_uint4(0u, 0u, 0u, 0u);
     __syncthreads();
+    {
+        const uint32_t hot = (uint32_t)__builtin_amdgcn_readfirstlane((int)(key[0][0] >> 24)); // lane 0's key 0 is real
+        const uint32_t mirror = 255u - hot;
+        uint32_t in_pair = 0u, sampled = 0u;
 #pragma unroll
-    for (int r = 0; r < RV; ++r)
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t d = key[0][e] >> 24;
+            in_pair += (uint32_t)__builtin_popcountll(__ballot(valid(0, e) && (d == hot || d == mirror)));
+            sampled += (uint32_t)__builtin_popcountll(__ballot(valid(0, e)));
+        }
+        if (2u * in_pair > sampled) {
+            uint32_t hot_count = 0u, mirror_count = 0u;
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-            atomicAdd(&hist[valid(r, e) ? key[r][e] >> 24 : 256u + lane], 1u);
+            for (int r = 0; r < RV; ++r)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t d = key[r][e] >> 24;
+                    const bool v = valid(r, e);
+                    const bool h = v && d == hot, m = v && d == mirror;
+                    hot_count += (uint32_t)__builtin_popcountll(__ballot(h));
+                    mirror_count += (uint32_t)__builtin_popcountll(__ballot(m));
+                    atomicAdd(&hist[(v && !h && !m) ? d : 256u + lane], 1u);
+                }
+            if (lane == 0) {
+                atomicAdd(&hist[hot], hot_count);
+                atomicAdd(&hist[mirror], mirror_count);
+            }
+        } else {
+#pragma unroll
+            for (int r = 0; r < RV; ++r)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    atomicAdd(&hist[valid(r, e) ? key[r][e] >> 24 : 256u + lane], 1u);
+        }
+    }
     __syncthreads();
     choose_digit(hist, lane, 24, st);
     __syncthreads();
