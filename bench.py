@@ -698,8 +698,10 @@ def cpu_baseline(wl, ins, outs, target_s: float) -> dict:
         timing["swiglu"] += time.perf_counter() - t0
         return res
 
+    fused_seconds = [0.0]
+
     def fused_check(rows, host, gpu):
-        """Fused residual -> AdaLN z on the same rows (not part of the timed oracle work)."""
+        """Fused residual -> AdaLN z on the same rows (timed apart from the four ops' oracle work)."""
         samples = np.asarray(rows) // N
         ratio = 0.0
         for b in range(B):
@@ -707,9 +709,11 @@ def cpu_baseline(wl, ins, outs, target_s: float) -> dict:
             if sel.size == 0:
                 continue
             n = sel.size
+            t0 = time.perf_counter()
             _, z = oracle.gated_residual_adaln(host["rx"][sel].reshape(1, n, -1), host["ry"][sel].reshape(1, n, -1),
                                                gate[b:b + 1], shift[b:b + 1], scale[b:b + 1], eps=wl.eps,
                                                threads=threads)
+            fused_seconds[0] += time.perf_counter() - t0
             ratio = max(ratio, worst_ratio(gpu["fz"][sel], z.reshape(n, -1)))
         return ratio
 
@@ -743,6 +747,7 @@ def cpu_baseline(wl, ins, outs, target_s: float) -> dict:
     t = time.perf_counter()
     run_oracle(rows, host, nthreads=1, timing=single)
     single_tokens_per_s = len(rows) / (time.perf_counter() - t)
+    next_rows = next_row_oracle_rates(wl, ins, pos_ref, done, fused_seconds[0], threads)
     cpu_model = ""
     try:
         with open("/proc/cpuinfo", encoding="utf-8") as fh:
@@ -766,7 +771,74 @@ def cpu_baseline(wl, ins, outs, target_s: float) -> dict:
         "parity_rows_checked": done,
         "parity_max_err_over_bound": round(max_ratio, 4),
         "parity_ok": bool(max_ratio <= 1.0),
+        "next_rows": next_rows,
     }
+
+
+def next_row_oracle_rates(wl, ins, pos_ref, fused_tokens: int, fused_seconds: float, threads: int) -> dict:
+    """The oracle's rate on each next row, from a bounded sample of the workload's own inputs.
+
+    Fused residual -> AdaLN: the calls made to check the GPU's z above (``threads`` threads).  The
+    rest run single-threaded (the oracle has no threaded form of them) on a sample: 2048 tokens
+    for QK from a fused buffer to head-major, 16,384 tokens for the residual-change statistic and
+    for the block means (256 blocks), 256 query blocks of one head against all key blocks for the
+    scores, and the kept blocks of those 256 rows.  Inputs are the workload's seeded tensors (the
+    means are seeded normal values); nothing is taken from the GPU's outputs.
+    """
+    import numpy as np
+
+    import oracle
+    from synthetic_inputs import bits
+
+    R, N, D, H, Dh = wl.R, wl.N, wl.D, wl.H, wl.Dh
+    HD = H * Dh
+    out = {}
+    if fused_seconds > 0:
+        rate = fused_tokens / fused_seconds
+        out["fused_residual_adaln"] = {"tokens_per_s": round(rate, 1),
+                                       "GB_s": round(rate * 8 * D / 1e9, 4), "threads": threads,
+                                       "sample": f"{fused_tokens} tokens"}
+    n = min(2048, N)
+    q = bits(ins["q"].reshape(R, HD)[:n])
+    k = bits(ins["k"].reshape(R, HD)[:n])
+    qk = np.ascontiguousarray(np.concatenate([q, k], axis=1)).reshape(-1)
+    wq, wk = bits(ins["wq"]), bits(ins["wk"])
+    t = time.perf_counter()
+    oracle.qk_rmsnorm_rope3d_layout(qk, qk[HD:], wq, wk, pos_ref[:n], wl.bands, 1, n, H, Dh, 2 * HD, 1,
+                                    wl.theta, wl.eps)
+    dt = time.perf_counter() - t
+    out["qk_layout"] = {"tokens_per_s": round(n / dt, 1), "GB_s": round(n * (8 * HD + 12) / dt / 1e9, 4),
+                        "threads": 1, "sample": f"{n} tokens, fused q|k buffer in, head-major out"}
+    n = min(16384, N)
+    r = bits(ins["res_x"].reshape(R, D)[:n]).reshape(1, n, D)
+    rc = bits(ins["res_y"].reshape(R, D)[:n]).reshape(1, n, D)
+    t = time.perf_counter()
+    oracle.residual_change(r, rc)
+    dt = time.perf_counter() - t
+    out["residual_change"] = {"tokens_per_s": round(n / dt, 1), "GB_s": round(n * 4 * D / dt / 1e9, 4),
+                              "threads": 1, "sample": f"{n} tokens"}
+    t = time.perf_counter()
+    oracle.subblock_pool(bits(ins["q"].reshape(R, HD)[:n]).reshape(1, n, H, Dh))
+    dt = time.perf_counter() - t
+    out["subblock_pool"] = {"tokens_per_s": round(n / dt, 1), "GB_s": round(n * 2 * HD / dt / 1e9, 4),
+                            "threads": 1, "sample": f"{n} tokens ({-(-n // 64)} blocks) of q"}
+    nb = -(-N // 64)
+    nq = min(256, nb)
+    g = np.random.default_rng(0)
+    qp = g.standard_normal((1, 1, nq, Dh)) * 0.125
+    kp = g.standard_normal((1, 1, nb, Dh)) * 0.125
+    t = time.perf_counter()
+    s = oracle.subblock_scores(qp, kp)
+    dt = time.perf_counter() - t
+    out["subblock_scores"] = {"scores_per_s": round(nq * nb / dt, 1), "GFLOP_s": round(2 * nq * nb * Dh / dt / 1e9, 4),
+                              "threads": 1, "sample": f"{nq} query blocks x {nb} key blocks, Dh {Dh}"}
+    keep = oracle.subblock_keep(nb, 0.75)
+    t = time.perf_counter()
+    oracle.subblock_topk(s, keep)
+    dt = time.perf_counter() - t
+    out["subblock_topk"] = {"rows_per_s": round(nq / dt, 1), "GB_s": round(nq * (4 * nb + 4 * keep) / dt / 1e9, 4),
+                            "threads": 1, "sample": f"{nq} rows of {nb} scores, keep {keep}"}
+    return out
 
 # --------------------------------------------------------------------------- rocprofv3 summaries
 

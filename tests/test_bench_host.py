@@ -1,0 +1,73 @@
+"""Host-side pieces of bench.py, on the CPU.
+
+The byte counts that every GB/s figure divides by are checked against the
+per-token sizes the workload's tensor shapes fix (bf16 activations: AdaLN
+reads and writes D values, the gated residual reads two and writes one row of
+D, SwiGLU reads 2F and writes F, QK reads and writes q and k of H x Dh plus a
+12-byte position).  The oracle-rate leg of the CPU baseline runs on the
+32-token workload.
+"""
+import math
+
+import pytest
+
+import bench
+import oracle
+import synthetic_inputs as si
+
+
+def test_more_than_one_gpu_is_refused_before_any_device_work(capsys):
+    assert bench.main(["--gpus", "2"]) == 2
+    assert "one GPU" in capsys.readouterr().err
+
+
+@pytest.mark.parametrize("name", ["tiny", "full5s", "batch2"])
+def test_chain_bytes_per_token(name):
+    wl = si.WORKLOADS[name]
+    b = bench.op_bytes(wl)
+    R, B, N = wl.R, wl.B, wl.N
+    per_token = {"adaln": 2 * 2 * wl.D, "residual": 3 * 2 * wl.D, "swiglu": 3 * 2 * wl.F,
+                 "qk": 4 * 2 * wl.H * wl.Dh}
+    if name != "tiny":
+        # the 1344x768 workloads: 16,384 + 24,576 + 98,304 + 32,768 = 172,032 bytes per token
+        assert per_token == {"adaln": 16384, "residual": 24576, "swiglu": 98304, "qk": 32768}
+    # per-launch extras: the [B, D] modulation vectors, positions once per token of a sample, the two
+    # RMSNorm weights
+    assert b["adaln"] == R * per_token["adaln"] + 2 * B * wl.D * 2
+    assert b["residual"] == R * per_token["residual"] + B * wl.D * 2
+    assert b["swiglu"] == R * per_token["swiglu"]
+    assert b["qk"] == R * per_token["qk"] + 12 * N + 2 * wl.Dh * 2
+    assert b["positions"] == 12 * N
+
+
+def test_next_row_bytes_full5s():
+    wl = si.WORKLOADS["full5s"]
+    b = bench.op_bytes(wl, next_rows=True)
+    nb, keep = 1953, 489  # ceil(124,992 / 64) blocks; 1953 - floor(0.75 * 1953) kept
+    assert bench.dit_keep(nb) == keep
+    assert b["residual_adaln"] == 4 * wl.R * wl.D * 2 + 3 * wl.D * 2  # 8 bytes per element
+    assert b["residual_adaln"] < b["adaln"] + b["residual"]  # the fusion saves the re-read of x_out
+    assert b["qk_layout"] == b["qk"]
+    assert b["scores"] == 2 * 32 * nb * 128 * 4 + 32 * nb * nb * 4
+    assert b["topk"] == 32 * nb * nb * 4 + 32 * nb * keep * 4
+
+
+def test_committed_traffic_is_gated_by_workload_and_close_to_algorithmic():
+    assert bench.committed_traffic("swiglu", "tiny") is None  # no counter summary for that workload
+    t = bench.committed_traffic("swiglu", "full5s")
+    if t is not None:  # present while the kernel source matches the summary's hash
+        assert abs(t / bench.op_bytes(si.WORKLOADS["full5s"])["swiglu"] - 1) < 0.02
+
+
+def test_next_row_oracle_rates_on_the_tiny_workload():
+    wl = si.WORKLOADS["tiny"]
+    ins = si.make_inputs(wl, "cpu", names=["q", "k", "wq", "wk", "res_x", "res_y"])
+    pos = oracle.packed_positions(*wl.grid, wl.n_extra)
+    rates = bench.next_row_oracle_rates(wl, ins, pos, fused_tokens=32, fused_seconds=0.01, threads=1)
+    assert set(rates) == {"fused_residual_adaln", "qk_layout", "residual_change", "subblock_pool",
+                          "subblock_scores", "subblock_topk"}
+    for row in rates.values():
+        rate = row.get("tokens_per_s") or row.get("scores_per_s") or row.get("rows_per_s")
+        assert rate is not None and rate > 0 and math.isfinite(rate)
+        assert row["threads"] >= 1 and row["sample"]
+    assert rates["subblock_scores"]["sample"].startswith("1 query blocks x 1 key blocks")  # 32 tokens: one block
