@@ -155,6 +155,9 @@ def parse_args(argv=None):
     p.add_argument("--summarize-rocprof", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
                    help="write profiles/ summaries from rocprofv3 CSV output of a kernel-trace run and of "
                         "FETCH_SIZE and WRITE_SIZE counter runs of this benchmark, then exit")
+    p.add_argument("--summarize-sq", nargs=2, metavar=("TRACE_DIR", "SQ_DIR"),
+                   help="write the profiles/ summary of the shader-sequencer counter run (instruction mix, LDS "
+                        "waits, VALU issue rate, MFMA work) next to the kernel trace, then exit")
     return p.parse_args(argv)
 
 
@@ -162,6 +165,8 @@ def main(argv=None) -> int:
     args = parse_args(argv)
     if args.summarize_rocprof:
         return summarize_rocprof(*args.summarize_rocprof, workload=args.workload)
+    if args.summarize_sq:
+        return summarize_sq(*args.summarize_sq, workload=args.workload)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures the chain on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
@@ -873,6 +878,22 @@ rocprofv3 --pmc WRITE_SIZE --output-format csv -d $OUT/prof_write -o write -- \\
     python $REPO/bench.py --workload {wl} --steps 2 --warmup 1 --no-cpu-baseline --copy-calibration
 cd $REPO && python bench.py --workload {wl} --summarize-rocprof $OUT/prof_trace $OUT/prof_fetch $OUT/prof_write"""
 
+SQ_COUNTERS = ("SQ_WAVES", "SQ_INSTS_VALU", "SQ_INSTS_SALU", "SQ_INSTS_LDS", "SQ_INSTS_MFMA", "SQ_INSTS_VMEM_RD",
+               "SQ_WAIT_INST_LDS", "SQ_WAVE_CYCLES")
+
+SQ_COMMANDS = """\
+cd /tmp && export TMPDIR=/tmp
+rocprofv3 --kernel-trace --stats --output-format csv -d $OUT/prof_trace -o trace -- \\
+    python $REPO/bench.py --workload {wl} --steps 10 --warmup 2 --no-cpu-baseline
+rocprofv3 --pmc {counters} --output-format csv -d $OUT/prof_sq -o sq -- \\
+    python $REPO/bench.py --workload {wl} --steps 2 --warmup 1 --no-cpu-baseline --no-graph
+cd $REPO && python bench.py --workload {wl} --summarize-sq $OUT/prof_trace $OUT/prof_sq"""
+
+# wave64 VALU instructions the chip can issue per second: 256 CUs x 4 SIMDs x 2.4 GHz, one wave64
+# instruction per SIMD every 4 cycles (16 lanes wide)
+VALU_ISSUE_PEAK = 256 * 4 * 2.4e9 / 4
+MFMA_16X16X16_FLOPS = 2 * 16 * 16 * 16
+
 
 def _kernel_op(name: str):
     for pattern, op in KERNEL_OPS:
@@ -1002,6 +1023,87 @@ def summarize_rocprof(trace_dir: str, fetch_dir: str, write_dir: str, workload: 
         with open(os.path.join(out_dir, f"{op}_{workload}_counters.md"), "w", encoding="utf-8") as fh:
             fh.write("\n".join(body) + "\n")
     print(f"wrote profiles/ summaries for {workload}; calibration factors {factor}")
+    return 0
+
+
+def _full_size_durations(trace_dir: str) -> dict:
+    """op -> average duration (us) of its full-size launches in a kernel-trace run."""
+    by_grid = {}
+    for r in _csv_rows(trace_dir, "kernel_trace.csv"):
+        op = _kernel_op(r["Kernel_Name"])
+        if op:
+            grid = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
+            by_grid.setdefault(op, {}).setdefault(grid, []).append(
+                (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    return {op: sum(g[max(g)]) / len(g[max(g)]) for op, g in by_grid.items()}
+
+
+def summarize_sq(trace_dir: str, sq_dir: str, workload: str = "full5s", out_dir: str | None = None) -> int:
+    """Shader-sequencer counters per kernel (full-size launches, averaged per dispatch) as a profiles/ summary.
+
+    VALU issue is SQ_INSTS_VALU over the kernel-trace average duration, against VALU_ISSUE_PEAK; the
+    LDS wait share is SQ_WAIT_INST_LDS over SQ_WAVE_CYCLES (both in quad-cycles); MFMA work is
+    SQ_INSTS_MFMA x 8192 flops (v_mfma_f32_16x16x16_bf16) against the algorithmic flops of the scores.
+    """
+    import synthetic_inputs as si
+
+    wl = si.WORKLOADS[workload]
+    avg_us = _full_size_durations(trace_dir)
+    per = {}  # op -> grid -> dispatch id -> counter -> value
+    for r in _csv_rows(sq_dir, "counter_collection.csv"):
+        op = _kernel_op(r["Kernel_Name"])
+        if op is None or r["Counter_Name"] not in SQ_COUNTERS:
+            continue
+        d = per.setdefault(op, {}).setdefault(int(r["Grid_Size"]), {}).setdefault(r["Dispatch_Id"], {})
+        d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    nb = -(-wl.N // 64)
+    score_flops = 2.0 * wl.B * wl.H * nb * nb * wl.Dh
+    lines = [f"# Shader-sequencer counters per kernel: {wl.description}", "",
+             "One rocprofv3 counter run of the benchmark with the eight SQ counters below, next to the "
+             "kernel-trace run that gives each kernel's average duration. Full-size launches only, averaged "
+             "per dispatch. Per-wave figures divide by SQ_WAVES. VALU issue = SQ_INSTS_VALU per second of "
+             "the traced average duration, as a share of the chip's wave64 issue limit (256 CUs x 4 SIMDs x "
+             f"2.4 GHz / 4 cycles = {VALU_ISSUE_PEAK:.3e} per second). LDS wait = SQ_WAIT_INST_LDS / "
+             "SQ_WAVE_CYCLES (both in quad-cycles). MFMA flops = SQ_INSTS_MFMA x 8192.", "",
+             f"Counters: {' '.join(SQ_COUNTERS)}", "",
+             "Commands (REPO = the repository root, OUT = an output directory for the raw rocprofv3 files):", "",
+             "```", SQ_COMMANDS.format(wl=workload, counters=" ".join(SQ_COUNTERS)), "```", "",
+             "| kernel | dispatches | waves | VALU / wave | SALU / wave | LDS / wave | MFMA / wave | "
+             "VMEM reads / wave | LDS wait % | avg us | VALU issue % of limit |",
+             "|---|---|---|---|---|---|---|---|---|---|---|"]
+    extra = []
+    for op in (*OPS, *NEXT_OPS, "copy"):
+        if op not in per:
+            continue
+        grids = per[op]
+        ds = list(grids[max(grids)].values())
+        mean = {c: sum(d.get(c, 0.0) for d in ds) / len(ds) for c in SQ_COUNTERS}
+        waves = mean["SQ_WAVES"]
+        if waves <= 0:
+            continue
+        pw = {c: mean[c] / waves for c in SQ_COUNTERS}
+        wait = 100.0 * mean["SQ_WAIT_INST_LDS"] / mean["SQ_WAVE_CYCLES"] if mean["SQ_WAVE_CYCLES"] else 0.0
+        us = avg_us.get(op)
+        issue = f"{100.0 * mean['SQ_INSTS_VALU'] / (us * 1e-6) / VALU_ISSUE_PEAK:.1f}" if us else "-"
+        us_s = f"{us:.2f}" if us else "-"
+        lines.append(f"| {op} | {len(ds)} | {waves:.0f} | {pw['SQ_INSTS_VALU']:.1f} | {pw['SQ_INSTS_SALU']:.1f} "
+                     f"| {pw['SQ_INSTS_LDS']:.1f} | {pw['SQ_INSTS_MFMA']:.1f} | {pw['SQ_INSTS_VMEM_RD']:.1f} "
+                     f"| {wait:.1f} | {us_s} | {issue} |")
+        if op == "scores" and mean["SQ_INSTS_MFMA"] > 0:
+            mf = mean["SQ_INSTS_MFMA"] * MFMA_16X16X16_FLOPS
+            extra.append(f"- scores: MFMA flops per launch {mf:.4e} against {score_flops:.4e} algorithmic "
+                         f"({mf / score_flops:.3f}x: tiles padded to 128 blocks)"
+                         + (f"; {mf / (us * 1e-6) / 1e12:.1f} TFLOP/s issued at the traced average" if us else ""))
+    sources = {}
+    for op in per:
+        if op in KERNEL_SOURCES:
+            sources.setdefault(KERNEL_SOURCES[op], source_digest(op))
+    lines += [""] + extra + [f"- kernel source sha256 ({name} and device_common.hpp): {digest}"
+                             for name, digest in sorted(sources.items())]
+    out = os.path.join(out_dir or os.path.join(ROOT, "profiles"), f"kernels_{workload}_sq_counters.md")
+    with open(out, "w", encoding="utf-8") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print(f"wrote {out}")
     return 0
 
 

@@ -71,3 +71,33 @@ def test_next_row_oracle_rates_on_the_tiny_workload():
         assert rate is not None and rate > 0 and math.isfinite(rate)
         assert row["threads"] >= 1 and row["sample"]
     assert rates["subblock_scores"]["sample"].startswith("1 query blocks x 1 key blocks")  # 32 tokens: one block
+
+
+def test_sq_summary_from_synthetic_counter_files(tmp_path):
+    import csv
+
+    topk = "void dit::(anonymous namespace)::subblock_topk_kernel<8>(float const*, int*, int, int, int, int)"
+    trace, sq = tmp_path / "trace", tmp_path / "sq"
+    trace.mkdir()
+    sq.mkdir()
+    with open(trace / "t_kernel_trace.csv", "w", newline="") as fh:
+        w = csv.writer(fh)
+        w.writerow(["Kernel_Name", "Grid_Size_X", "Grid_Size_Y", "Grid_Size_Z", "Start_Timestamp", "End_Timestamp"])
+        w.writerow([topk, 64 * 1953, 32, 1, 1_000, 201_000])  # 200 us
+        w.writerow([topk, 64 * 100, 32, 1, 0, 50_000])  # a smaller launch, left out
+    waves = 62_496
+    vals = {"SQ_WAVES": waves, "SQ_INSTS_VALU": waves * 1000, "SQ_INSTS_SALU": waves * 500, "SQ_INSTS_LDS": waves * 80,
+            "SQ_INSTS_MFMA": 0, "SQ_INSTS_VMEM_RD": waves * 8, "SQ_WAIT_INST_LDS": 25, "SQ_WAVE_CYCLES": 100}
+    with open(sq / "p_counter_collection.csv", "w", newline="") as fh:
+        w = csv.writer(fh)
+        w.writerow(["Dispatch_Id", "Kernel_Name", "Grid_Size", "Counter_Name", "Counter_Value"])
+        for c, v in vals.items():
+            w.writerow([7, topk, 64 * 1953 * 32, c, v])
+    assert bench.summarize_sq(str(trace), str(sq), "full5s", out_dir=str(tmp_path)) == 0
+    text = (tmp_path / "kernels_full5s_sq_counters.md").read_text()
+    row = next(line for line in text.splitlines() if line.startswith("| topk |"))
+    cells = [c.strip() for c in row.strip("|").split("|")]
+    # waves, VALU / wave, SALU / wave, LDS / wave, MFMA / wave, VMEM / wave, LDS wait %, avg us
+    assert cells[1:10] == ["1", "62496", "1000.0", "500.0", "80.0", "0.0", "8.0", "25.0", "200.00"]
+    # 62.5 M wave instructions in 200 us against 256 x 4 x 2.4e9 / 4 per second
+    assert float(cells[10]) == pytest.approx(100 * waves * 1000 / 200e-6 / (256 * 4 * 2.4e9 / 4), abs=0.06)
