@@ -230,7 +230,9 @@ dit_status dit_gated_residual_adaln(const dit_bf16 *x, const dit_bf16 *y,
  *                 least dit_residual_change_workspace_bytes(B, N, D) bytes
  *                 (DIT_ERR_ARG if smaller); its contents on entry do not
  *                 matter and on return are unspecified
- *   D             multiple of 8; B <= 65535
+ *   D             multiple of 8; B <= 65535; per sample at most
+ *                 4,194,303 tiles of 2048 16-byte vectors, i.e. N * D <=
+ *                 68,719,460,352 (else DIT_ERR_ARG)
  * Sums are fp32 over each 8-value vector and fp64 above, in a fixed order:
  * repeated calls give bit-identical results.  B == 0 is a no-op; N == 0
  * writes zeros.  No buffer may overlap another (DIT_ERR_ARG).

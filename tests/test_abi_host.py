@@ -196,11 +196,15 @@ def test_residual_change_validation(lib):
     assert ws(2, 3, 8) == 2 * 16
     assert ws(1, 0, 8) == 0
     assert ws(-1, 4, 8) == -1 and ws(1, 4, 12) == -1 and ws(70000, 4, 8) == -1
+    # at most 2^22 - 1 tiles of 2048 vectors per sample (1024-thread workgroups: < 2^32 work-items)
+    assert ws(1, 8_388_606, 8192) == 16 * 4_194_303
+    assert ws(1, 8_388_607, 8192) == -1
 
     def f(r=P, rc=Q, out=R, w=S, wb=1 << 20, B=1, N=4, D=4096):
         return lib.dit_residual_change(r, rc, out, w, wb, B, N, D, None)
 
     assert f(B=-1) == DIT_ERR_ARG
+    assert f(N=8_388_607, D=8192) == DIT_ERR_ARG  # 4,194,304 tiles
     assert f(D=12) == DIT_ERR_SHAPE
     assert f(wb=0) == DIT_ERR_ARG  # workspace too small
     assert f(out=0) == DIT_ERR_NULL

@@ -221,9 +221,10 @@ dit_status dit_gated_residual_adaln(const dit_bf16 *x, const dit_bf16 *y, const 
 }
 
 // Samples per call of the residual-change statistic (one grid row each) and
-// tiles per sample (the grid's x extent, kept below 2^24 workgroups).
+// tiles per sample: the grid's x extent in 1024-thread workgroups, so that its
+// work-item count stays below 2^32.
 constexpr int64_t kMaxSamples = 65535;
-constexpr int64_t kMaxChangeTiles = (int64_t(1) << 24) - 1;
+constexpr int64_t kMaxChangeTiles = (int64_t(1) << 22) - 1;
 
 int64_t dit_residual_change_workspace_bytes(int64_t B, int64_t N, int64_t D)
 {

@@ -52,9 +52,9 @@ hipError_t launch_gated_residual(const void *x, const void *y, const void *gate,
     const int C = (int)(D / 8);
     const unsigned segs = (unsigned)((C + kResidualThreads - 1) / kResidualThreads);
     const uint64_t tiles = (uint64_t)rows * segs;
-    if (tiles > 0xffffffffull)
-        return hipErrorInvalidConfiguration;
     const unsigned grid = tiles < (1u << 23) - 1 ? (unsigned)tiles : (1u << 23) - 1; // < 2^32 work-items
+    if (tiles > 0xffffffffull - grid) // the kernel's 32-bit tile counter must not wrap (tile + grid)
+        return hipErrorInvalidConfiguration;
     const int B = (int)(rows / N);
     const auto *xv = static_cast<const u32x4 *>(x);
     const auto *yv = static_cast<const u32x4 *>(y);

@@ -66,11 +66,12 @@ hipError_t launch_swiglu(const void *in, void *out, int64_t M, int64_t F, hipStr
     const int C = (int)(F / 8);
     const unsigned segs = (unsigned)((C + kSwigluThreads - 1) / kSwigluThreads);
     const uint64_t tiles = (uint64_t)M * segs;
-    if (tiles > 0xffffffffull)
-        return hipErrorInvalidConfiguration;
     // A dispatch holds fewer than 2^32 work-items: beyond 2^24-1 workgroups the
-    // grid stays at that size and workgroups loop over tiles.
+    // grid stays at that size and workgroups loop over tiles.  The kernel's
+    // 32-bit tile counter must not wrap on its last step (tile + grid).
     const unsigned grid = tiles < (1u << 24) - 1 ? (unsigned)tiles : (1u << 24) - 1;
+    if (tiles > 0xffffffffull - grid)
+        return hipErrorInvalidConfiguration;
     const auto *src = static_cast<const u32x4 *>(in);
     auto *dst = static_cast<u32x4 *>(out);
     if ((segs & (segs - 1)) == 0) {
