@@ -129,3 +129,49 @@ def test_swiglu_past_the_grid_cap():
     idx = sampled(M, around=(((1 << 24) - 1) // 2,))
     assert_close(rows_of(out, idx, F), oracle.swiglu(bits(rows_of(inp, idx, 2 * F))), "swiglu past the cap")
     del inp, out
+
+
+def test_width_limits_streaming_ops():
+    W = 1 << 24  # the widest row SwiGLU, the gated residual and the residual change accept
+    print(f"[limits] rows {W} wide", flush=True)
+    sw_in = randn_bf16((2, 2 * W), 31, 2.0)
+    sw = dit.dit_swiglu(sw_in)
+    x, y = randn_bf16((1, 2, W), 32), randn_bf16((1, 2, W), 33)
+    gate = randn_bf16((1, W), 34, 0.1)
+    res = dit.dit_gated_residual(x, y, gate)
+    change = dit.dit_residual_change(x, y)
+    torch.cuda.synchronize()
+    assert_close(sw, oracle.swiglu(bits(sw_in)), "swiglu 2^24 wide")
+    assert_close(res, oracle.gated_residual(bits(x), bits(y), bits(gate)), "residual 2^24 wide")
+    ref = oracle.residual_change(bits(x), bits(y))
+    got = change.cpu().numpy()
+    # fp32 sums over each 8-value vector, fp64 above: relative error below 8 * 2^-24
+    assert np.allclose(got, ref, rtol=2e-6, atol=0.0), (got, ref)
+
+
+@pytest.mark.parametrize("head_major", [False, True])
+def test_head_row_limit_qk(head_major):
+    B, N, H, Dh, bands = 1, 67, 256, 256, (64, 96, 96)  # H * Dh = 65536, the largest head row
+    print(f"[limits] QK with H*Dh={H * Dh}, head_major={head_major}", flush=True)
+    pos = dit.dit_packed_positions(1, 1, N - 3, 3)
+    q, k = randn_bf16((B, N, H, Dh), 41), randn_bf16((B, N, H, Dh), 42)
+    wq = (1 + 0.02 * randn_bf16((Dh,), 43).float()).to(torch.bfloat16)
+    wk = (1 + 0.02 * randn_bf16((Dh,), 44).float()).to(torch.bfloat16)
+    qo, ko = dit.dit_qk_rmsnorm_rope3d(q, k, wq, wk, pos, bands)
+    qkv = torch.cat([q.reshape(B, N, H * Dh), k.reshape(B, N, H * Dh)], dim=2)
+    ql, kl = dit.dit_qk_rmsnorm_rope3d_layout(qkv, H, Dh, wq, wk, pos, bands, head_major=head_major)
+    qp_out, kp_out, qp, kp = dit.dit_qk_rmsnorm_rope3d_pool(q, k, wq, wk, pos, bands, head_major=head_major)
+    torch.cuda.synchronize()
+    pos_ref = oracle.packed_positions(1, 1, N - 3, 3)
+    q_ref, k_ref = oracle.qk_rmsnorm_rope3d(bits(q), bits(k), bits(wq), bits(wk), pos_ref, bands)
+    assert_close(qo, q_ref, "q")
+    assert_close(ko, k_ref, "k")
+    t = (lambda a: a.transpose(0, 2, 1, 3)) if head_major else (lambda a: a)
+    assert_close(ql, t(q_ref), "q layout")
+    assert_close(kl, t(k_ref), "k layout")
+    # the fused pooling writes the same q', k' and the 64-token block means of the stored values
+    assert torch.equal(qp_out, ql) and torch.equal(kp_out, kl)
+    qo_tm = qp_out.permute(0, 2, 1, 3).contiguous() if head_major else qp_out
+    ko_tm = kp_out.permute(0, 2, 1, 3).contiguous() if head_major else kp_out
+    assert_close(qp, oracle.subblock_pool(bits(qo_tm)), "q block means")
+    assert_close(kp, oracle.subblock_pool(bits(ko_tm)), "k block means")
