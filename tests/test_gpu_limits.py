@@ -175,3 +175,37 @@ def test_head_row_limit_qk(head_major):
     ko_tm = kp_out.permute(0, 2, 1, 3).contiguous() if head_major else kp_out
     assert_close(qp, oracle.subblock_pool(bits(qo_tm)), "q block means")
     assert_close(kp, oracle.subblock_pool(bits(ko_tm)), "k block means")
+
+
+def test_sample_limit():
+    B = 65535  # the most samples a call accepts (samples index a grid dimension)
+    print(f"[limits] B={B} samples", flush=True)
+    from subblock_checks import pool_bound
+
+    # routing on exact means (a 1/8 grid: every score is exact in fp32), 3 blocks of Dh 16 per sample
+    rng = np.random.default_rng(7)
+    qp = rng.integers(-8, 9, size=(B, 1, 3, 16)) / 8.0
+    kp = rng.integers(-8, 9, size=(B, 1, 3, 16)) / 8.0
+    kept, scores = dit.dit_subblock_route(torch.from_numpy(qp).float().to(DEV), torch.from_numpy(kp).float().to(DEV),
+                                          keep=2)
+    # block means over 65 tokens per sample (a ragged block of one token)
+    q = randn_bf16((B, 65, 1, 16), 51)
+    k = randn_bf16((B, 65, 1, 16), 52)
+    qm, km = dit.dit_subblock_pool(q, k)
+    # the residual change and AdaLN with one short row per sample
+    r, rc = randn_bf16((B, 2, 8), 53), randn_bf16((B, 2, 8), 54, 0.9)
+    change = dit.dit_residual_change(r, rc)
+    x = randn_bf16((B, 1, 8), 55)
+    shift, scale = randn_bf16((B, 8), 56, 0.1), randn_bf16((B, 8), 57, 0.1)
+    y = dit.dit_adaln_modulate(x, shift, scale)
+    torch.cuda.synchronize()
+
+    s_ref = oracle.subblock_scores(qp, kp)
+    assert np.array_equal(scores[..., :3].cpu().numpy().astype(np.float64), s_ref)
+    assert np.array_equal(kept.cpu().numpy(), oracle.subblock_topk(s_ref, 2))
+    for got, src in ((qm, q), (km, k)):
+        ref = oracle.subblock_pool(bits(src))
+        assert np.all(np.abs(got.cpu().numpy().astype(np.float64) - ref) <= pool_bound(bits(src), ref))
+    ref = oracle.residual_change(bits(r), bits(rc))
+    assert np.allclose(change.cpu().numpy(), ref, rtol=2e-6, atol=0.0)
+    assert_close(y, oracle.adaln_modulate(bits(x), bits(shift), bits(scale), threads=8), "adaln")
