@@ -100,6 +100,7 @@ ROUTE_SHAPES = [
     (1, 2, 700, 128),
     (1, 1, 2100, 64),   # more than 2048 blocks
     (1, 1, 4096, 16),   # the largest block count
+    (1, 1, 4096, 256),  # the largest block count at the largest head (64 x 64 score tiles)
 ]
 
 
