@@ -629,12 +629,20 @@ def main(argv=None) -> int:
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, ins, {"y": y, "out": out, "sw": sw, "qo": qo, "ko": ko,
                                                         "fz": fused_z}, args.cpu_seconds)
-    ok = all(consistency.values()) and result.get("cpu_baseline", {}).get("parity_ok", True)
+    # A figure is only credited to kernels whose outputs were checked: when the
+    # oracle check or a consistency check fails, `value` is null and the exit
+    # status is non-zero.  Without the oracle leg the line says it is unchecked.
+    checked = "cpu_baseline" in result
+    ok = all(consistency.values()) and (not checked or result["cpu_baseline"]["parity_ok"])
+    result["parity_checked"] = checked
+    result["parity_ok"] = bool(ok) if checked else None
     if not ok:
-        print("[bench] WARNING: GPU outputs disagree with the oracle or with each other", file=sys.stderr,
-              flush=True)
+        result["value_if_parity_held"] = result["value"]
+        result["value"] = None
+        print("[bench] FAILED: GPU outputs disagree with the oracle or with each other; value withheld",
+              file=sys.stderr, flush=True)
     print(json.dumps(result), flush=True)
-    return 0
+    return 0 if ok else 3
 
 
 def cpu_baseline(wl, ins, outs, target_s: float) -> dict:

@@ -100,7 +100,9 @@ dit_status dit_adaln_modulate(const dit_bf16 *x, const dit_bf16 *shift,
  *   gate   [B][D]
  *   out    [B][N][D]; out == x or out == y (in place) is allowed, any other
  *          overlap with an input is rejected (DIT_ERR_ARG)
- *   D      multiple of 8, D >= 8
+ *   D      multiple of 8, 8 <= D <= 2^24
+ *   B * N * ceil(D / 4096) <= 4,286,578,688 (2^32 - 2^23) row segments, else
+ *          DIT_ERR_ARG
  */
 dit_status dit_gated_residual(const dit_bf16 *x, const dit_bf16 *y,
                               const dit_bf16 *gate, dit_bf16 *out, int64_t B,
@@ -115,7 +117,9 @@ dit_status dit_gated_residual(const dit_bf16 *x, const dit_bf16 *y,
  * projection of width 2F emits them; the first half is gated.
  *   in     [M][2F]
  *   out    [M][F]; must not overlap `in` (DIT_ERR_ARG)
- *   F      multiple of 8, F >= 8
+ *   F      multiple of 8, 8 <= F <= 2^24
+ *   M * ceil(F / 2048) <= 4,278,190,080 (2^32 - 2^24) row segments, else
+ *          DIT_ERR_ARG
  * Finite inputs give finite outputs: silu saturates to a for large a and to
  * (-)0 for very negative a.
  */

@@ -41,7 +41,10 @@ def worst_ratio(gpu, ref) -> float:
 
 
 def assert_close(gpu, ref, what: str = ""):
-    """Fail with the worst element if any element breaks the bound or is not finite."""
+    """Fail with the worst element if any element breaks the bound or is not finite.
+
+    Returns the worst |gpu - ref| / bound over the elements (<= 1 when it passes).
+    """
     g = to_f64(gpu) if isinstance(gpu, torch.Tensor) else np.asarray(gpu, dtype=np.float64)
     r = np.asarray(ref, dtype=np.float64)
     assert g.shape == r.shape, f"{what}: shape {g.shape} vs oracle {r.shape}"
@@ -49,4 +52,21 @@ def assert_close(gpu, ref, what: str = ""):
     ex, i, gv, rv = worst(g, r)
     assert ex <= 0.0, (f"{what}: element {np.unravel_index(i, g.shape)} gpu={gv!r} oracle={rv!r} "
                        f"|err|={abs(gv - rv):.3e} > bound {ATOL + RTOL * abs(rv):.3e}")
-    return ex
+    return worst_ratio(g, r)
+
+
+def worst_ratio_threaded(gpu, ref, threads: int = 8) -> float:
+    """worst_ratio over large arrays, computed on row slices in parallel threads (numpy releases the GIL)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    gpu = np.asarray(gpu).reshape(-1)
+    ref = np.asarray(ref).reshape(-1)
+    assert gpu.shape == ref.shape, (gpu.shape, ref.shape)
+    n = gpu.size
+    if n == 0:
+        return 0.0
+    parts = max(1, min(threads, n // (1 << 16)))
+    bounds = [n * i // parts for i in range(parts + 1)]
+    with ThreadPoolExecutor(max_workers=parts) as pool:
+        return max(pool.map(lambda i: worst_ratio(gpu[bounds[i]:bounds[i + 1]], ref[bounds[i]:bounds[i + 1]]),
+                            range(parts)))

@@ -105,6 +105,8 @@ dit_status dit_gated_residual(const dit_bf16 *x, const dit_bf16 *y, const dit_bf
         return DIT_ERR_ARG;
     if (D < 8 || D % 8 != 0 || D > kMaxWidth)
         return DIT_ERR_SHAPE;
+    if (!dit::gated_residual_fits(rows, D))
+        return DIT_ERR_ARG;
     if (rows == 0)
         return DIT_OK;
     if (!x || !y || !gate || !out)
@@ -123,6 +125,8 @@ dit_status dit_swiglu(const dit_bf16 *in, dit_bf16 *out, int64_t M, int64_t F, v
         return DIT_ERR_ARG;
     if (F < 8 || F % 8 != 0 || F > kMaxWidth)
         return DIT_ERR_SHAPE;
+    if (!dit::swiglu_fits(M, F))
+        return DIT_ERR_ARG;
     if (M == 0)
         return DIT_OK;
     if (!in || !out)

@@ -25,7 +25,8 @@
 // reads, which measurably shortens the ALU phase each wave runs between its
 // loads and its stores.  A wave whose row belongs to a different sample than
 // the workgroup's first row (rows straddling a sample boundary) reads the
-// vectors from cache instead.
+// vectors from cache instead, and evaluates the same expression, so a row's
+// result does not depend on where it sits in the batch.
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -138,10 +139,8 @@ __global__ __launch_bounds__(256) void adaln_modulate_kernel(const u32x4 *x, con
                 unpack8(load_cached(sc + c), s);
                 unpack8(load_cached(sh + c), t);
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const float a = fmaf(rstd, s[i], rstd); // rstd * (1 + scale)
-                    o[i] = fmaf(v[k][i] - mean, a, t[i]);
-                }
+                for (int i = 0; i < 8; ++i) // the staged path's expression: same bits in any sample
+                    o[i] = fmaf((v[k][i] - mean) * rstd, 1.f + s[i], t[i]);
                 store_stream(y + base + c, pack8(o));
             }
         }

@@ -16,6 +16,12 @@ hipError_t launch_adaln_modulate(const void *x, const void *shift, const void *s
 hipError_t launch_gated_residual(const void *x, const void *y, const void *gate, void *out,
                                  int64_t rows, int64_t N, int64_t D, hipStream_t stream);
 
+// Whether rows x ceil(D / 4096) residual tiles fit the kernel's 32-bit tile counter.
+bool gated_residual_fits(int64_t rows, int64_t D);
+
+// Whether M x ceil(F / 2048) SwiGLU tiles fit the kernel's 32-bit tile counter.
+bool swiglu_fits(int64_t M, int64_t F);
+
 // out[r][j] = silu(in[r][j]) * in[r][F+j]; F % 8 == 0.
 hipError_t launch_swiglu(const void *in, void *out, int64_t M, int64_t F, hipStream_t stream);
 

@@ -44,16 +44,33 @@ __global__ __launch_bounds__(kResidualThreads) void gated_residual_kernel(const 
     }
 }
 
+// A dispatch holds fewer than 2^32 work-items: beyond 2^23 - 1 workgroups the
+// grid stays at that size and workgroups loop over tiles, and the kernel's
+// 32-bit tile counter must not wrap on its last step (tile + grid).
+constexpr uint64_t kGridCap = (1u << 23) - 1;
+
+uint64_t residual_tiles(int64_t rows, int64_t D)
+{
+    const uint64_t segs = (uint64_t)((D / 8 + kResidualThreads - 1) / kResidualThreads);
+    return (uint64_t)rows * segs;
+}
+
 } // namespace
+
+bool gated_residual_fits(int64_t rows, int64_t D)
+{
+    const uint64_t tiles = residual_tiles(rows, D);
+    return tiles <= 0xffffffffull - (tiles < kGridCap ? tiles : kGridCap);
+}
 
 hipError_t launch_gated_residual(const void *x, const void *y, const void *gate, void *out, int64_t rows, int64_t N,
                                  int64_t D, hipStream_t stream)
 {
     const int C = (int)(D / 8);
     const unsigned segs = (unsigned)((C + kResidualThreads - 1) / kResidualThreads);
-    const uint64_t tiles = (uint64_t)rows * segs;
-    const unsigned grid = tiles < (1u << 23) - 1 ? (unsigned)tiles : (1u << 23) - 1; // < 2^32 work-items
-    if (tiles > 0xffffffffull - grid) // the kernel's 32-bit tile counter must not wrap (tile + grid)
+    const uint64_t tiles = residual_tiles(rows, D);
+    const unsigned grid = (unsigned)(tiles < kGridCap ? tiles : kGridCap); // < 2^32 work-items
+    if (!gated_residual_fits(rows, D)) // the entry point refuses these sizes first
         return hipErrorInvalidConfiguration;
     const int B = (int)(rows / N);
     const auto *xv = static_cast<const u32x4 *>(x);

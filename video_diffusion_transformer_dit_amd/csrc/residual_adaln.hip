@@ -143,8 +143,9 @@ __global__ __launch_bounds__(256) void gated_residual_adaln_kernel(
     for (int k = 0; k < VPL; ++k) {
         const int c = lane + kWave * k;
         if (FULL || c < C) {
-            // The same expressions as adaln.hip on each path, so the fused op
-            // matches the two separate calls bit for bit.
+            // One expression on both paths, the same as adaln.hip's: the fused
+            // op matches the two separate calls bit for bit, and a row's result
+            // does not depend on where it sits in the batch.
             float t[8], o[8];
             if (staged) {
                 float ps[8];
@@ -159,7 +160,7 @@ __global__ __launch_bounds__(256) void gated_residual_adaln_kernel(
                 unpack8(load_cached(shift + (size_t)b * C + c), t);
 #pragma unroll
                 for (int i = 0; i < 8; ++i)
-                    o[i] = fmaf(v[k][i] - mean, fmaf(rstd, s[i], rstd), t[i]);
+                    o[i] = fmaf((v[k][i] - mean) * rstd, 1.f + s[i], t[i]);
             }
             store_stream(z + base + c, pack8(o));
         }

@@ -59,18 +59,32 @@ __global__ __launch_bounds__(kSwigluThreads) void swiglu_kernel(const u32x4 *__r
     }
 }
 
+// A dispatch holds fewer than 2^32 work-items: beyond 2^24 - 1 workgroups the
+// grid stays at that size and workgroups loop over tiles, and the kernel's
+// 32-bit tile counter must not wrap on its last step (tile + grid).
+constexpr uint64_t kGridCap = (1u << 24) - 1;
+
+uint64_t swiglu_tiles(int64_t M, int64_t F)
+{
+    const uint64_t segs = (uint64_t)((F / 8 + kSwigluThreads - 1) / kSwigluThreads);
+    return (uint64_t)M * segs;
+}
+
 } // namespace
+
+bool swiglu_fits(int64_t M, int64_t F)
+{
+    const uint64_t tiles = swiglu_tiles(M, F);
+    return tiles <= 0xffffffffull - (tiles < kGridCap ? tiles : kGridCap);
+}
 
 hipError_t launch_swiglu(const void *in, void *out, int64_t M, int64_t F, hipStream_t stream)
 {
     const int C = (int)(F / 8);
     const unsigned segs = (unsigned)((C + kSwigluThreads - 1) / kSwigluThreads);
-    const uint64_t tiles = (uint64_t)M * segs;
-    // A dispatch holds fewer than 2^32 work-items: beyond 2^24-1 workgroups the
-    // grid stays at that size and workgroups loop over tiles.  The kernel's
-    // 32-bit tile counter must not wrap on its last step (tile + grid).
-    const unsigned grid = tiles < (1u << 24) - 1 ? (unsigned)tiles : (1u << 24) - 1;
-    if (tiles > 0xffffffffull - grid)
+    const uint64_t tiles = swiglu_tiles(M, F);
+    const unsigned grid = (unsigned)(tiles < kGridCap ? tiles : kGridCap);
+    if (!swiglu_fits(M, F)) // the entry point refuses these sizes first
         return hipErrorInvalidConfiguration;
     const auto *src = static_cast<const u32x4 *>(in);
     auto *dst = static_cast<u32x4 *>(out);
