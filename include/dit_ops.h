@@ -24,7 +24,8 @@
  *     with a single round-to-nearest-even to bf16 at each output element.
  *   - Every pointer is a DEVICE pointer on the current HIP device.  The caller
  *     owns all buffers; the library allocates nothing, keeps no state between
- *     calls, and never synchronises.  Work is enqueued on `stream` (a
+ *     calls (one exception: the static scratch array of
+ *     dit_residual_change_noalloc), and never synchronises.  Work is enqueued on `stream` (a
  *     hipStream_t cast to void*; NULL = the default stream) and completes
  *     asynchronously, in stream order.
  *   - Arguments are validated on the host BEFORE any HIP call or write; a
@@ -39,6 +40,9 @@
  *                      call, or outputs that overlap inputs in a way the entry
  *                      point forbids
  *       DIT_ERR_HIP    the kernel launch itself failed (hipGetLastError)
+ *       DIT_ERR_SCRATCH  the sizes need more than the fixed capacity of the
+ *                      library's static scratch array (allocation-free entry
+ *                      points only)
  *     A call with zero rows is a no-op returning DIT_OK (its pointers are not
  *     examined).  Faults inside a
  *     kernel (for example a pointer that is not device memory) surface at the
@@ -62,10 +66,11 @@ typedef enum {
     DIT_ERR_SHAPE = 2,
     DIT_ERR_ALIGN = 3,
     DIT_ERR_ARG = 4,
-    DIT_ERR_HIP = 5
+    DIT_ERR_HIP = 5,
+    DIT_ERR_SCRATCH = 6 /* sizes beyond a static scratch buffer's capacity */
 } dit_status;
 
-#define DIT_ABI_VERSION 1
+#define DIT_ABI_VERSION 2
 
 /* Human-readable name of a status code; never NULL. */
 const char *dit_status_str(int status);
@@ -252,6 +257,31 @@ dit_status dit_residual_change(const dit_bf16 *r, const dit_bf16 *r_cached,
  * invalid.  Host-only; makes no HIP call.
  */
 int64_t dit_residual_change_workspace_bytes(int64_t B, int64_t N, int64_t D);
+
+/*
+ * dit_residual_change without the workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  The per-tile partials live in a static
+ * 2 MiB array inside the library's device code (one copy per GPU, held until
+ * the process ends), so the call allocates nothing: it makes no hipMalloc or
+ * hipFree and calls no allocating library routine.  Results are bit-identical
+ * to dit_residual_change on the same inputs (same kernels, same order).
+ *   r, r_cached, out, B, N, D  as for dit_residual_change
+ *   capacity   B * ceil(N * D / 16384) <= 131,072 partials (2 MiB), else
+ *              DIT_ERR_SCRATCH before any HIP call: about 2^31 elements in
+ *              all, e.g. one sample of up to 524,288 tokens of width 4096, or
+ *              two samples of 124,992 tokens.
+ * The first call on a device looks up the array's device address
+ * (hipGetSymbolAddress) and caches it; DIT_ERR_HIP if that fails.  Every call
+ * on one GPU shares the one array, which keeps the last call's partials: calls
+ * that overlap in time on one GPU (on different streams, or from several host
+ * threads without stream ordering) race on it and may return wrong sums.
+ * Calls ordered on one stream are safe.  Nothing in the array needs clearing
+ * between calls: each call writes every partial it reads.
+ */
+dit_status dit_residual_change_noalloc(const dit_bf16 *r, const dit_bf16 *r_cached,
+                                       double *out, int64_t B, int64_t N,
+                                       int64_t D, void *stream);
 
 /*
  * SubBlock sparse-attention routing, front-end.

@@ -67,7 +67,7 @@ def test_abi_version_matches_header(lib):
 
 
 def test_status_strings(lib):
-    for code in range(6):
+    for code in range(7):
         assert dit.dit_status_str(code).startswith(("DIT_OK", "DIT_ERR_"))
     assert dit.dit_status_str(99) == "unknown dit_status"
 
@@ -224,6 +224,34 @@ def test_residual_change_validation(lib):
     assert f(out=P + 64) == DIT_ERR_ARG  # output inside r
     assert f(w=Q) == DIT_ERR_ARG  # workspace over r_cached
     assert f(r=0, rc=0, out=0, w=0, B=0) == DIT_OK
+
+
+def test_residual_change_noalloc_validation(lib):
+    from video_diffusion_transformer_dit_amd import DIT_ERR_SCRATCH
+
+    def f(r=P, rc=Q, out=R, B=1, N=4, D=4096):
+        return lib.dit_residual_change_noalloc(r, rc, out, B, N, D, None)
+
+    # capacity 131,072 partials: B * ceil(N * D / 16384) of them
+    tiles_10s = (246_432 * 4096 // 8 + 2047) // 2048
+    assert tiles_10s == 61_608 and 2 * ((124_992 * 512 + 2047) // 2048) == 62_496  # the shipped workloads fit
+    assert f(N=524_288, D=4096, r=0) == DIT_ERR_NULL  # 524,288 tokens of width 4096 fill it exactly
+    assert f(N=524_289, D=4096) == DIT_ERR_SCRATCH
+    assert f(B=2, N=524_288, D=4096) == DIT_ERR_SCRATCH  # 2 x 131,072 partials
+    assert f(B=1, N=262_145, D=8192) == DIT_ERR_SCRATCH  # one partial more than the capacity
+    assert f(B=1, N=262_144, D=8192, out=0) == DIT_ERR_NULL  # exactly the capacity
+    assert f(B=-1) == DIT_ERR_ARG
+    assert f(B=70_000) == DIT_ERR_ARG
+    assert f(N=8_388_607, D=8192) == DIT_ERR_ARG  # past the per-sample tile limit, before the capacity check
+    assert f(D=12) == DIT_ERR_SHAPE
+    assert f(out=0) == DIT_ERR_NULL
+    assert f(r=0) == DIT_ERR_NULL
+    assert f(out=R + 4) == DIT_ERR_ALIGN
+    assert f(rc=Q + 8) == DIT_ERR_ALIGN
+    assert f(out=P + 64) == DIT_ERR_ARG  # output inside r
+    assert f(out=Q + 8) == DIT_ERR_ARG  # output inside r_cached
+    assert f(r=0, rc=0, out=0, B=0) == DIT_OK
+    assert f(B=2, N=524_288, D=4096, r=0, rc=0, out=0) == DIT_ERR_SCRATCH  # capacity before pointers
 
 
 def test_subblock_keep_and_ld(lib):

@@ -11,6 +11,8 @@ hand-written HIP kernels (``csrc/``; declarations in ``include/dit_ops.h``):
   dit_qk_rmsnorm_rope3d_layout  the same, reading q/k from a fused QKV buffer and
                           writing head-major outputs
   dit_residual_change     Cache-DiT statistic: sum |r - r_cached| / sum |r_cached| per sample
+  dit_residual_change_noalloc  the same with no workspace (a static scratch array), for callers
+                          that cannot allocate
   dit_subblock_pool       SubBlock routing: means of each 64-token block of q' and k'
   dit_qk_rmsnorm_rope3d_pool  QK RMSNorm + RoPE that also writes those block means
   dit_subblock_route      SubBlock routing: block scores and the kept key blocks per query block
@@ -24,6 +26,7 @@ from ._binding import (  # noqa: F401
     DIT_ERR_ALIGN,
     DIT_ERR_ARG,
     DIT_ERR_HIP,
+    DIT_ERR_SCRATCH,
     DIT_ERR_NULL,
     DIT_ERR_SHAPE,
     DIT_OK,
@@ -43,6 +46,7 @@ from ._binding import (  # noqa: F401
     dit_qk_rmsnorm_rope3d_layout,
     dit_qk_rmsnorm_rope3d_pool,
     dit_residual_change,
+    dit_residual_change_noalloc,
     dit_residual_change_workspace_bytes,
     dit_status_str,
     dit_subblock_keep,

@@ -16,7 +16,7 @@ import torch
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdit_ops.so")
 
-DIT_OK, DIT_ERR_NULL, DIT_ERR_SHAPE, DIT_ERR_ALIGN, DIT_ERR_ARG, DIT_ERR_HIP = range(6)
+DIT_OK, DIT_ERR_NULL, DIT_ERR_SHAPE, DIT_ERR_ALIGN, DIT_ERR_ARG, DIT_ERR_HIP, DIT_ERR_SCRATCH = range(7)
 
 # Every entry point the header declares, with its ctypes signature.
 _I64, _I32, _F32, _P = ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_void_p
@@ -33,6 +33,7 @@ SIGNATURES = {
     "dit_gated_residual_adaln": ([_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _F32, _P], ctypes.c_int),
     "dit_residual_change": ([_P, _P, _P, _P, _I64, _I64, _I64, _I64, _P], ctypes.c_int),
     "dit_residual_change_workspace_bytes": ([_I64, _I64, _I64], ctypes.c_int64),
+    "dit_residual_change_noalloc": ([_P, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
     "dit_subblock_keep": ([_I64, ctypes.c_double], ctypes.c_int64),
     "dit_subblock_scores_ld": ([_I64], ctypes.c_int64),
     "dit_subblock_pool": ([_P, _P, _P, _P, _I64, _I64, _I64, _I64, _I32, _P], ctypes.c_int),
@@ -266,6 +267,23 @@ def dit_residual_change(r, r_cached, out=None, workspace=None, stream=None):
         _check("dit_residual_change", load_library().dit_residual_change(
             r.data_ptr(), r_cached.data_ptr(), out.data_ptr(), workspace.data_ptr(), nbytes, B, N, D,
             _stream(stream, dev)))
+    return out
+
+
+def dit_residual_change_noalloc(r, r_cached, out, stream=None):
+    """dit_residual_change with its partials in the library's static scratch array: no workspace, no allocation.
+
+    ``out`` is a caller-owned [B, 3] float64 device tensor (this wrapper allocates nothing either).  Calls that
+    overlap in time on one GPU share the scratch array and race; calls ordered on one stream are safe.
+    """
+    _tensor(r, "r", ndim=3)
+    B, N, D = r.shape
+    _shape(_tensor(r_cached, "r_cached"), "r_cached", (B, N, D))
+    _shape(_tensor(out, "out", dtype=torch.float64), "out", (B, 3))
+    dev = _same_device(r, r_cached, out)
+    with torch.cuda.device(dev):
+        _check("dit_residual_change_noalloc", load_library().dit_residual_change_noalloc(
+            r.data_ptr(), r_cached.data_ptr(), out.data_ptr(), B, N, D, _stream(stream, dev)))
     return out
 
 

@@ -11,7 +11,9 @@
 //   6. misaligned pointers                      -> DIT_ERR_ALIGN
 //   7. forbidden overlaps                       -> DIT_ERR_ARG
 // and only then launches on the caller's stream; a failed launch returns
-// DIT_ERR_HIP.  Nothing is allocated, cached or synchronised.
+// DIT_ERR_HIP.  Nothing is allocated or synchronised; the only state is the
+// per-device address of the allocation-free residual-change entry point's
+// static scratch array, looked up on its first call on a device.
 #include <math.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -69,6 +71,7 @@ const char *dit_status_str(int status)
     case DIT_ERR_ALIGN: return "DIT_ERR_ALIGN: pointer not aligned (bf16 tensors need 16 bytes)";
     case DIT_ERR_ARG: return "DIT_ERR_ARG: size, eps, theta or buffer overlap out of range";
     case DIT_ERR_HIP: return "DIT_ERR_HIP: kernel launch failed";
+    case DIT_ERR_SCRATCH: return "DIT_ERR_SCRATCH: sizes exceed the library's static scratch buffer";
     default: return "unknown dit_status";
     }
 }
@@ -265,6 +268,33 @@ dit_status dit_residual_change(const dit_bf16 *r, const dit_bf16 *r_cached, doub
                                                           overlap(workspace, need, r_cached, nin))))
         return DIT_ERR_ARG;
     return launched(dit::launch_residual_change(r, r_cached, out, workspace, B, N, D, (hipStream_t)stream));
+}
+
+dit_status dit_residual_change_noalloc(const dit_bf16 *r, const dit_bf16 *r_cached, double *out, int64_t B,
+                                      int64_t N, int64_t D, void *stream)
+{
+    if (B < 0 || N < 0 || D < 0 || B > kMaxSamples || N > kMaxRows)
+        return DIT_ERR_ARG;
+    if (D < 8 || D % 8 != 0 || D > kMaxWidth)
+        return DIT_ERR_SHAPE;
+    const int64_t need = dit_residual_change_workspace_bytes(B, N, D);
+    if (need < 0)
+        return DIT_ERR_ARG;
+    if (need > dit::kResidualChangeScratchPartials * 16)
+        return DIT_ERR_SCRATCH;
+    if (B == 0)
+        return DIT_OK;
+    if (!out || (N > 0 && (!r || !r_cached)))
+        return DIT_ERR_NULL;
+    if (!aligned(out, 8) || (N > 0 && (!aligned(r, 16) || !aligned(r_cached, 16))))
+        return DIT_ERR_ALIGN;
+    const int64_t nin = B * N * D * 2, nout = B * 3 * 8;
+    if (N > 0 && (overlap(out, nout, r, nin) || overlap(out, nout, r_cached, nin)))
+        return DIT_ERR_ARG;
+    void *ws = nullptr;
+    if (dit::residual_change_scratch(&ws) != hipSuccess)
+        return DIT_ERR_HIP;
+    return launched(dit::launch_residual_change(r, r_cached, out, ws, B, N, D, (hipStream_t)stream));
 }
 
 // SubBlock routing: at most 4096 blocks of 64 tokens per sample (262,144 tokens).

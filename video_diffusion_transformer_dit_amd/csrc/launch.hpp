@@ -47,6 +47,13 @@ int64_t residual_change_tiles(int64_t N, int64_t D);
 hipError_t launch_residual_change(const void *r, const void *r_cached, double *out, void *workspace, int64_t B,
                                   int64_t N, int64_t D, hipStream_t stream);
 
+// Capacity, in (num, den) partials, of the library's static scratch array used by the
+// allocation-free residual-change entry point: 2 MiB per device.
+constexpr int64_t kResidualChangeScratchPartials = 131072;
+
+// Device address of that scratch array on the current device (looked up once per device).
+hipError_t residual_change_scratch(void **ptr);
+
 // QK RMSNorm + 3D RoPE and the means of each 64-token block of the stored q', k':
 // [B][H][ceil(N/64)][Dh] fp32.  Inputs with in_token_stride elements between tokens; outputs
 // [B][N][H][Dh] or [B][H][N][Dh] (head_major).  Dh in {16,...,256}, power of two.

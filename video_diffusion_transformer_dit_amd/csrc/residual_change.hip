@@ -13,10 +13,23 @@
 // tile into the caller's workspace; stage 2 reduces each sample's partials
 // in a fixed order.  Every sum has a fixed shape (fp32 over the 8 values of a
 // 16-byte vector, then fp64), so repeated calls give bit-identical results.
+//
+// The allocation-free variant keeps the partials in `scratch`, a 2 MiB array
+// in the library's own device memory (one copy per GPU, held until the
+// process ends).  Its device address is looked up once per device with
+// hipGetSymbolAddress and cached; host code never passes the array's name
+// itself to a kernel (on the host that name is only a stand-in).  Stage 1
+// writes every partial stage 2 reads, so nothing in it has to start at zero.
+#include <mutex>
+
 #include "device_common.hpp"
 #include "launch.hpp"
 
 namespace dit {
+
+// Partials of the allocation-free entry point: B * tiles (num, den) pairs.
+static __device__ __align__(256) double2 scratch[kResidualChangeScratchPartials];
+
 namespace {
 
 constexpr int kPartialThreads = 1024;
@@ -129,7 +142,31 @@ __global__ __launch_bounds__(kFinalThreads) void residual_change_final_kernel(co
     }
 }
 
+constexpr int kMaxScratchDevices = 256;
+std::mutex g_scratch_mutex;
+void *g_scratch_addr[kMaxScratchDevices]; // device address of `scratch`, per device id
+
 } // namespace
+
+hipError_t residual_change_scratch(void **ptr)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    if (dev < 0 || dev >= kMaxScratchDevices)
+        return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_addr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess)
+            return e;
+        g_scratch_addr[dev] = p;
+    }
+    *ptr = g_scratch_addr[dev];
+    return hipSuccess;
+}
 
 int64_t residual_change_tiles(int64_t N, int64_t D) { return (N * (D / 8) + kTileVectors - 1) / kTileVectors; }
 
