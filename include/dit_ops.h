@@ -70,7 +70,7 @@ typedef enum {
     DIT_ERR_SCRATCH = 6 /* sizes beyond a static scratch buffer's capacity */
 } dit_status;
 
-#define DIT_ABI_VERSION 2
+#define DIT_ABI_VERSION 3
 
 /* Human-readable name of a status code; never NULL. */
 const char *dit_status_str(int status);
@@ -163,7 +163,7 @@ dit_status dit_qk_rmsnorm_rope3d(const dit_bf16 *q, const dit_bf16 *k,
 
 /* Output layouts of dit_qk_rmsnorm_rope3d_layout. */
 #define DIT_QK_TOKEN_MAJOR 0 /* [B][N][H][Dh] */
-#define DIT_QK_HEAD_MAJOR 1  /* [B][H][N][Dh] */
+#define DIT_QK_HEAD_MAJOR 1  /* [B][H][N][Dh], head planes out_plane_stride apart */
 
 /*
  * dit_qk_rmsnorm_rope3d with the memory layouts around it made explicit:
@@ -171,6 +171,8 @@ dit_status dit_qk_rmsnorm_rope3d(const dit_bf16 *q, const dit_bf16 *k,
  * fused QKV projection [B][N][3][H][Dh] (q = qkv, k = qkv + H*Dh, stride
  * 3*H*Dh) with no split pass, and q_out, k_out can be written head-major
  * [B][H][N][Dh], the layout an attention kernel reads, with no transpose pass.
+ * Head-major planes may be padded apart (out_plane_stride), so that they do
+ * not all start at the same offset modulo the memory system's interleave.
  * The arithmetic is exactly that of dit_qk_rmsnorm_rope3d.
  * Cited: the Sol-H3 abstract (its search covers memory layouts as well as
  * kernel fusions); xhh.club Q&A for the operation itself.
@@ -179,9 +181,18 @@ dit_status dit_qk_rmsnorm_rope3d(const dit_bf16 *q, const dit_bf16 *k,
  *   in_token_stride  elements between consecutive tokens: a multiple of 8 and
  *                    >= H*Dh (DIT_ERR_SHAPE otherwise)
  *   out_layout       DIT_QK_TOKEN_MAJOR or DIT_QK_HEAD_MAJOR (else DIT_ERR_ARG)
+ *   out_plane_stride head-major: elements from head plane (b, h) to the next,
+ *                    element (b, h, n, i) at (b*H + h) * out_plane_stride +
+ *                    n*Dh + i; 0 selects N*Dh (packed [B][H][N][Dh]); else a
+ *                    multiple of 8 and >= N*Dh (DIT_ERR_SHAPE otherwise), at
+ *                    most 2^40, with the whole output under 2^62 bytes
+ *                    (DIT_ERR_ARG otherwise).  The padding between planes is
+ *                    never read or written.  Token-major: must be 0
+ *                    (DIT_ERR_ARG otherwise)
  *   q_out, k_out     [B][N][H][Dh] or [B][H][N][Dh]; in place (q_out == q,
  *                    k_out == k) only when in_token_stride == H*Dh and the
- *                    layout is token-major; any other overlap is rejected
+ *                    layout is token-major; any other overlap (over the
+ *                    output's whole extent, padding included) is rejected
  * All other arguments and limits as for dit_qk_rmsnorm_rope3d.
  */
 dit_status dit_qk_rmsnorm_rope3d_layout(const dit_bf16 *q, const dit_bf16 *k,
@@ -190,7 +201,8 @@ dit_status dit_qk_rmsnorm_rope3d_layout(const dit_bf16 *q, const dit_bf16 *k,
                                         const int32_t *pos, int64_t B, int64_t N,
                                         int64_t H, int64_t Dh,
                                         int64_t in_token_stride,
-                                        int32_t out_layout, int32_t d_t,
+                                        int32_t out_layout,
+                                        int64_t out_plane_stride, int32_t d_t,
                                         int32_t d_h, int32_t d_w, float theta,
                                         float eps, void *stream);
 
@@ -354,6 +366,7 @@ dit_status dit_subblock_pool(const dit_bf16 *q, const dit_bf16 *k,
  *                    (DIT_QK_HEAD_MAJOR; else DIT_ERR_ARG); q_out == q and
  *                    k_out == k only when in_token_stride == H*Dh and the output
  *                    is token-major; any other overlap DIT_ERR_ARG
+ *   out_plane_stride as for dit_qk_rmsnorm_rope3d_layout
  *   wq, wk, pos      as for dit_qk_rmsnorm_rope3d
  *   q_pooled, k_pooled  fp32 [B][H][ceil(N/64)][Dh], 16-byte aligned,
  *                    overlapping nothing else (DIT_ERR_ARG)
@@ -368,7 +381,8 @@ dit_status dit_qk_rmsnorm_rope3d_pool(const dit_bf16 *q, const dit_bf16 *k,
                                       float *k_pooled, int64_t B, int64_t N,
                                       int64_t H, int64_t Dh,
                                       int64_t in_token_stride,
-                                      int32_t out_layout, int32_t d_t,
+                                      int32_t out_layout,
+                                      int64_t out_plane_stride, int32_t d_t,
                                       int32_t d_h, int32_t d_w, float theta,
                                       float eps, void *stream);
 

@@ -182,9 +182,9 @@ def test_qk_validation(lib):
 
 def test_qk_layout_validation(lib):
     def f(q=P, k=P + 256, qo=R, ko=S, wq=T, wk=U, pos=V, B=1, N=8, H=32, Dh=128, stride=3 * 4096, layout=1,
-          bands=(16, 56, 56), theta=1e4, eps=1e-6):
-        return lib.dit_qk_rmsnorm_rope3d_layout(q, k, qo, ko, wq, wk, pos, B, N, H, Dh, stride, layout, *bands,
-                                                theta, eps, None)
+          plane=0, bands=(16, 56, 56), theta=1e4, eps=1e-6):
+        return lib.dit_qk_rmsnorm_rope3d_layout(q, k, qo, ko, wq, wk, pos, B, N, H, Dh, stride, layout, plane,
+                                                *bands, theta, eps, None)
 
     assert f(stride=-8) == DIT_ERR_ARG
     assert f(layout=2) == DIT_ERR_ARG
@@ -198,6 +198,18 @@ def test_qk_layout_validation(lib):
     assert f(pos=0) == DIT_ERR_NULL
     assert f(q=P + 8) == DIT_ERR_ALIGN
     assert f(q=0, k=0, qo=0, ko=0, wq=0, wk=0, pos=0, N=0) == DIT_OK
+    # head-plane stride: 0 (packed) or a multiple of 8 >= N*Dh = 1024; token-major outputs take only 0
+    assert f(plane=-8) == DIT_ERR_ARG
+    assert f(plane=1016, pos=0) == DIT_ERR_SHAPE  # shorter than a plane
+    assert f(plane=1028, pos=0) == DIT_ERR_SHAPE  # not a multiple of 8
+    assert f(plane=1024, pos=0) == DIT_ERR_NULL and f(plane=1024 + 2048, pos=0) == DIT_ERR_NULL
+    assert f(plane=(1 << 40) + 8) == DIT_ERR_ARG  # past the stride limit
+    assert f(layout=0, stride=4096, plane=4096) == DIT_ERR_ARG
+    assert f(B=1 << 16, N=1, plane=1 << 40) == DIT_ERR_ARG  # the whole output past 2^62 bytes
+    # the padded extent counts for overlaps: 32 planes of 1024 + 1024 padding values = 32 * 4 KiB - 2 KiB bytes
+    assert f(plane=2048, ko=R + 31 * 4096 + 2048 - 16) == DIT_ERR_ARG
+    assert f(plane=2048, ko=R + 31 * 4096 + 2048, pos=0) == DIT_ERR_NULL
+    assert f(plane=2048, q=0, k=0, qo=0, ko=0, wq=0, wk=0, pos=0, N=0) == DIT_OK
 
 
 def test_residual_change_validation(lib):
@@ -287,9 +299,9 @@ def test_subblock_pool_validation(lib):
 def test_qk_pool_validation(lib):
     # B=1, N=128, H=2, Dh=16 (bands 4/6/6): q, k 8 KiB each, pooled 2*2*16 floats
     def f(q=P, k=Q, qo=R, ko=S, wq=T, wk=T + 64, pos=U, qp=V, kp=V + 4096, B=1, N=128, H=2, Dh=16, stride=32,
-          layout=0, bands=(4, 6, 6), theta=1e4, eps=1e-6):
-        return lib.dit_qk_rmsnorm_rope3d_pool(q, k, qo, ko, wq, wk, pos, qp, kp, B, N, H, Dh, stride, layout, *bands,
-                                              theta, eps, None)
+          layout=0, plane=0, bands=(4, 6, 6), theta=1e4, eps=1e-6):
+        return lib.dit_qk_rmsnorm_rope3d_pool(q, k, qo, ko, wq, wk, pos, qp, kp, B, N, H, Dh, stride, layout, plane,
+                                              *bands, theta, eps, None)
 
     assert f(B=-1, qp=0) == DIT_ERR_ARG
     assert f(N=4096 * 64 + 1, qp=0) == DIT_ERR_ARG
@@ -309,6 +321,12 @@ def test_qk_pool_validation(lib):
     assert f(layout=1, qo=P) == DIT_ERR_ARG  # head-major output over its own input is not in place
     assert f(stride=96, qo=P + 64 * 200, k=P + 64) == DIT_ERR_ARG  # inside the strided input's extent
     assert f(q=0, k=0, qo=0, ko=0, wq=0, wk=0, pos=0, qp=0, kp=0, N=0) == DIT_OK
+    # head-plane stride (N*Dh = 2048 values per plane)
+    assert f(plane=2048) == DIT_ERR_ARG  # token-major output with a plane stride
+    assert f(layout=1, plane=2040, qp=0) == DIT_ERR_SHAPE
+    assert f(layout=1, plane=2052, qp=0) == DIT_ERR_SHAPE
+    assert f(layout=1, plane=4096, qp=0) == DIT_ERR_NULL
+    assert f(layout=1, plane=4096, ko=R + 4096 * 2 + 2048 * 2 - 16) == DIT_ERR_ARG  # k_out inside q_out's extent
 
 
 def test_subblock_route_validation(lib):

@@ -392,6 +392,50 @@ def test_qk_layout_fused_qkv(B, N, H, Dh, bands, parts, head_major):
     assert_close(ko, kr, f"k layout {B}x{N}x{H}x{Dh} hm={head_major}")
 
 
+# (B, N, H, Dh, bands, extra values of padding after each head plane)
+QK_PLANE_CASES = [(1, 33, 32, 128, (16, 56, 56), 64), (2, 17, 4, 64, (16, 24, 24), 8), (1, 130, 5, 16, (4, 6, 6), 2048),
+                  (2, 65, 32, 128, (16, 56, 56), 128), (1, 7, 3, 256, (64, 96, 96), 0)]
+
+
+def padded_head_major(B, H, N, Dh, pad):
+    """[B,H,N,Dh] views into [B,H,N*Dh+pad] buffers pre-filled with NaN bits."""
+    buf = torch.full((B, H, N * Dh + pad), float("nan"), dtype=torch.bfloat16, device=DEV)
+    return buf, buf[..., :N * Dh].view(B, H, N, Dh)
+
+
+@pytest.mark.parametrize("B,N,H,Dh,bands,pad", QK_PLANE_CASES)
+@pytest.mark.parametrize("with_means", [False, True])
+def test_qk_head_major_padded_planes(B, N, H, Dh, bands, pad, with_means):
+    """Head planes pad apart: values as the oracle's head-major layout, padding never written."""
+    qkv = randn_bf16((B, N, 3 * H * Dh), seed=N * H + Dh + pad)
+    qkv[..., 2 * H * Dh:] = float("nan")
+    wq, wk = weights(Dh, 161), weights(Dh, 162)
+    pos = random_positions(N, seed=N + 9).to(DEV)
+    qbuf, qv = padded_head_major(B, H, N, Dh, pad)
+    kbuf, kv = padded_head_major(B, H, N, Dh, pad)
+    if with_means:
+        qo, ko, qp, kp = dit.dit_qk_rmsnorm_rope3d_pool(qkv, None, wq, wk, pos, bands, head_major=True, heads=(H, Dh),
+                                                        q_out=qv, k_out=kv)
+        packed = dit.dit_qk_rmsnorm_rope3d_pool(qkv, None, wq, wk, pos, bands, head_major=True, heads=(H, Dh))
+    else:
+        qo, ko = dit.dit_qk_rmsnorm_rope3d_layout(qkv, H, Dh, wq, wk, pos, bands, head_major=True, q_out=qv,
+                                                  k_out=kv)
+        packed = dit.dit_qk_rmsnorm_rope3d_layout(qkv, H, Dh, wq, wk, pos, bands, head_major=True)
+    sync()
+    assert qo.data_ptr() == qv.data_ptr() and ko.data_ptr() == kv.data_ptr()
+    flat = bits(qkv).ravel()
+    qr, kr = oracle.qk_rmsnorm_rope3d_layout(flat, flat[H * Dh:], bits(wq), bits(wk), pos.cpu().numpy(), bands,
+                                             B, N, H, Dh, 3 * H * Dh, 1)
+    assert_close(qv.contiguous(), qr, f"q padded {B}x{N}x{H}x{Dh}+{pad}")
+    assert_close(kv.contiguous(), kr, f"k padded {B}x{N}x{H}x{Dh}+{pad}")
+    # the same bits as the packed layout, and the padding untouched (still NaN bits)
+    assert torch.equal(qv, packed[0]) and torch.equal(kv, packed[1])
+    if with_means:
+        assert torch.equal(qp, packed[2]) and torch.equal(kp, packed[3])
+    for buf in (qbuf, kbuf):
+        assert torch.isnan(buf[..., N * Dh:].float()).all(), "padding between head planes was written"
+
+
 def test_qk_layout_plain_case_equals_qk():
     B, N, H, Dh = 2, 65, 32, 128
     q = randn_bf16((B, N, H, Dh), seed=151)

@@ -28,8 +28,8 @@ SIGNATURES = {
     "dit_swiglu": ([_P, _P, _I64, _I64, _P], ctypes.c_int),
     "dit_qk_rmsnorm_rope3d": ([_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I32, _I32, _I32, _F32, _F32, _P],
                               ctypes.c_int),
-    "dit_qk_rmsnorm_rope3d_layout": ([_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I32, _I32, _I32,
-                                      _I32, _F32, _F32, _P], ctypes.c_int),
+    "dit_qk_rmsnorm_rope3d_layout": ([_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I32, _I64, _I32,
+                                      _I32, _I32, _F32, _F32, _P], ctypes.c_int),
     "dit_gated_residual_adaln": ([_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _F32, _P], ctypes.c_int),
     "dit_residual_change": ([_P, _P, _P, _P, _I64, _I64, _I64, _I64, _P], ctypes.c_int),
     "dit_residual_change_workspace_bytes": ([_I64, _I64, _I64], ctypes.c_int64),
@@ -38,8 +38,8 @@ SIGNATURES = {
     "dit_subblock_scores_ld": ([_I64], ctypes.c_int64),
     "dit_subblock_pool": ([_P, _P, _P, _P, _I64, _I64, _I64, _I64, _I32, _P], ctypes.c_int),
     "dit_subblock_route": ([_P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _P], ctypes.c_int),
-    "dit_qk_rmsnorm_rope3d_pool": ([_P, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I32, _I32,
-                                    _I32, _I32, _F32, _F32, _P], ctypes.c_int),
+    "dit_qk_rmsnorm_rope3d_pool": ([_P, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I32, _I64,
+                                    _I32, _I32, _I32, _F32, _F32, _P], ctypes.c_int),
     "dit_packed_positions": ([_P, _I64, _I64, _I64, _I64, _P], ctypes.c_int),
     "dit_copy16": ([_P, _P, _I64, _P], ctypes.c_int),
 }
@@ -209,13 +209,55 @@ def dit_qk_rmsnorm_rope3d(q, k, wq, wk, pos, bands, q_out=None, k_out=None, thet
 DIT_QK_TOKEN_MAJOR, DIT_QK_HEAD_MAJOR = 0, 1
 
 
+def _qk_outputs(q_out, k_out, shape, head_major: bool, plane_stride, device):
+    """Output tensors of a QK entry point and their head-plane stride argument (0 = packed).
+
+    Token-major outputs are contiguous [B,N,H,Dh].  Head-major outputs are [B,H,N,Dh] views whose head
+    planes may sit ``P`` elements apart (strides (H*P, P, Dh, 1), P >= N*Dh), e.g. slices of a [B,H,P]
+    buffer; given ``plane_stride`` and no outputs, such buffers are allocated and their views returned.
+    """
+    B, A, C, Dh = shape  # head-major: A = H, C = N
+    if plane_stride is not None and not head_major:
+        raise ValueError("plane_stride applies to head-major outputs only")
+    if plane_stride and (plane_stride < C * Dh or plane_stride % 8):
+        raise ValueError(f"plane_stride must be 0 or a multiple of 8 >= N*Dh = {C * Dh}, got {plane_stride}")
+    outs = []
+    for t, name in ((q_out, "q_out"), (k_out, "k_out")):
+        if t is None:
+            if head_major and plane_stride:
+                t = torch.empty((B, A, int(plane_stride)), dtype=torch.bfloat16, device=device)[..., :C * Dh]
+                t = t.view(B, A, C, Dh)
+            else:
+                t = torch.empty(shape, dtype=torch.bfloat16, device=device)
+        outs.append(t)
+    planes = set()
+    for t, name in zip(outs, ("q_out", "k_out")):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.bfloat16 or t.device.type != "cuda":
+            raise TypeError(f"{name} must be a bf16 tensor on a HIP device")
+        _shape(t, name, shape)
+        if t.is_contiguous():
+            planes.add(0)
+            continue
+        st = t.stride()
+        if not head_major or st[3] != 1 or st[2] != Dh or st[1] < C * Dh or st[1] % 8 or st[0] != A * st[1]:
+            raise ValueError(f"{name} must be contiguous, or head-major with strides (H*P, P, Dh, 1), P >= N*Dh "
+                             f"a multiple of 8; got strides {st}")
+        planes.add(st[1])
+    if len(planes) != 1:
+        raise ValueError("q_out and k_out must have the same head-plane stride")
+    P = planes.pop()
+    return outs[0], outs[1], (0 if P == C * Dh else P)
+
+
 def dit_qk_rmsnorm_rope3d_layout(qkv, H: int, Dh: int, wq, wk, pos, bands, head_major: bool = True,
-                                 q_out=None, k_out=None, theta: float = 1e4, eps: float = 1e-6, stream=None):
+                                 q_out=None, k_out=None, plane_stride=None, theta: float = 1e4, eps: float = 1e-6,
+                                 stream=None):
     """Per-head RMSNorm + 3D RoPE of the q and k parts of a fused projection ``qkv`` [B,N,S] whose last
     dimension holds q at [0, H*Dh) and k at [H*Dh, 2*H*Dh) (S >= 2*H*Dh, e.g. 3*H*Dh with v after k).
 
-    Outputs are head-major [B,H,N,Dh] (or token-major [B,N,H,Dh] with ``head_major=False``).
-    Returns (q_out, k_out).
+    Outputs are head-major [B,H,N,Dh] (or token-major [B,N,H,Dh] with ``head_major=False``).  Head-major
+    outputs may have padded head planes: pass views with strides (H*P, P, Dh, 1), or ``plane_stride=P``
+    to allocate them.  Returns (q_out, k_out).
     """
     _tensor(qkv, "qkv", ndim=3)
     B, N, S = qkv.shape
@@ -225,18 +267,15 @@ def dit_qk_rmsnorm_rope3d_layout(qkv, H: int, Dh: int, wq, wk, pos, bands, head_
     _shape(_tensor(wk, "wk"), "wk", (Dh,))
     _shape(_tensor(pos, "pos", dtype=torch.int32), "pos", (N, 3))
     shape = (B, H, N, Dh) if head_major else (B, N, H, Dh)
-    q_out = torch.empty(shape, dtype=qkv.dtype, device=qkv.device) if q_out is None else q_out
-    k_out = torch.empty(shape, dtype=qkv.dtype, device=qkv.device) if k_out is None else k_out
-    _shape(_tensor(q_out, "q_out"), "q_out", shape)
-    _shape(_tensor(k_out, "k_out"), "k_out", shape)
+    q_out, k_out, plane = _qk_outputs(q_out, k_out, shape, head_major, plane_stride, qkv.device)
     d_t, d_h, d_w = (int(b) for b in bands)
     dev = _same_device(qkv, wq, wk, pos, q_out, k_out)
     k_ptr = qkv.data_ptr() + H * Dh * qkv.element_size()
     with torch.cuda.device(dev):
         _check("dit_qk_rmsnorm_rope3d_layout", load_library().dit_qk_rmsnorm_rope3d_layout(
             qkv.data_ptr(), k_ptr, q_out.data_ptr(), k_out.data_ptr(), wq.data_ptr(), wk.data_ptr(), pos.data_ptr(),
-            B, N, H, Dh, S, DIT_QK_HEAD_MAJOR if head_major else DIT_QK_TOKEN_MAJOR, d_t, d_h, d_w, float(theta),
-            float(eps), _stream(stream, dev)))
+            B, N, H, Dh, S, DIT_QK_HEAD_MAJOR if head_major else DIT_QK_TOKEN_MAJOR, plane, d_t, d_h, d_w,
+            float(theta), float(eps), _stream(stream, dev)))
     return q_out, k_out
 
 
@@ -331,13 +370,14 @@ def dit_subblock_pool(q, k, head_major: bool = False, q_pooled=None, k_pooled=No
 
 
 def dit_qk_rmsnorm_rope3d_pool(q, k, wq, wk, pos, bands, head_major: bool = False, q_out=None, k_out=None,
-                               q_pooled=None, k_pooled=None, heads=None, theta: float = 1e4, eps: float = 1e-6,
-                               stream=None):
+                               q_pooled=None, k_pooled=None, heads=None, plane_stride=None, theta: float = 1e4,
+                               eps: float = 1e-6, stream=None):
     """QK RMSNorm + 3D RoPE plus the 64-token block means of its stored outputs.
 
     Inputs: q, k bf16 [B,N,H,Dh]; or, with ``k=None`` and ``heads=(H, Dh)``, q is a fused projection
     [B,N,S] holding q at [0, H*Dh) and k at [H*Dh, 2*H*Dh) of each token.  Outputs q', k' are
-    [B,N,H,Dh], or [B,H,N,Dh] with ``head_major=True``; the means are fp32 [B,H,nb,Dh], nb = ceil(N/64).
+    [B,N,H,Dh], or [B,H,N,Dh] with ``head_major=True`` (head planes optionally padded apart, as for
+    dit_qk_rmsnorm_rope3d_layout); the means are fp32 [B,H,nb,Dh], nb = ceil(N/64).
     Returns (q_out, k_out, q_pooled, k_pooled).
     """
     if k is None:
@@ -358,10 +398,7 @@ def dit_qk_rmsnorm_rope3d_pool(q, k, wq, wk, pos, bands, head_major: bool = Fals
     _shape(_tensor(wk, "wk"), "wk", (Dh,))
     _shape(_tensor(pos, "pos", dtype=torch.int32), "pos", (N, 3))
     shape = (B, H, N, Dh) if head_major else (B, N, H, Dh)
-    q_out = torch.empty(shape, dtype=torch.bfloat16, device=q.device) if q_out is None else q_out
-    k_out = torch.empty(shape, dtype=torch.bfloat16, device=q.device) if k_out is None else k_out
-    _shape(_tensor(q_out, "q_out"), "q_out", shape)
-    _shape(_tensor(k_out, "k_out"), "k_out", shape)
+    q_out, k_out, plane = _qk_outputs(q_out, k_out, shape, head_major, plane_stride, q.device)
     nb = -(-N // DIT_SUBBLOCK_TOKENS)
     pshape = (B, H, nb, Dh)
     q_pooled = torch.empty(pshape, dtype=torch.float32, device=q.device) if q_pooled is None else q_pooled
@@ -374,7 +411,7 @@ def dit_qk_rmsnorm_rope3d_pool(q, k, wq, wk, pos, bands, head_major: bool = Fals
         _check("dit_qk_rmsnorm_rope3d_pool", load_library().dit_qk_rmsnorm_rope3d_pool(
             q_ptr, k_ptr, q_out.data_ptr(), k_out.data_ptr(), wq.data_ptr(), wk.data_ptr(), pos.data_ptr(),
             q_pooled.data_ptr(), k_pooled.data_ptr(), B, N, H, Dh, stride,
-            DIT_QK_HEAD_MAJOR if head_major else DIT_QK_TOKEN_MAJOR, d_t, d_h, d_w, float(theta), float(eps),
+            DIT_QK_HEAD_MAJOR if head_major else DIT_QK_TOKEN_MAJOR, plane, d_t, d_h, d_w, float(theta), float(eps),
             _stream(stream, dev)))
     return q_out, k_out, q_pooled, k_pooled
 

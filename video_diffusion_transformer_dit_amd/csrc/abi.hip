@@ -58,6 +58,36 @@ int64_t row_count(int64_t a, int64_t b)
 
 dit_status launched(hipError_t e) { return e == hipSuccess ? DIT_OK : DIT_ERR_HIP; }
 
+// Largest head-plane stride of a head-major QK output (elements).
+constexpr int64_t kMaxPlaneStride = int64_t(1) << 40;
+
+// Resolved head-plane stride of a QK output (0 selects N*Dh, the packed
+// layout; token-major outputs take only 0), or a status: DIT_ERR_ARG for a
+// negative or oversized stride, a stride with a token-major output, or an
+// output extent past 2^62 bytes; DIT_ERR_SHAPE for a stride that is not a
+// multiple of 8 or is shorter than a plane.
+dit_status plane_stride(int64_t requested, int32_t out_layout, int64_t B, int64_t N, int64_t H, int64_t Dh,
+                        int64_t *plane)
+{
+    if (requested < 0 || requested > kMaxPlaneStride || (out_layout == DIT_QK_TOKEN_MAJOR && requested != 0))
+        return DIT_ERR_ARG;
+    *plane = requested == 0 ? N * Dh : requested;
+    if (out_layout == DIT_QK_HEAD_MAJOR && (*plane % 8 != 0 || *plane < N * Dh))
+        return DIT_ERR_SHAPE;
+    const int64_t planes = B * H; // B < 2^24, H <= 2^16: no overflow
+    if (planes > 1 && *plane > ((int64_t(1) << 61) - N * Dh) / (planes - 1))
+        return DIT_ERR_ARG;
+    return DIT_OK;
+}
+
+// Bytes from the first to one past the last element of a QK output.
+int64_t qk_out_extent(int32_t out_layout, int64_t B, int64_t N, int64_t H, int64_t Dh, int64_t plane)
+{
+    if (out_layout == DIT_QK_TOKEN_MAJOR || B * N == 0)
+        return B * N * H * Dh * 2;
+    return ((B * H - 1) * plane + N * Dh) * 2;
+}
+
 } // namespace
 
 extern "C" {
@@ -144,8 +174,8 @@ dit_status dit_swiglu(const dit_bf16 *in, dit_bf16 *out, int64_t M, int64_t F, v
 dit_status dit_qk_rmsnorm_rope3d_layout(const dit_bf16 *q, const dit_bf16 *k, dit_bf16 *q_out, dit_bf16 *k_out,
                                         const dit_bf16 *wq, const dit_bf16 *wk, const int32_t *pos, int64_t B,
                                         int64_t N, int64_t H, int64_t Dh, int64_t in_token_stride,
-                                        int32_t out_layout, int32_t d_t, int32_t d_h, int32_t d_w, float theta,
-                                        float eps, void *stream)
+                                        int32_t out_layout, int64_t out_plane_stride, int32_t d_t, int32_t d_h,
+                                        int32_t d_w, float theta, float eps, void *stream)
 {
     const int64_t rows = row_count(B, N);
     if (rows < 0 || H < 0 || Dh < 0 || in_token_stride < 0 || in_token_stride > kMaxWidth)
@@ -156,6 +186,10 @@ dit_status dit_qk_rmsnorm_rope3d_layout(const dit_bf16 *q, const dit_bf16 *k, di
     if (!dh_ok || H < 1 || H * Dh > kMaxHeadRow || d_t < 0 || d_h < 0 || d_w < 0 || (d_t | d_h | d_w) & 1 ||
         (int64_t)d_t + d_h + d_w != Dh || in_token_stride % 8 != 0 || in_token_stride < H * Dh)
         return DIT_ERR_SHAPE;
+    int64_t plane = 0;
+    const dit_status ps = plane_stride(out_plane_stride, out_layout, B, N, H, Dh, &plane);
+    if (ps != DIT_OK)
+        return ps;
     if (!(eps > 0.f) || !isfinite(eps) || !(theta > 1.f) || !isfinite(theta))
         return DIT_ERR_ARG;
     if (rows == 0)
@@ -165,8 +199,8 @@ dit_status dit_qk_rmsnorm_rope3d_layout(const dit_bf16 *q, const dit_bf16 *k, di
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(q_out, 16) || !aligned(k_out, 16) || !aligned(wq, 16) ||
         !aligned(wk, 16) || !aligned(pos, 4))
         return DIT_ERR_ALIGN;
-    const int64_t nt = rows * H * Dh * 2;                          // bytes of each output
-    const int64_t ni = ((rows - 1) * in_token_stride + H * Dh) * 2; // byte extent of each input
+    const int64_t nt = qk_out_extent(out_layout, B, N, H, Dh, plane); // byte extent of each output
+    const int64_t ni = ((rows - 1) * in_token_stride + H * Dh) * 2;   // byte extent of each input
     const int64_t nw = Dh * 2, np = N * 12;
     // In place (q_out == q, k_out == k) only where the layouts coincide.
     const bool same_layout = in_token_stride == H * Dh && out_layout == DIT_QK_TOKEN_MAJOR;
@@ -180,7 +214,7 @@ dit_status dit_qk_rmsnorm_rope3d_layout(const dit_bf16 *q, const dit_bf16 *k, di
         if (overlap(q_out, nt, small[i], small_n[i]) || overlap(k_out, nt, small[i], small_n[i]))
             return DIT_ERR_ARG;
     return launched(dit::launch_qk_rmsnorm_rope3d(q, k, q_out, k_out, wq, wk, pos, rows, N, H, Dh, in_token_stride,
-                                                  out_layout == DIT_QK_HEAD_MAJOR, d_t, d_h, d_w, theta, eps,
+                                                  out_layout == DIT_QK_HEAD_MAJOR, plane, d_t, d_h, d_w, theta, eps,
                                                   (hipStream_t)stream));
 }
 
@@ -192,8 +226,8 @@ dit_status dit_qk_rmsnorm_rope3d(const dit_bf16 *q, const dit_bf16 *k, dit_bf16 
     // Token-major q and k in, token-major out: the layout entry point with the plain layout.
     if (H < 0 || Dh < 0 || H > kMaxHeadRow || Dh > kMaxHeadRow)
         return H < 0 || Dh < 0 ? DIT_ERR_ARG : DIT_ERR_SHAPE;
-    return dit_qk_rmsnorm_rope3d_layout(q, k, q_out, k_out, wq, wk, pos, B, N, H, Dh, H * Dh, DIT_QK_TOKEN_MAJOR, d_t,
-                                        d_h, d_w, theta, eps, stream);
+    return dit_qk_rmsnorm_rope3d_layout(q, k, q_out, k_out, wq, wk, pos, B, N, H, Dh, H * Dh, DIT_QK_TOKEN_MAJOR, 0,
+                                        d_t, d_h, d_w, theta, eps, stream);
 }
 
 dit_status dit_gated_residual_adaln(const dit_bf16 *x, const dit_bf16 *y, const dit_bf16 *gate, const dit_bf16 *shift,
@@ -351,8 +385,8 @@ dit_status dit_subblock_pool(const dit_bf16 *q, const dit_bf16 *k, float *q_pool
 dit_status dit_qk_rmsnorm_rope3d_pool(const dit_bf16 *q, const dit_bf16 *k, dit_bf16 *q_out, dit_bf16 *k_out,
                                       const dit_bf16 *wq, const dit_bf16 *wk, const int32_t *pos, float *q_pooled,
                                       float *k_pooled, int64_t B, int64_t N, int64_t H, int64_t Dh,
-                                      int64_t in_token_stride, int32_t out_layout, int32_t d_t, int32_t d_h,
-                                      int32_t d_w, float theta, float eps, void *stream)
+                                      int64_t in_token_stride, int32_t out_layout, int64_t out_plane_stride,
+                                      int32_t d_t, int32_t d_h, int32_t d_w, float theta, float eps, void *stream)
 {
     if (B < 0 || N < 0 || H < 0 || Dh < 0 || B > kMaxSamples || N > kMaxSubBlocks * DIT_SUBBLOCK_TOKENS ||
         in_token_stride < 0 || in_token_stride > kMaxWidth)
@@ -362,6 +396,10 @@ dit_status dit_qk_rmsnorm_rope3d_pool(const dit_bf16 *q, const dit_bf16 *k, dit_
     if (!subblock_head_ok(H, Dh) || d_t < 0 || d_h < 0 || d_w < 0 || (d_t | d_h | d_w) & 1 ||
         (int64_t)d_t + d_h + d_w != Dh || in_token_stride % 8 != 0 || in_token_stride < H * Dh)
         return DIT_ERR_SHAPE;
+    int64_t plane = 0;
+    const dit_status ps = plane_stride(out_plane_stride, out_layout, B, N, H, Dh, &plane);
+    if (ps != DIT_OK)
+        return ps;
     if (!(eps > 0.f) || !isfinite(eps) || !(theta > 1.f) || !isfinite(theta))
         return DIT_ERR_ARG;
     if (B == 0 || N == 0)
@@ -373,8 +411,8 @@ dit_status dit_qk_rmsnorm_rope3d_pool(const dit_bf16 *q, const dit_bf16 *k, dit_
         return DIT_ERR_ALIGN;
     const int64_t rows = B * N;
     const int64_t nb = (N + DIT_SUBBLOCK_TOKENS - 1) / DIT_SUBBLOCK_TOKENS;
-    const int64_t nt = rows * H * Dh * 2;                          // bytes of each output
-    const int64_t ni = ((rows - 1) * in_token_stride + H * Dh) * 2; // byte extent of each input
+    const int64_t nt = qk_out_extent(out_layout, B, N, H, Dh, plane); // byte extent of each output
+    const int64_t ni = ((rows - 1) * in_token_stride + H * Dh) * 2;   // byte extent of each input
     const int64_t npool = B * H * nb * Dh * 4, nw = Dh * 2, np = N * 12;
     // q' may overwrite q and k' k exactly, where the two layouts coincide; the
     // inputs may share a buffer (fused QKV); nothing else overlaps.
@@ -396,8 +434,8 @@ dit_status dit_qk_rmsnorm_rope3d_pool(const dit_bf16 *q, const dit_bf16 *k, dit_
                 return DIT_ERR_ARG;
     }
     return launched(dit::launch_qk_rmsnorm_rope3d_pool(q, k, q_out, k_out, wq, wk, pos, q_pooled, k_pooled, B, N, H,
-                                                       Dh, in_token_stride, out_layout == DIT_QK_HEAD_MAJOR, d_t, d_h,
-                                                       d_w, theta, eps, (hipStream_t)stream));
+                                                       Dh, in_token_stride, out_layout == DIT_QK_HEAD_MAJOR, plane,
+                                                       d_t, d_h, d_w, theta, eps, (hipStream_t)stream));
 }
 
 dit_status dit_subblock_route(const float *q_pooled, const float *k_pooled, float *scores, int32_t *kept, int64_t B,

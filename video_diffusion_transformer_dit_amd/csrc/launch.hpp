@@ -27,11 +27,12 @@ hipError_t launch_swiglu(const void *in, void *out, int64_t M, int64_t F, hipStr
 
 // Per-head RMSNorm + 3D RoPE of q and k; Dh in {8,...,256} (power of two).  Inputs have
 // in_token_stride elements (a multiple of 8, >= H*Dh) between consecutive tokens; outputs are
-// [B][N][H][Dh], or [B][H][N][Dh] when head_major.
+// [B][N][H][Dh], or [B][H][N][Dh] when head_major, with out_plane_stride elements (a multiple
+// of 8, >= N*Dh) between consecutive head planes.
 hipError_t launch_qk_rmsnorm_rope3d(const void *q, const void *k, void *q_out, void *k_out,
                                     const void *wq, const void *wk, const int32_t *pos,
                                     int64_t rows, int64_t N, int64_t H, int64_t Dh,
-                                    int64_t in_token_stride, bool head_major,
+                                    int64_t in_token_stride, bool head_major, int64_t out_plane_stride,
                                     int d_t, int d_h, int d_w, float theta, float eps,
                                     hipStream_t stream);
 
@@ -56,12 +57,13 @@ hipError_t residual_change_scratch(void **ptr);
 
 // QK RMSNorm + 3D RoPE and the means of each 64-token block of the stored q', k':
 // [B][H][ceil(N/64)][Dh] fp32.  Inputs with in_token_stride elements between tokens; outputs
-// [B][N][H][Dh] or [B][H][N][Dh] (head_major).  Dh in {16,...,256}, power of two.
+// [B][N][H][Dh] or [B][H][N][Dh] (head_major, out_plane_stride elements between head planes).
+// Dh in {16,...,256}, power of two.
 hipError_t launch_qk_rmsnorm_rope3d_pool(const void *q, const void *k, void *q_out, void *k_out, const void *wq,
                                          const void *wk, const int32_t *pos, float *q_pooled, float *k_pooled,
                                          int64_t B, int64_t N, int64_t H, int64_t Dh, int64_t in_token_stride,
-                                         bool head_major, int d_t, int d_h, int d_w, float theta, float eps,
-                                         hipStream_t stream);
+                                         bool head_major, int64_t out_plane_stride, int d_t, int d_h, int d_w,
+                                         float theta, float eps, hipStream_t stream);
 
 // Means of each 64-token block of q and of k, per sample and head: [B][H][ceil(N/64)][Dh] fp32.
 // Inputs [B][N][H][Dh] (token-major) or [B][H][N][Dh] (head_major); Dh in {16,...,256}, power of two.

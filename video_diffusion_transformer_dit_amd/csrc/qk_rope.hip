@@ -151,9 +151,10 @@ __global__ __launch_bounds__(kQKThreads) void qk_rmsnorm_rope3d_kernel(
                       tid, kQKThreads, o);
 }
 
-// Head-major outputs [B][H][N][Dh].  Each head's q' (or k') is a plane of
-// N * Dh contiguous values, and at 1344x768 5 s a plane is 1953 * 16 KiB, so
-// the planes all start at the same offset modulo 4 KiB.  Writing one token's
+// Head-major outputs [B][H][N][Dh], head plane (b, h) starting `plane`
+// vectors after plane (b, h - 1) (plane = N * Dh / 8 when packed).  Packed,
+// at 1344x768 5 s a plane is 1953 * 16 KiB, so the planes all start at the
+// same offset modulo 4 KiB; a caller-chosen plane stride can pad that away.  Writing one token's
 // heads with one store instruction (as the token-major mapping does) then
 // sends its 256-byte pieces to the same offset in several planes at once,
 // which measured 13-18% slower than token-major output.  Here a workgroup
@@ -171,7 +172,7 @@ template <int LPH>
 __global__ __launch_bounds__(kQKThreads) void qk_rmsnorm_rope3d_head_major_kernel(
     const u32x4 *q, const u32x4 *k, u32x4 *q_out, u32x4 *k_out, const u32x4 *__restrict__ wq,
     const u32x4 *__restrict__ wk, const int32_t *__restrict__ pos, int N, int B, int H, int VPR, int64_t in_stride,
-    int half_parts, int rows, float inv_dh, float eps, const RotaryPlan plan)
+    int64_t plane, int half_parts, int rows, float inv_dh, float eps, const RotaryPlan plan)
 {
     constexpr int kPairs = 4 * LPH;
     __shared__ float2 rot[kHmTokens * kPairs];
@@ -239,7 +240,7 @@ __global__ __launch_bounds__(kQKThreads) void qk_rmsnorm_rope3d_head_major_kerne
         if (col < VPR && r < (unsigned)rows) {
             const int h = col / LPH;
             const unsigned b = B == 1 ? 0u : r / (unsigned)N, n = B == 1 ? r : r % (unsigned)N;
-            store_stream((which ? k_out : q_out) + ((size_t)(b * (unsigned)H + h) * N + n) * LPH + s,
+            store_stream((which ? k_out : q_out) + ((size_t)b * (unsigned)H + h) * plane + (size_t)n * LPH + s,
                          stage[t][hl * LPH + s]);
         }
     }
@@ -286,13 +287,15 @@ constexpr int kQKPoolTokens = 64; // SubBlock block size
 
 // in_stride = vectors from one token's q (or k) to the next token's (C for
 // contiguous inputs, more for q and k inside a fused QKV projection).
-// HEAD_MAJOR: q', k' written [B][H][N][Dh]; the workgroup's 64 tokens of a head
-// are then 64 * Dh contiguous values of its plane.
+// HEAD_MAJOR: q', k' written [B][H][N][Dh] with `plane` vectors between head
+// planes; the workgroup's 64 tokens of a head are then 64 * Dh contiguous
+// values of its plane.
 template <int LPH, bool HEAD_MAJOR>
 __global__ __launch_bounds__(kQKPoolWaves * kWave) void qk_rmsnorm_rope3d_pool_kernel(
     const u32x4 *q, const u32x4 *k, u32x4 *q_out, u32x4 *k_out, const u32x4 *__restrict__ wq,
     const u32x4 *__restrict__ wk, const int32_t *__restrict__ pos, float *__restrict__ qp, float *__restrict__ kp,
-    int N, int nb, int C, int64_t in_stride, int chunks, float inv_dh, float eps, const RotaryPlan plan)
+    int N, int nb, int C, int64_t in_stride, int64_t plane, int chunks, float inv_dh, float eps,
+    const RotaryPlan plan)
 {
     constexpr int kPerWave = kQKPoolTokens / kQKPoolWaves;
     constexpr int kPairs = 4 * LPH;                       // channel pairs per head
@@ -324,7 +327,7 @@ __global__ __launch_bounds__(kQKPoolWaves * kWave) void qk_rmsnorm_rope3d_pool_k
     const size_t row0 = (size_t)b * N + n0;
     const int H = C / LPH, h = c / LPH;
     // output vector of token n0 + n: token-major row, or the head's plane
-    const size_t out0 = HEAD_MAJOR ? (((size_t)b * H + h) * N + n0) * LPH + slot : row0 * C + c;
+    const size_t out0 = HEAD_MAJOR ? ((size_t)b * H + h) * plane + (size_t)n0 * LPH + slot : row0 * C + c;
     const size_t out_step = HEAD_MAJOR ? LPH : C;
     u32x4 raw[kPerWave];
 #pragma unroll
@@ -401,32 +404,33 @@ __global__ __launch_bounds__(kQKPoolWaves * kWave) void qk_rmsnorm_rope3d_pool_k
 template <int LPH>
 hipError_t launch_pool_lph(const u32x4 *q, const u32x4 *k, u32x4 *qo, u32x4 *ko, const u32x4 *wq, const u32x4 *wk,
                            const int32_t *pos, float *qp, float *kp, int B, int N, int C, int64_t in_stride,
-                           bool head_major, float inv_dh, float eps, const RotaryPlan &plan, hipStream_t stream)
+                           bool head_major, int64_t plane, float inv_dh, float eps, const RotaryPlan &plan,
+                           hipStream_t stream)
 {
     const int nb = (N + kQKPoolTokens - 1) / kQKPoolTokens;
     const int chunks = (C + kWave - 1) / kWave;
     const dim3 grid((unsigned)(chunks * nb), 2u, (unsigned)B), block(kQKPoolWaves * kWave);
     if (head_major)
         hipLaunchKernelGGL((qk_rmsnorm_rope3d_pool_kernel<LPH, true>), grid, block, 0, stream, q, k, qo, ko, wq, wk,
-                           pos, qp, kp, N, nb, C, in_stride, chunks, inv_dh, eps, plan);
+                           pos, qp, kp, N, nb, C, in_stride, plane, chunks, inv_dh, eps, plan);
     else
         hipLaunchKernelGGL((qk_rmsnorm_rope3d_pool_kernel<LPH, false>), grid, block, 0, stream, q, k, qo, ko, wq, wk,
-                           pos, qp, kp, N, nb, C, in_stride, chunks, inv_dh, eps, plan);
+                           pos, qp, kp, N, nb, C, in_stride, plane, chunks, inv_dh, eps, plan);
     return hipGetLastError();
 }
 
 template <int LPH>
 hipError_t launch_lph(const u32x4 *q, const u32x4 *k, u32x4 *qo, u32x4 *ko, const u32x4 *wq, const u32x4 *wk,
                       const int32_t *pos, int rows, int N, int H, int VPR, int64_t in_stride, bool head_major,
-                      float inv_dh, float eps, const RotaryPlan &plan, hipStream_t stream)
+                      int64_t plane, float inv_dh, float eps, const RotaryPlan &plan, hipStream_t stream)
 {
     const int half_parts = (VPR + kQKThreads - 1) / kQKThreads;
     const dim3 block(kQKThreads);
     if (head_major)
         hipLaunchKernelGGL((qk_rmsnorm_rope3d_head_major_kernel<LPH>),
                            dim3((unsigned)((rows + kHmTokens - 1) / kHmTokens), (unsigned)(2 * half_parts)), block, 0,
-                           stream, q, k, qo, ko, wq, wk, pos, N, rows / N, H, VPR, in_stride, half_parts, rows, inv_dh,
-                           eps, plan);
+                           stream, q, k, qo, ko, wq, wk, pos, N, rows / N, H, VPR, in_stride, plane, half_parts, rows,
+                           inv_dh, eps, plan);
     else
         hipLaunchKernelGGL((qk_rmsnorm_rope3d_kernel<LPH>), dim3((unsigned)rows, (unsigned)(2 * half_parts)), block, 0,
                            stream, q, k, qo, ko, wq, wk, pos, N, rows / N, H, VPR, in_stride, half_parts, inv_dh, eps,
@@ -438,8 +442,8 @@ hipError_t launch_lph(const u32x4 *q, const u32x4 *k, u32x4 *qo, u32x4 *ko, cons
 
 hipError_t launch_qk_rmsnorm_rope3d(const void *q, const void *k, void *q_out, void *k_out, const void *wq,
                                     const void *wk, const int32_t *pos, int64_t rows, int64_t N, int64_t H,
-                                    int64_t Dh, int64_t in_token_stride, bool head_major, int d_t, int d_h, int d_w,
-                                    float theta, float eps, hipStream_t stream)
+                                    int64_t Dh, int64_t in_token_stride, bool head_major, int64_t out_plane_stride,
+                                    int d_t, int d_h, int d_w, float theta, float eps, hipStream_t stream)
 {
     const auto *qv = static_cast<const u32x4 *>(q);
     const auto *kv = static_cast<const u32x4 *>(k);
@@ -449,11 +453,13 @@ hipError_t launch_qk_rmsnorm_rope3d(const void *q, const void *k, void *q_out, v
     const auto *wkv = static_cast<const u32x4 *>(wk);
     const int VPR = (int)(H * Dh / 8);
     const int64_t in_stride = in_token_stride / 8;
+    const int64_t plane = out_plane_stride / 8;
     const float inv_dh = 1.f / (float)Dh;
     const int r = (int)rows, n = (int)N, h = (int)H;
 
     const RotaryPlan plan = make_rotary_plan(Dh, d_t, d_h, d_w, theta);
-#define DIT_QK_LAUNCH(L) launch_lph<L>(qv, kv, qo, ko, wqv, wkv, pos, r, n, h, VPR, in_stride, head_major, inv_dh, eps, plan, stream)
+#define DIT_QK_LAUNCH(L)                                                                                             \
+    launch_lph<L>(qv, kv, qo, ko, wqv, wkv, pos, r, n, h, VPR, in_stride, head_major, plane, inv_dh, eps, plan, stream)
     switch (Dh) {
     case 8: return DIT_QK_LAUNCH(1);
     case 16: return DIT_QK_LAUNCH(2);
@@ -469,8 +475,8 @@ hipError_t launch_qk_rmsnorm_rope3d(const void *q, const void *k, void *q_out, v
 hipError_t launch_qk_rmsnorm_rope3d_pool(const void *q, const void *k, void *q_out, void *k_out, const void *wq,
                                          const void *wk, const int32_t *pos, float *q_pooled, float *k_pooled,
                                          int64_t B, int64_t N, int64_t H, int64_t Dh, int64_t in_token_stride,
-                                         bool head_major, int d_t, int d_h, int d_w, float theta, float eps,
-                                         hipStream_t stream)
+                                         bool head_major, int64_t out_plane_stride, int d_t, int d_h, int d_w,
+                                         float theta, float eps, hipStream_t stream)
 {
     const auto *qv = static_cast<const u32x4 *>(q);
     const auto *kv = static_cast<const u32x4 *>(k);
@@ -483,9 +489,10 @@ hipError_t launch_qk_rmsnorm_rope3d_pool(const void *q, const void *k, void *q_o
     const RotaryPlan plan = make_rotary_plan(Dh, d_t, d_h, d_w, theta);
     const int b = (int)B, n = (int)N;
     const int64_t in_stride = in_token_stride / 8;
+    const int64_t plane = out_plane_stride / 8;
 #define DIT_QK_POOL_LAUNCH(L)                                                                                        \
-    launch_pool_lph<L>(qv, kv, qo, ko, wqv, wkv, pos, q_pooled, k_pooled, b, n, C, in_stride, head_major, inv_dh, eps, \
-                       plan, stream)
+    launch_pool_lph<L>(qv, kv, qo, ko, wqv, wkv, pos, q_pooled, k_pooled, b, n, C, in_stride, head_major, plane,      \
+                       inv_dh, eps, plan, stream)
     switch (Dh) {
     case 16: return DIT_QK_POOL_LAUNCH(2);
     case 32: return DIT_QK_POOL_LAUNCH(4);
