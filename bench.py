@@ -107,6 +107,14 @@ def op_bytes(wl, next_rows: bool = False) -> dict:
             "pool_hm": 2 * R * H * Dh * 2 + pooled,
             "scores": pooled + B * H * nb * nb * 4,            # means in, fp32 scores out
             "topk": B * H * nb * nb * 4 + B * H * nb * keep * 4,  # scores in, kept indices out
+            # access-pattern streams (one launch each; the head-major copy moves one of q, k)
+            "p_read": R * 4 * F,
+            "p_write": R * 2 * F,
+            "p_swiglu": R * 6 * F,
+            "p_residual": R * 6 * D,
+            "p_adaln": R * 4 * D,
+            "p_residual_adaln": R * 8 * D,
+            "p_head_major": R * 4 * H * Dh,
         })
     return out
 
@@ -556,6 +564,11 @@ def main(argv=None) -> int:
                     "memcpy_dtod_GB_s": round(2 * cbytes / (memcpy_ms * 1e-3) / 1e9, 1)}
     del src, dst
 
+    # Access-pattern ceilings: each kernel's traffic with no arithmetic, in that
+    # kernel's own launch shape (dit_stream_pattern), on buffers of the same
+    # sizes; the chain's outputs are left intact for the oracle check below.
+    ceilings = pattern_ceilings(dit, wl, ins, ops, fused_ms, layout_ms, timed, dev)
+
     mix_ms = 2 * ops["adaln"]["avg_ms"] + ops["qk"]["avg_ms"] + 2 * ops["residual"]["avg_ms"] + ops["swiglu"]["avg_ms"]
     mix_bytes = 2 * nbytes["adaln"] + nbytes["qk"] + 2 * nbytes["residual"] + nbytes["swiglu"]
     block_mix = {"ops": "2 adaln + qk + 2 residual + swiglu (kernel-time sum)", "ms": round(mix_ms, 4),
@@ -614,6 +627,7 @@ def main(argv=None) -> int:
         "ops_flushed": flushed,
         "roofline": roofline,
         "copy_ceiling": copy_ceiling,
+        "ceilings": ceilings,
         "graph_replay": graph_replay,
         "block_mix": block_mix,
         "next_fused_residual_adaln": fused,
@@ -629,20 +643,79 @@ def main(argv=None) -> int:
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, ins, {"y": y, "out": out, "sw": sw, "qo": qo, "ko": ko,
                                                         "fz": fused_z}, args.cpu_seconds)
-    # A figure is only credited to kernels whose outputs were checked: when the
-    # oracle check or a consistency check fails, `value` is null and the exit
-    # status is non-zero.  Without the oracle leg the line says it is unchecked.
-    checked = "cpu_baseline" in result
-    ok = all(consistency.values()) and (not checked or result["cpu_baseline"]["parity_ok"])
-    result["parity_checked"] = checked
-    result["parity_ok"] = bool(ok) if checked else None
+    ok = gate_on_parity(result, consistency)
     if not ok:
-        result["value_if_parity_held"] = result["value"]
-        result["value"] = None
         print("[bench] FAILED: GPU outputs disagree with the oracle or with each other; value withheld",
               file=sys.stderr, flush=True)
     print(json.dumps(result), flush=True)
     return 0 if ok else 3
+
+
+def gate_on_parity(result: dict, consistency: dict) -> bool:
+    """Credit a figure only to kernels whose outputs were checked.
+
+    Sets `parity_checked` (the oracle leg ran) and `parity_ok` (null when unchecked).  When the oracle check
+    or a consistency check fails, `value` becomes null (the figure moves to `value_if_parity_held`) and the
+    return is False, which main() turns into a non-zero exit status.
+    """
+    checked = "cpu_baseline" in result
+    ok = all(consistency.values()) and (not checked or bool(result["cpu_baseline"]["parity_ok"]))
+    result["parity_checked"] = checked
+    result["parity_ok"] = ok if checked else None
+    if not ok:
+        result["value_if_parity_held"] = result["value"]
+        result["value"] = None
+    return ok
+
+
+def pattern_ceilings(dit, wl, ins, ops, fused_ms: float, layout_ms: float, timed, dev) -> dict:
+    """Each kernel's memory traffic with no arithmetic, in its own launch shape, timed as the kernels are.
+
+    `kernel_over_pattern` is the kernel's average duration over its pattern's: 1.0 means the kernel moves
+    its bytes as fast as a stream of the same shape with nothing to compute.
+    """
+    import torch
+
+    R, D, F, H, Dh = wl.R, wl.D, wl.F, wl.H, wl.Dh
+    HD = H * Dh
+    swiglu_out = torch.empty((R, F), dtype=torch.bfloat16, device=dev)
+    o1 = torch.empty((R, D), dtype=torch.bfloat16, device=dev)
+    o2 = torch.empty_like(o1)
+    sink = torch.empty(16, dtype=torch.uint8, device=dev)
+    q, k = ins["q"].reshape(R, HD), ins["k"].reshape(R, HD)
+    qo, ko = torch.empty_like(q), torch.empty_like(k)
+    a, b = ins["res_x"].reshape(R, D), ins["res_y"].reshape(R, D)
+    sp = dit.dit_stream_pattern
+    cases = {
+        # name: (launch, bytes, kernel ms it bounds or None)
+        "read": (lambda: sp(dit.DIT_STREAM_READ, R, 4 * F, in0=ins["swiglu_in"], out0=sink), R * 4 * F, None),
+        "write": (lambda: sp(dit.DIT_STREAM_WRITE, R, 2 * F, out0=swiglu_out), R * 2 * F, None),
+        "swiglu_shape": (lambda: sp(dit.DIT_STREAM_SPLIT_ROWS, R, 2 * F, in0=ins["swiglu_in"], out0=swiglu_out),
+                         R * 6 * F, ops["swiglu"]["avg_ms"]),
+        "residual_shape": (lambda: sp(dit.DIT_STREAM_TWO_IN, R, 2 * D, in0=a, in1=b, out0=o1), R * 6 * D,
+                           ops["residual"]["avg_ms"]),
+        "adaln_shape": (lambda: sp(dit.DIT_STREAM_ROW_WAVE, R, 2 * D, in0=ins["x_mod"], out0=o1), R * 4 * D,
+                        ops["adaln"]["avg_ms"]),
+        "fused_residual_adaln_shape": (
+            lambda: sp(dit.DIT_STREAM_ROW_WAVE_2X2, R, 2 * D, in0=a, in1=b, out0=o1, out1=o2), R * 8 * D, fused_ms),
+        "qk_token_major_copy": (lambda: (dit.dit_copy16(q, qo), dit.dit_copy16(k, ko)), R * 8 * HD,
+                                ops["qk"]["avg_ms"]),
+        "qk_head_major_copy": (lambda: (sp(dit.DIT_STREAM_HEAD_MAJOR, R, 2 * HD, in0=q, out0=qo, heads=H),
+                                        sp(dit.DIT_STREAM_HEAD_MAJOR, R, 2 * HD, in0=k, out0=ko, heads=H)),
+                               R * 8 * HD, layout_ms),
+    }
+    out = {}
+    for name, (fn, nbytes, kernel_ms) in cases.items():
+        ms = timed(fn)
+        entry = {"avg_ms": round(ms, 5), "bytes": nbytes, "GB_s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                 "pct_of_peak": round(100.0 * nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2)}
+        if kernel_ms:
+            entry["kernel_over_pattern"] = round(kernel_ms / ms, 4)
+        out[name] = entry
+    out["note"] = ("qk copies are two launches (q, then k) where the QK kernel is one; the head-major copy reads "
+                   "separate q, k and is compared with QK from a fused QKV buffer (next_qk_layout)")
+    del swiglu_out, o1, o2, qo, ko
+    return out
 
 
 def cpu_baseline(wl, ins, outs, target_s: float) -> dict:
@@ -857,6 +930,13 @@ def next_row_oracle_rates(wl, ins, pos_ref, fused_tokens: int, fused_seconds: fl
 
 # Kernel name pattern -> op, most specific first (names carry template arguments).
 KERNEL_OPS = (
+    (r"pattern_read_kernel", "p_read"),
+    (r"pattern_write_kernel", "p_write"),
+    (r"pattern_split_rows_kernel", "p_swiglu"),
+    (r"pattern_two_in_kernel", "p_residual"),
+    (r"pattern_row_wave_kernel<\d+, false,", "p_adaln"),
+    (r"pattern_row_wave_kernel<\d+, true,", "p_residual_adaln"),
+    (r"pattern_head_major_kernel", "p_head_major"),
     (r"gated_residual_adaln_kernel", "residual_adaln"),
     (r"adaln_modulate_kernel", "adaln"),
     (r"gated_residual_kernel", "residual"),
@@ -1030,8 +1110,46 @@ def summarize_rocprof(trace_dir: str, fetch_dir: str, write_dir: str, workload: 
                         f"({nbytes[op] / (stats[op]['avg_us'] * 1e-6) / 1e9:.1f} GB/s algorithmic)")
         with open(os.path.join(out_dir, f"{op}_{workload}_counters.md"), "w", encoding="utf-8") as fh:
             fh.write("\n".join(body) + "\n")
+    write_ceilings_summary(stats, nbytes, wl, workload, commands, out_dir)
     print(f"wrote profiles/ summaries for {workload}; calibration factors {factor}")
     return 0
+
+
+# pattern -> (kernel it bounds, launches of the pattern per kernel launch)
+PATTERN_BOUNDS = {"p_read": (None, 1), "p_write": (None, 1), "p_swiglu": ("swiglu", 1),
+                  "p_residual": ("residual", 1), "p_adaln": ("adaln", 1), "p_residual_adaln": ("residual_adaln", 1),
+                  "p_head_major": ("qk_layout", 2)}
+
+
+def write_ceilings_summary(stats: dict, nbytes: dict, wl, workload: str, commands: str, out_dir: str):
+    """profiles/ceilings_<workload>.md: each access-pattern stream against the kernel whose traffic it carries."""
+    lines = [f"# Access-pattern ceilings: {wl.description}", "",
+             "Each stream (dit_stream_pattern) carries one kernel's loads and stores with no arithmetic, in that "
+             "kernel's launch shape; durations from the same rocprofv3 kernel trace as the kernels "
+             "(kernels_<workload>_trace.md), full-size launches only. `kernel / pattern` is the kernel's average "
+             "duration over its pattern's (the head-major copy moves one of q and k per launch, so QK with "
+             "head-major output is set against two of its launches; that kernel also reads q, k out of a fused "
+             "QKV buffer).", "",
+             "Commands (REPO = the repository root, OUT = an output directory for the raw rocprofv3 files):", "",
+             "```", commands, "```", "",
+             "| pattern | kernel | calls | avg us | bytes | GB/s | % of 8 TB/s | kernel avg us | kernel / pattern |",
+             "|---|---|---|---|---|---|---|---|---|"]
+    for pat, (kernel, per) in PATTERN_BOUNDS.items():
+        if pat not in stats:
+            continue
+        st = stats[pat]
+        b = nbytes[pat]
+        gbs = b / (st["avg_us"] * 1e-6) / 1e9
+        k_us = stats[kernel]["avg_us"] if kernel in stats else None
+        ratio = f"{k_us / (per * st['avg_us']):.3f}" if k_us else "-"
+        lines.append(f"| `{st['name']}` | {kernel or '-'} | {st['calls']} | {st['avg_us']:.2f} | {b} | {gbs:.1f} "
+                     f"| {100 * gbs / HBM_PEAK_GBPS:.1f} | {f'{k_us:.2f}' if k_us else '-'} | {ratio} |")
+    if "copy" in stats:
+        cb = 2 * (2 << 30)
+        lines += ["", f"- `copy16_kernel` (2 GiB read + 2 GiB written): {stats['copy']['avg_us']:.2f} us, "
+                      f"{cb / (stats['copy']['avg_us'] * 1e-6) / 1e9:.1f} GB/s"]
+    with open(os.path.join(out_dir, f"ceilings_{workload}.md"), "w", encoding="utf-8") as fh:
+        fh.write("\n".join(lines) + "\n")
 
 
 def _full_size_durations(trace_dir: str) -> dict:

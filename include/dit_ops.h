@@ -434,6 +434,44 @@ dit_status dit_packed_positions(int32_t *pos, int64_t T, int64_t Hg, int64_t Wg,
  */
 dit_status dit_copy16(const void *src, void *dst, int64_t bytes, void *stream);
 
+/*
+ * Access-pattern streams: the memory traffic of the chain's kernels with no
+ * arithmetic, each with the launch shape of the kernel it stands for.  Not
+ * operators of the chain: they are the ceilings the kernels are measured
+ * against ("X% of its own pattern").  Outputs are plain copies or XORs of the
+ * inputs.  `rows` rows of `row_bytes` bytes each (a multiple of 16):
+ *   DIT_STREAM_READ          reads in0 [rows][row_bytes]; out0 is a 16-byte
+ *                            sink written only when the XOR of everything
+ *                            read equals a fixed key (keeps the loads live)
+ *   DIT_STREAM_WRITE         writes out0 [rows][row_bytes] (in0 unused)
+ *   DIT_STREAM_SPLIT_ROWS    in0 [rows][2*row_bytes] -> out0 [rows][row_bytes],
+ *                            out = first half XOR second half (SwiGLU's shape)
+ *   DIT_STREAM_TWO_IN        out0 = in0 XOR in1 (the gated residual's shape)
+ *   DIT_STREAM_ROW_WAVE      out0 = in0, one wave per row with every load
+ *                            before any store (AdaLN's shape); row_bytes <=
+ *                            16384
+ *   DIT_STREAM_ROW_WAVE_2X2  out0 = in0 and out1 = in1 with ROW_WAVE's mapping
+ *                            (the fused residual -> AdaLN's shape)
+ *   DIT_STREAM_HEAD_MAJOR    in0 [rows][heads][row_bytes/heads] ->
+ *                            out0 [heads][rows][row_bytes/heads] (token-major
+ *                            to head-major copy); row_bytes/16 a multiple of
+ *                            heads; rows * ceil(row_bytes / 4096) < 2^24
+ * Limits: rows < 2^24; row_bytes <= 2^25; SPLIT_ROWS and TWO_IN as for
+ * dit_swiglu and dit_gated_residual on the same rows and widths.  Pointers
+ * 16-byte aligned; no output may overlap an input (DIT_ERR_ARG); unused
+ * pointers may be NULL.
+ */
+#define DIT_STREAM_READ 0
+#define DIT_STREAM_WRITE 1
+#define DIT_STREAM_SPLIT_ROWS 2
+#define DIT_STREAM_TWO_IN 3
+#define DIT_STREAM_ROW_WAVE 4
+#define DIT_STREAM_ROW_WAVE_2X2 5
+#define DIT_STREAM_HEAD_MAJOR 6
+dit_status dit_stream_pattern(int32_t kind, const void *in0, const void *in1,
+                              void *out0, void *out1, int64_t rows,
+                              int64_t row_bytes, int64_t heads, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -101,3 +101,33 @@ def test_sq_summary_from_synthetic_counter_files(tmp_path):
     assert cells[1:10] == ["1", "62496", "1000.0", "500.0", "80.0", "0.0", "8.0", "25.0", "200.00"]
     # 62.5 M wave instructions in 200 us against 256 x 4 x 2.4e9 / 4 per second
     assert float(cells[10]) == pytest.approx(100 * waves * 1000 / 200e-6 / (256 * 4 * 2.4e9 / 4), abs=0.06)
+
+
+def test_value_is_withheld_when_parity_fails():
+    good = {"value": 6500.0, "cpu_baseline": {"parity_ok": True}}
+    assert bench.gate_on_parity(good, {"a": True}) and good["value"] == 6500.0
+    assert good["parity_checked"] is True and good["parity_ok"] is True
+    bad_oracle = {"value": 6500.0, "cpu_baseline": {"parity_ok": False}}
+    assert not bench.gate_on_parity(bad_oracle, {"a": True})
+    assert bad_oracle["value"] is None and bad_oracle["value_if_parity_held"] == 6500.0
+    assert bad_oracle["parity_ok"] is False
+    bad_consistency = {"value": 1.0, "cpu_baseline": {"parity_ok": True}}
+    assert not bench.gate_on_parity(bad_consistency, {"a": True, "b": False}) and bad_consistency["value"] is None
+    unchecked = {"value": 2.0}
+    assert bench.gate_on_parity(unchecked, {"a": True})
+    assert unchecked["parity_checked"] is False and unchecked["parity_ok"] is None and unchecked["value"] == 2.0
+
+
+def test_ceilings_summary_from_synthetic_trace(tmp_path):
+    wl = si.WORKLOADS["full5s"]
+    nbytes = bench.op_bytes(wl, next_rows=True)
+    stats = {"p_swiglu": {"name": "pattern_split_rows_kernel", "calls": 10, "avg_us": 1800.0},
+             "swiglu": {"name": "swiglu_kernel<true>", "calls": 10, "avg_us": 1890.0},
+             "p_head_major": {"name": "pattern_head_major_kernel", "calls": 20, "avg_us": 350.0},
+             "qk_layout": {"name": "qk_rmsnorm_rope3d_head_major_kernel<16>", "calls": 10, "avg_us": 728.0}}
+    bench.write_ceilings_summary(stats, nbytes, wl, "full5s", "cmd", str(tmp_path))
+    text = (tmp_path / "ceilings_full5s.md").read_text()
+    assert "| 1.050 |" in text  # 1890 / 1800
+    assert "| 1.040 |" in text  # 728 / (2 x 350)
+    assert nbytes["p_swiglu"] == nbytes["swiglu"]
+

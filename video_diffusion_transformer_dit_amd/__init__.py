@@ -18,6 +18,7 @@ hand-written HIP kernels (``csrc/``; declarations in ``include/dit_ops.h``):
   dit_subblock_route      SubBlock routing: block scores and the kept key blocks per query block
   dit_packed_positions    (t, h, w) coordinates of a packed token sequence
   dit_copy16              plain 16-byte-vector copy (bandwidth ceiling)
+  dit_stream_pattern      each kernel's memory traffic with no arithmetic (its own ceiling)
 
 PyTorch supplies device memory and streams only.  Build the library with
 ``python -m video_diffusion_transformer_dit_amd.build``.
@@ -32,6 +33,13 @@ from ._binding import (  # noqa: F401
     DIT_OK,
     DIT_QK_HEAD_MAJOR,
     DIT_QK_TOKEN_MAJOR,
+    DIT_STREAM_HEAD_MAJOR,
+    DIT_STREAM_READ,
+    DIT_STREAM_ROW_WAVE,
+    DIT_STREAM_ROW_WAVE_2X2,
+    DIT_STREAM_SPLIT_ROWS,
+    DIT_STREAM_TWO_IN,
+    DIT_STREAM_WRITE,
     DIT_SUBBLOCK_TOKENS,
     LIB_PATH,
     SIGNATURES,
@@ -49,6 +57,7 @@ from ._binding import (  # noqa: F401
     dit_residual_change_noalloc,
     dit_residual_change_workspace_bytes,
     dit_status_str,
+    dit_stream_pattern,
     dit_subblock_keep,
     dit_subblock_pool,
     dit_subblock_route,

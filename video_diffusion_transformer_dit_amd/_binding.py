@@ -42,6 +42,7 @@ SIGNATURES = {
                                     _I32, _I32, _I32, _F32, _F32, _P], ctypes.c_int),
     "dit_packed_positions": ([_P, _I64, _I64, _I64, _I64, _P], ctypes.c_int),
     "dit_copy16": ([_P, _P, _I64, _P], ctypes.c_int),
+    "dit_stream_pattern": ([_I32, _P, _P, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
 }
 
 _lib = None
@@ -468,3 +469,35 @@ def dit_copy16(src, dst, stream=None):
     with torch.cuda.device(dev):
         _check("dit_copy16", load_library().dit_copy16(src.data_ptr(), dst.data_ptr(), nbytes, _stream(stream, dev)))
     return dst
+
+
+DIT_STREAM_READ, DIT_STREAM_WRITE, DIT_STREAM_SPLIT_ROWS, DIT_STREAM_TWO_IN, DIT_STREAM_ROW_WAVE, \
+    DIT_STREAM_ROW_WAVE_2X2, DIT_STREAM_HEAD_MAJOR = range(7)
+
+
+def dit_stream_pattern(kind: int, rows: int, row_bytes: int, in0=None, in1=None, out0=None, out1=None, heads: int = 0,
+                       stream=None):
+    """Access-pattern stream (measurement only): the traffic of one of the chain's kernels with no arithmetic.
+
+    Tensors are contiguous device tensors of any dtype holding at least the bytes the pattern touches
+    (see dit_ops.h); unused ones may be None.
+    """
+    split = kind == DIT_STREAM_SPLIT_ROWS
+    need = {"in0": rows * row_bytes * (2 if split else 1), "in1": rows * row_bytes,
+            "out0": 16 if kind == DIT_STREAM_READ else rows * row_bytes, "out1": rows * row_bytes}
+    ptrs, devs = {}, []
+    for name, t in (("in0", in0), ("in1", in1), ("out0", out0), ("out1", out1)):
+        if t is None:
+            ptrs[name] = None
+            continue
+        if not isinstance(t, torch.Tensor) or t.device.type != "cuda" or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous device tensor")
+        if t.numel() * t.element_size() < need[name]:
+            raise ValueError(f"{name} holds {t.numel() * t.element_size()} bytes, the pattern touches {need[name]}")
+        ptrs[name] = t.data_ptr()
+        devs.append(t)
+    dev = _same_device(*devs)
+    with torch.cuda.device(dev):
+        _check("dit_stream_pattern", load_library().dit_stream_pattern(
+            int(kind), ptrs["in0"], ptrs["in1"], ptrs["out0"], ptrs["out1"], int(rows), int(row_bytes), int(heads),
+            _stream(stream, dev)))

@@ -480,6 +480,58 @@ dit_status dit_packed_positions(int32_t *pos, int64_t T, int64_t Hg, int64_t Wg,
     return launched(dit::launch_packed_positions(pos, T, Hg, Wg, n_extra, (hipStream_t)stream));
 }
 
+static_assert(DIT_STREAM_READ == dit::kPatternRead && DIT_STREAM_WRITE == dit::kPatternWrite &&
+                  DIT_STREAM_SPLIT_ROWS == dit::kPatternSplitRows && DIT_STREAM_TWO_IN == dit::kPatternTwoIn &&
+                  DIT_STREAM_ROW_WAVE == dit::kPatternRowWave && DIT_STREAM_ROW_WAVE_2X2 == dit::kPatternRowWave2x2 &&
+                  DIT_STREAM_HEAD_MAJOR == dit::kPatternHeadMajor,
+              "pattern kinds");
+
+dit_status dit_stream_pattern(int32_t kind, const void *in0, const void *in1, void *out0, void *out1, int64_t rows,
+                              int64_t row_bytes, int64_t heads, void *stream)
+{
+    if (kind < DIT_STREAM_READ || kind > DIT_STREAM_HEAD_MAJOR || rows < 0 || rows > kMaxRows || row_bytes < 0 ||
+        heads < 0)
+        return DIT_ERR_ARG;
+    if (row_bytes < 16 || row_bytes % 16 != 0 || row_bytes > 2 * kMaxWidth)
+        return DIT_ERR_SHAPE;
+    if (kind == DIT_STREAM_ROW_WAVE || kind == DIT_STREAM_ROW_WAVE_2X2) {
+        if (row_bytes > 2 * kMaxAdaLNWidth)
+            return DIT_ERR_SHAPE;
+    }
+    if (kind == DIT_STREAM_HEAD_MAJOR) {
+        if (heads < 1 || (row_bytes / 16) % heads != 0)
+            return DIT_ERR_SHAPE;
+        if (rows * ((row_bytes / 16 + 255) / 256) > kMaxRows)
+            return DIT_ERR_ARG;
+    }
+    if ((kind == DIT_STREAM_SPLIT_ROWS && !dit::swiglu_fits(rows, row_bytes / 2)) ||
+        (kind == DIT_STREAM_TWO_IN && !dit::gated_residual_fits(rows, row_bytes / 2)))
+        return DIT_ERR_ARG;
+    if (rows == 0)
+        return DIT_OK;
+    const bool two_in = kind == DIT_STREAM_TWO_IN || kind == DIT_STREAM_ROW_WAVE_2X2;
+    if ((kind != DIT_STREAM_WRITE && !in0) || (two_in && !in1) || !out0 || (kind == DIT_STREAM_ROW_WAVE_2X2 && !out1))
+        return DIT_ERR_NULL;
+    if (!aligned(in0, 16) || !aligned(in1, 16) || !aligned(out0, 16) || !aligned(out1, 16))
+        return DIT_ERR_ALIGN;
+    const int64_t n = rows * row_bytes;
+    const int64_t nin = kind == DIT_STREAM_SPLIT_ROWS ? 2 * n : n;
+    const int64_t nout = kind == DIT_STREAM_READ ? 16 : n;
+    const void *ins[2] = {kind == DIT_STREAM_WRITE ? nullptr : in0, two_in ? in1 : nullptr};
+    void *outs[2] = {out0, kind == DIT_STREAM_ROW_WAVE_2X2 ? out1 : nullptr};
+    for (void *o : outs) {
+        if (!o)
+            continue;
+        for (const void *i : ins)
+            if (i && overlap(o, nout, i, nin))
+                return DIT_ERR_ARG;
+    }
+    if (outs[1] && overlap(outs[0], nout, outs[1], nout))
+        return DIT_ERR_ARG;
+    return launched(dit::launch_stream_pattern(kind, in0, in1, out0, out1, rows, row_bytes, heads,
+                                               (hipStream_t)stream));
+}
+
 dit_status dit_copy16(const void *src, void *dst, int64_t bytes, void *stream)
 {
     if (bytes < 0)

@@ -83,4 +83,17 @@ hipError_t launch_packed_positions(int32_t *pos, int64_t T, int64_t Hg, int64_t 
 // dst = src, bytes % 16 == 0.
 hipError_t launch_copy16(const void *src, void *dst, int64_t bytes, hipStream_t stream);
 
+// Access-pattern streams (measurement only); kinds as the DIT_STREAM_* values of dit_ops.h.
+enum : int {
+    kPatternRead = 0,
+    kPatternWrite = 1,
+    kPatternSplitRows = 2,
+    kPatternTwoIn = 3,
+    kPatternRowWave = 4,
+    kPatternRowWave2x2 = 5,
+    kPatternHeadMajor = 6,
+};
+hipError_t launch_stream_pattern(int kind, const void *in0, const void *in1, void *out0, void *out1, int64_t rows,
+                                 int64_t row_bytes, int64_t heads, hipStream_t stream);
+
 } // namespace dit
