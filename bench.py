@@ -73,11 +73,12 @@ KERNEL_SOURCES = {
     "pool_hm": "subblock.hip",
     "scores": "subblock.hip",
     "topk": "subblock.hip",
+    "route_fused": "subblock.hip",
     "copy": "copy.hip",
 }
 # Kernels of the next rows, measured after the chain (see main()).
 NEXT_OPS = ("residual_adaln", "qk_layout", "qk_pool_layout", "change", "change_final", "qk_pool", "pool", "pool_hm",
-            "scores", "topk")
+            "scores", "topk", "route_fused")
 ROUTE_SPARSITY = 0.75
 COUNTER_SUMMARY = os.path.join(ROOT, "profiles", "{op}_{workload}_counters.md")
 
@@ -107,6 +108,7 @@ def op_bytes(wl, next_rows: bool = False) -> dict:
             "pool_hm": 2 * R * H * Dh * 2 + pooled,
             "scores": pooled + B * H * nb * nb * 4,            # means in, fp32 scores out
             "topk": B * H * nb * nb * 4 + B * H * nb * keep * 4,  # scores in, kept indices out
+            "route_fused": pooled + B * H * nb * keep * 4,     # means in, kept indices out (no score matrix)
             # access-pattern streams (one launch each; the head-major copy moves one of q, k)
             "p_read": R * 4 * F,
             "p_write": R * 2 * F,
@@ -505,6 +507,10 @@ def main(argv=None) -> int:
                                                      k_pooled=kp_s, stream=stream))
     scores_ms = timed(lambda: dit.dit_subblock_route(qp_s, kp_s, keep=0, scores=sc, kept=kept0, stream=stream))
     route_ms = timed(lambda: dit.dit_subblock_route(qp_s, kp_s, keep=keep, scores=sc, kept=kept, stream=stream))
+    # the same kept lists with the scores kept on chip (one fused kernel, no score matrix)
+    kept_f = torch.empty_like(kept)
+    fused_route_ms = timed(lambda: dit.dit_subblock_route(qp_s, kp_s, keep=keep, kept=kept_f, write_scores=False,
+                                                          stream=stream))
     # QK RMSNorm + RoPE that also writes the block means (no second read of q', k')
     qo_f, ko_f = torch.empty_like(qo), torch.empty_like(ko)
     qk_pool_ms = timed(lambda: dit.dit_qk_rmsnorm_rope3d_pool(ins["q"], ins["k"], ins["wq"], ins["wk"], pos, wl.bands,
@@ -519,6 +525,7 @@ def main(argv=None) -> int:
     topk_bytes = score_elems * 4 + wl.B * wl.H * nb * keep * 4
     score_flops = 2 * score_elems * wl.Dh
     topk_ms = route_ms - scores_ms
+    fused_route_bytes = pooled_bytes + wl.B * wl.H * nb * keep * 4
     subblock = {
         "sparsity": sparsity, "blocks": nb, "keep": keep,
         "pool": rate(pool_bytes, pool_ms, "pool"),
@@ -530,10 +537,16 @@ def main(argv=None) -> int:
                    "TFLOP_s": round(score_flops / (scores_ms * 1e-3) / 1e12, 1),
                    "pct_of_bf16_mfma_peak": round(100.0 * score_flops / (scores_ms * 1e-3) / 2.5e15, 2)},
         "topk": rate(topk_bytes, topk_ms, "topk"),
+        "route_fused": {**rate(fused_route_bytes, fused_route_ms, "route_fused"),
+                        "op": "dit_subblock_route with scores = NULL (scores and selection in one kernel)",
+                        "TFLOP_s": round(score_flops / (fused_route_ms * 1e-3) / 1e12, 1),
+                        "two_kernel_ms": round(route_ms, 5)},
         "total_ms": round(pool_ms + route_ms, 5),
         "total_after_fused_qk_ms": round(qk_pool_ms - ops["qk"]["avg_ms"] + route_ms, 5),
+        "total_after_fused_qk_and_route_ms": round(qk_pool_ms - ops["qk"]["avg_ms"] + fused_route_ms, 5),
     }
-    del qp_s, kp_s, sc, kept, kept0
+    route_fused_same = bool(torch.equal(kept_f, kept))
+    del qp_s, kp_s, sc, kept, kept0, kept_f
 
     # A plain streaming copy on the same device: the practical ceiling.
     cbytes = 2 << 30
@@ -587,6 +600,7 @@ def main(argv=None) -> int:
     consistency = {
         "fused_x_out_equals_residual": bool(torch.equal(fused_x, out)),
         "fused_pool_head_major_equals_layout_qk": layout_pool_same,
+        "fused_route_equals_scores_then_topk": route_fused_same,
         "head_major_equals_token_major": bool(
             torch.equal(qo_hm.permute(0, 2, 1, 3), qo.view(wl.B, wl.N, wl.H, wl.Dh))
             and torch.equal(ko_hm.permute(0, 2, 1, 3), ko.view(wl.B, wl.N, wl.H, wl.Dh))),
@@ -952,6 +966,7 @@ KERNEL_OPS = (
     (r"subblock_scores_persistent_kernel", "scores"),
     (r"subblock_scores_kernel", "scores"),
     (r"subblock_topk_kernel", "topk"),
+    (r"subblock_route_fused_kernel", "route_fused"),
     (r"packed_positions_kernel", "positions"),
     (r"copy16_kernel", "copy"),
 )

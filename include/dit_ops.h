@@ -397,7 +397,11 @@ dit_status dit_qk_rmsnorm_rope3d_pool(const dit_bf16 *q, const dit_bf16 *k,
  *                       dit_subblock_pool); may be the same buffer
  *   scores    fp32 [B][H][nb][ld], ld = dit_subblock_scores_ld(nb), 16-byte
  *             aligned, an output; entries j >= nb of a row are unspecified
- *             (the kernel may write them)
+ *             (the kernel may write them).  NULL: the score matrix is not
+ *             written at all -- scores and selection run in one kernel that
+ *             keeps each strip's scores on chip, reading only the means and
+ *             writing only the kept lists (the same lists, bit for bit, as
+ *             with a score matrix); with keep == 0 the call is then a no-op
  *   kept      int32 [B][H][nb][keep], 4-byte aligned; unused if keep == 0
  *   keep      0 <= keep <= nb (else DIT_ERR_ARG); dit_subblock_keep gives the
  *             count for a sparsity

@@ -339,7 +339,12 @@ def test_subblock_route_validation(lib):
     assert f(keep=-1) == DIT_ERR_ARG
     assert f(keep=6) == DIT_ERR_ARG  # more than nb
     assert f(Dh=8) == DIT_ERR_SHAPE and f(Dh=100) == DIT_ERR_SHAPE and f(H=0) == DIT_ERR_SHAPE
-    assert f(sc=0) == DIT_ERR_NULL and f(kept=0) == DIT_ERR_NULL and f(qp=0) == DIT_ERR_NULL
+    assert f(kept=0) == DIT_ERR_NULL and f(qp=0) == DIT_ERR_NULL
+    # no score matrix (scores and selection fused): kept is still required, and checked for overlaps
+    assert f(sc=0, kept=0) == DIT_ERR_NULL and f(sc=0, kp=0) == DIT_ERR_NULL
+    assert f(sc=0, kept=P + 64) == DIT_ERR_ARG and f(sc=0, kept=S + 2) == DIT_ERR_ALIGN
+    assert f(sc=0, keep=0, qp=0, kp=0, kept=0) == DIT_OK  # neither output: a no-op
+    assert f(sc=0, keep=6) == DIT_ERR_ARG
     assert f(qp=P + 4) == DIT_ERR_ALIGN and f(sc=R + 8) == DIT_ERR_ALIGN and f(kept=S + 2) == DIT_ERR_ALIGN
     assert f(sc=P + 64) == DIT_ERR_ARG  # scores over q_pooled
     assert f(kept=R + 16) == DIT_ERR_ARG  # kept over scores

@@ -104,6 +104,13 @@ ROUTE_SHAPES = [
 ]
 
 
+def fused_kept(qd, kd, keep=None, sparsity=None):
+    """Kept lists from the fused route (no score matrix written)."""
+    kept, scores = dit.dit_subblock_route(qd, kd, keep=keep, sparsity=sparsity, write_scores=False)
+    assert scores is None
+    return kept
+
+
 def route_inputs(shape, seed):
     g = torch.Generator().manual_seed(seed)
     qp = torch.randn(shape, generator=g) * 0.25
@@ -130,6 +137,10 @@ def test_route_matches_oracle(shape):
         check_kept_lists(kh, nb, keep)
         check_valid_against_oracle(kh, s_ref, e)
         check_top_set_of_own_scores(kh, s_gpu)
+        # scores kept on chip: the same lists, bit for bit
+        kf = fused_kept(qd, kd, keep=keep)
+        torch.cuda.synchronize()
+        assert torch.equal(kf, kept), f"keep {keep}: fused route differs from scores + top-k"
 
 
 @pytest.mark.parametrize("nb", [7, 64, 200, 2100])
@@ -153,6 +164,9 @@ def test_route_exact_scores_and_ties_bit_exact(nb):
         torch.cuda.synchronize()
         assert np.array_equal(to_host(scores)[..., :nb].astype(np.float64), s_ref)
         assert np.array_equal(to_host(kept), oracle.subblock_topk(s_ref, keep)), sparsity
+        kf = fused_kept(qd, kd, sparsity=sparsity)
+        torch.cuda.synchronize()
+        assert np.array_equal(to_host(kf), oracle.subblock_topk(s_ref, keep)), f"fused, sparsity {sparsity}"
 
 
 @pytest.mark.parametrize("nb", [300, 1953, 2100])
@@ -187,6 +201,9 @@ def test_route_crowded_first_digit_bit_exact(nb, first_rare):
         torch.cuda.synchronize()
         assert np.array_equal(to_host(scores)[..., :nb].astype(np.float64), s_ref)
         assert np.array_equal(to_host(kept), oracle.subblock_topk(s_ref, keep)), sparsity
+        kf = fused_kept(qd, kd, sparsity=sparsity)
+        torch.cuda.synchronize()
+        assert np.array_equal(to_host(kf), oracle.subblock_topk(s_ref, keep)), f"fused, sparsity {sparsity}"
 
 
 def test_route_special_values():
@@ -198,12 +215,37 @@ def test_route_special_values():
     kept, scores = dit.dit_subblock_route(z, zn, keep=4)
     torch.cuda.synchronize()
     assert to_host(kept).tolist() == [[[list(range(4)) for _ in range(nb)]]]
+    kf = fused_kept(z, zn, keep=4)
+    torch.cuda.synchronize()
+    assert to_host(kf).tolist() == [[[list(range(4)) for _ in range(nb)]]]
     # NaN in one key block: kept lists stay keep distinct ascending in-range indices
     kn = torch.randn((B, H, nb, Dh), device=DEV)
     kn[0, 0, 3, 5] = float("nan")
-    kept, _ = dit.dit_subblock_route(torch.randn((B, H, nb, Dh), device=DEV), kn, keep=4)
+    qn = torch.randn((B, H, nb, Dh), device=DEV)
+    kept, _ = dit.dit_subblock_route(qn, kn, keep=4)
+    kf = fused_kept(qn, kn, keep=4)
     torch.cuda.synchronize()
     check_kept_lists(to_host(kept), nb, 4)
+    check_kept_lists(to_host(kf), nb, 4)
+    assert torch.equal(kf, kept)
+    # neither output asked for: a no-op
+    assert fused_kept(qn, kn, keep=0).shape[-1] == 0
+
+
+# the workloads' routing shapes, and the largest block count with two rows per wave and with one
+@pytest.mark.parametrize("shape", [(1, 32, 1953, 128), (2, 32, 1953, 128), (1, 32, 3851, 128), (1, 4, 2048, 128),
+                                   (1, 2, 2049, 256), (3, 5, 513, 16)], ids=lambda s: "x".join(map(str, s)))
+def test_route_fused_equals_scores_then_topk(shape):
+    B, H, nb, Dh = shape
+    qp, kp = route_inputs(shape, seed=81 + nb)
+    qd, kd = qp.to(DEV), kp.to(DEV)
+    for sparsity in (0.75, 0.8):
+        kept, _ = dit.dit_subblock_route(qd, kd, sparsity=sparsity)
+        kf = torch.full_like(kept, -3)
+        dit.dit_subblock_route(qd, kd, sparsity=sparsity, kept=kf, write_scores=False)
+        torch.cuda.synchronize()
+        assert torch.equal(kf, kept), f"sparsity {sparsity}"
+    check_kept_lists(to_host(kf), nb, dit.dit_subblock_keep(nb, 0.8))
 
 
 def test_route_deterministic_and_buffers_reused():
@@ -264,6 +306,9 @@ def end_to_end(B, N, H, Dh, sparsity, seed, head_major=False, sample_rows=None):
     check_kept_lists(kh, nb, keep)
     check_valid_against_oracle(kh[:, :, rows], s_ref, e)
     check_top_set_of_own_scores(kh, s_all)
+    kf = fused_kept(qp, kp, sparsity=sparsity)
+    torch.cuda.synchronize()
+    assert torch.equal(kf, kept), "fused route differs from scores + top-k"
     return set_agreement(kh[:, :, rows], oracle.subblock_topk(s_ref, keep), nb)
 
 

@@ -418,12 +418,13 @@ def dit_qk_rmsnorm_rope3d_pool(q, k, wq, wk, pos, bands, head_major: bool = Fals
 
 
 def dit_subblock_route(q_pooled, k_pooled, sparsity: float | None = None, keep: int | None = None, scores=None,
-                       kept=None, stream=None):
+                       kept=None, write_scores: bool = True, stream=None):
     """Block scores and kept key blocks from pooled q', k' fp32 [B,H,nb,Dh].
 
     Give ``sparsity`` (share of key blocks dropped) or ``keep`` (count kept).  Returns (kept, scores):
     kept int32 [B,H,nb,keep] ascending per query block; scores fp32 [B,H,nb,ld] whose first nb
-    columns hold the scores (ld = dit_subblock_scores_ld(nb)).
+    columns hold the scores (ld = dit_subblock_scores_ld(nb)).  With ``write_scores=False`` no score
+    matrix is written (the library keeps the scores on chip) and scores is None.
     """
     _tensor(q_pooled, "q_pooled", dtype=torch.float32, ndim=4)
     B, H, nb, Dh = q_pooled.shape
@@ -432,15 +433,19 @@ def dit_subblock_route(q_pooled, k_pooled, sparsity: float | None = None, keep: 
         raise ValueError("give exactly one of sparsity and keep")
     keep = dit_subblock_keep(nb, sparsity) if keep is None else int(keep)
     ld = dit_subblock_scores_ld(nb)
-    scores = torch.empty((B, H, nb, ld), dtype=torch.float32, device=q_pooled.device) if scores is None else scores
+    if write_scores:
+        scores = torch.empty((B, H, nb, ld), dtype=torch.float32, device=q_pooled.device) if scores is None \
+            else scores
+        _shape(_tensor(scores, "scores", dtype=torch.float32), "scores", (B, H, nb, ld))
+    elif scores is not None:
+        raise ValueError("scores given with write_scores=False")
     kept = torch.empty((B, H, nb, keep), dtype=torch.int32, device=q_pooled.device) if kept is None else kept
-    _shape(_tensor(scores, "scores", dtype=torch.float32), "scores", (B, H, nb, ld))
     _shape(_tensor(kept, "kept", dtype=torch.int32), "kept", (B, H, nb, keep))
-    dev = _same_device(q_pooled, k_pooled, scores, kept)
+    dev = _same_device(q_pooled, k_pooled, kept, *((scores,) if scores is not None else ()))
     with torch.cuda.device(dev):
         _check("dit_subblock_route", load_library().dit_subblock_route(
-            q_pooled.data_ptr(), k_pooled.data_ptr(), scores.data_ptr(), kept.data_ptr(), B, H, nb, Dh, keep,
-            _stream(stream, dev)))
+            q_pooled.data_ptr(), k_pooled.data_ptr(), scores.data_ptr() if scores is not None else None,
+            kept.data_ptr(), B, H, nb, Dh, keep, _stream(stream, dev)))
     return kept, scores
 
 

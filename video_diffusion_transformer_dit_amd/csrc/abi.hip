@@ -447,17 +447,18 @@ dit_status dit_subblock_route(const float *q_pooled, const float *k_pooled, floa
         return DIT_ERR_SHAPE;
     if (keep > nb)
         return DIT_ERR_ARG;
-    if (B == 0 || nb == 0)
+    if (B == 0 || nb == 0 || (!scores && keep == 0)) // nothing to compute
         return DIT_OK;
-    if (!q_pooled || !k_pooled || !scores || (keep > 0 && !kept))
+    if (!q_pooled || !k_pooled || (keep > 0 && !kept))
         return DIT_ERR_NULL;
     if (!aligned(q_pooled, 16) || !aligned(k_pooled, 16) || !aligned(scores, 16) || (keep > 0 && !aligned(kept, 4)))
         return DIT_ERR_ALIGN;
     const int64_t ld = dit_subblock_scores_ld(nb);
-    const int64_t np = B * H * nb * Dh * 4, ns = B * H * nb * ld * 4, nk = B * H * nb * keep * 4;
-    if (overlap(scores, ns, q_pooled, np) || overlap(scores, ns, k_pooled, np))
+    const int64_t np = B * H * nb * Dh * 4, ns = scores ? B * H * nb * ld * 4 : 0, nk = B * H * nb * keep * 4;
+    if (scores && (overlap(scores, ns, q_pooled, np) || overlap(scores, ns, k_pooled, np)))
         return DIT_ERR_ARG;
-    if (keep > 0 && (overlap(kept, nk, scores, ns) || overlap(kept, nk, q_pooled, np) || overlap(kept, nk, k_pooled, np)))
+    if (keep > 0 && ((scores && overlap(kept, nk, scores, ns)) || overlap(kept, nk, q_pooled, np) ||
+                     overlap(kept, nk, k_pooled, np)))
         return DIT_ERR_ARG;
     return launched(
         dit::launch_subblock_route(q_pooled, k_pooled, scores, kept, B, H, nb, Dh, ld, keep, (hipStream_t)stream));

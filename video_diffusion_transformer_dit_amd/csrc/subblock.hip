@@ -482,44 +482,43 @@ __device__ __forceinline__ uint32_t lane_offset(uint32_t c, uint32_t &total)
 }
 
 constexpr int kMaxSurvivors = 256;
+constexpr int kSelectWords = 2 * (256 + kWave); // LDS words one selecting wave uses: histogram, survivors
 
-// One wave (one workgroup) per query block; grid (nb, H, B).  Lane l loads
-// key blocks 256 r + 4 l .. 256 r + 4 l + 3 with one 16-byte load per r and
-// keeps their keys in registers.  A radix select over four 8-bit digits, most
-// significant first, finds the keep-th largest key T and how many keys equal
-// to T are kept (LDS histogram of the keys still matching the chosen prefix,
-// then a suffix scan across lanes).  After two digits the few keys that still
-// match are compacted into LDS and the last two digits count only those.  The
-// kept blocks -- every key above T and the lowest-indexed keys equal to T --
-// are written in ascending order, each lane's offset taken from ballots.
-// Counting never branches: a key that does not count adds to its lane's own
-// trash slot after the 256 bins (and a survivor past the bound to a trash
-// slot after the list), so the waves issue no exec-mask bookkeeping per key;
-// when the first digit's likeliest crowded bin pair holds most keys, that pair
-// is counted by ballots instead.
-template <int RV>
-__global__ __launch_bounds__(kWave) void subblock_topk_kernel(const float *__restrict__ scores,
-                                                              int32_t *__restrict__ kept, int nb, int ld, int keep,
-                                                              int H)
+// Orders the LDS accesses of one wave across its lanes: a wavefront's LDS
+// operations execute in order, so fences at wavefront scope that keep the
+// compiler from moving memory operations across the point are enough (no
+// workgroup barrier, so waves of a larger workgroup select independently).
+__device__ __forceinline__ void wave_sync()
 {
-    __shared__ __align__(16) uint32_t hist[256 + kWave]; // 256 digits, then one trash slot per lane
-    __shared__ uint32_t survivors[kMaxSurvivors + kWave]; // then one trash slot per lane
-    const int lane = threadIdx.x;
-    const size_t row = ((size_t)blockIdx.z * H + blockIdx.y) * nb + blockIdx.x;
-    const float *s = scores + row * ld;
-    int32_t *out = kept + row * keep;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
 
-    uint32_t key[RV][4];
-#pragma unroll
-    for (int r = 0; r < RV; ++r) {
-        const int j0 = 256 * r + 4 * lane;
-        f32x4 v = {0.f, 0.f, 0.f, 0.f};
-        if (j0 < nb) // the row is 16-byte aligned and ld >= nb rounded up to 4
-            v = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(s + j0));
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            key[r][e] = score_key(v[e]);
-    }
+// The keep largest of one query block's keys, written as ascending key-block
+// indices to out[0 .. keep-1]; executed by one whole wave.  Lane l holds the
+// keys of blocks 256 r + 4 l + e (r < RV, e < 4) in key[r][e]; blocks at or
+// past nb are not candidates.  `lds` is the wave's own kSelectWords words,
+// 16-byte aligned: a 256-bin histogram with one trash slot per lane after it,
+// then the survivor list with one trash slot per lane after it.
+// A radix select over four 8-bit digits, most significant first, finds the
+// keep-th largest key T and how many keys equal to T are kept (LDS histogram
+// of the keys still matching the chosen prefix, then a suffix scan across
+// lanes).  After two digits the few keys that still match are compacted into
+// LDS and the last two digits count only those.  The kept blocks -- every key
+// above T and the lowest-indexed keys equal to T -- are written in ascending
+// order, each lane's offset taken from ballots.  Counting never branches: a
+// key that does not count adds to its lane's own trash slot after the 256
+// bins (and a survivor past the bound to a trash slot after the list), so the
+// waves issue no exec-mask bookkeeping per key; when the first digit's
+// likeliest crowded bin pair holds most keys, that pair is counted by ballots
+// instead.
+template <int RV>
+__device__ __forceinline__ void select_top_keys(const uint32_t (&key)[RV][4], int nb, int keep, int lane,
+                                                uint32_t *lds, int32_t *__restrict__ out)
+{
+    uint32_t *hist = lds;                   // 256 digits, then one trash slot per lane
+    uint32_t *survivors = lds + 256 + kWave; // kMaxSurvivors, then one trash slot per lane
     const int limit = nb - 4 * lane; // key (r, e) is a real block when 256 r + e < limit
     auto valid = [&](int r, int e) { return 256 * r + e < limit; };
 
@@ -547,7 +546,7 @@ __global__ __launch_bounds__(kWave) void subblock_topk_kernel(const float *__res
     // they remove, and every key adds to its bin.  The counts, and so the
     // selection, are the same either way.
     reinterpret_cast<uint4 *>(hist)[lane] = make_uint4(0u, 0u, 0u, 0u);
-    __syncthreads();
+    wave_sync();
     {
         const uint32_t hot = (uint32_t)__builtin_amdgcn_readfirstlane((int)(key[0][0] >> 24)); // lane 0's key 0 is real
         const uint32_t mirror = 255u - hot;
@@ -583,15 +582,15 @@ __global__ __launch_bounds__(kWave) void subblock_topk_kernel(const float *__res
                     atomicAdd(&hist[valid(r, e) ? key[r][e] >> 24 : 256u + lane], 1u);
         }
     }
-    __syncthreads();
+    wave_sync();
     choose_digit(hist, lane, 24, st);
-    __syncthreads();
+    wave_sync();
     reinterpret_cast<uint4 *>(hist)[lane] = make_uint4(0u, 0u, 0u, 0u);
-    __syncthreads();
+    wave_sync();
     count_registers(16);
-    __syncthreads();
+    wave_sync();
     choose_digit(hist, lane, 16, st);
-    __syncthreads();
+    wave_sync();
     const bool compact = st.in_bin <= (uint32_t)kMaxSurvivors; // wave-uniform
     uint32_t n_surv = 0u;
     if (compact) {
@@ -611,7 +610,7 @@ __global__ __launch_bounds__(kWave) void subblock_topk_kernel(const float *__res
     for (int pass = 2; pass < 4; ++pass) {
         const int shift = 24 - 8 * pass;
         reinterpret_cast<uint4 *>(hist)[lane] = make_uint4(0u, 0u, 0u, 0u);
-        __syncthreads();
+        wave_sync();
         if (compact) {
             for (uint32_t c = lane; c < n_surv; c += kWave) {
                 const uint32_t k = survivors[c];
@@ -621,9 +620,9 @@ __global__ __launch_bounds__(kWave) void subblock_topk_kernel(const float *__res
         } else {
             count_registers(shift);
         }
-        __syncthreads();
+        wave_sync();
         choose_digit(hist, lane, shift, st);
-        __syncthreads();
+        wave_sync();
     }
 
     // st.prefix is now the keep-th largest key T; st.in_bin keys equal T and
@@ -670,6 +669,214 @@ __global__ __launch_bounds__(kWave) void subblock_topk_kernel(const float *__res
             }
         written += total;
     }
+}
+
+// One wave (one workgroup) per query block; grid (nb, H, B).  Lane l loads
+// key blocks 256 r + 4 l .. 256 r + 4 l + 3 with one 16-byte load per r and
+// keeps their keys in registers, then selects (select_top_keys).
+template <int RV>
+__global__ __launch_bounds__(kWave) void subblock_topk_kernel(const float *__restrict__ scores,
+                                                              int32_t *__restrict__ kept, int nb, int ld, int keep,
+                                                              int H)
+{
+    __shared__ __align__(16) uint32_t lds[kSelectWords];
+    const int lane = threadIdx.x;
+    const size_t row = ((size_t)blockIdx.z * H + blockIdx.y) * nb + blockIdx.x;
+    const float *s = scores + row * ld;
+
+    uint32_t key[RV][4];
+#pragma unroll
+    for (int r = 0; r < RV; ++r) {
+        const int j0 = 256 * r + 4 * lane;
+        f32x4 v = {0.f, 0.f, 0.f, 0.f};
+        if (j0 < nb) // the row is 16-byte aligned and ld >= nb rounded up to 4
+            v = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(s + j0));
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            key[r][e] = score_key(v[e]);
+    }
+    select_top_keys<RV>(key, nb, keep, lane, lds, kept + row * keep);
+}
+
+// ---------------------------------------------------------------- fused route
+
+// Scores and kept blocks in one kernel, for callers that do not need the
+// score matrix: the scores of a strip of query blocks go from the matrix
+// cores through LDS into the registers of the waves that select on them, and
+// never to memory.  Only the means are read and the kept indices written.
+//
+// Workgroup = 16 waves and a strip of ROWS = 16 * RPW query blocks of one
+// (sample, head); wave w selects for query blocks RPW w .. RPW w + RPW - 1 of
+// the strip.  Phase 1 walks the key blocks in chunks of 256: the chunk's fp32
+// means are loaded by the whole workgroup (consecutive bytes per load
+// instruction), rounded to bf16 into LDS (KD <= 128 dimensions at a time),
+// and wave w multiplies key tile w (16 key blocks) with each 16-row block of
+// the strip's bf16 query means on the matrix cores -- the same operands and
+// the same MFMA 16x16x16 sequence over the dimensions as the score kernels,
+// so every score is the same bits.  The order-preserving keys of the chunk's
+// scores are staged in LDS, and each wave reads its own query blocks' 256
+// keys into the register slot of the chunk: lane l ends up with key blocks
+// 256 r + 4 l + e, the layout select_top_keys takes.  Phase 2 reuses the LDS
+// as one selection area per wave and the waves select independently.
+//
+// RV = ceil(nb / 256) register slots per query block; RPW = 2 query blocks
+// per wave while RV <= 8 (up to 64 key registers of the 128 a wave has when
+// 16 share a CU), else 1.  Workgroups walk (sample, head, strip) items; the
+// XCD of workgroup g (g % 8, dispatch is round-robin) takes the (g % 8)-th
+// contiguous eighth of the items, so the 32 workgroups an XCD runs at once
+// share one head's key means in its L2.
+//
+// What bounds it (1344x768 5 s, 1953 blocks, 32 heads): each strip re-reads
+// its head's key means, 16 bytes of L2 traffic per score against the score
+// kernel's 4 (128 x 128 tiles), and the keys of a strip fill the register
+// file, so one workgroup runs per CU and its load, multiply and select phases
+// do not overlap with another's.
+constexpr int kRouteWaves = 16;
+constexpr int kChunkKeys = 256;
+
+template <int DH, int RV, int RPW>
+__global__ __launch_bounds__(kRouteWaves * kWave) void subblock_route_fused_kernel(
+    const float *__restrict__ qp, const float *__restrict__ kp, int32_t *__restrict__ kept, int nb, int keep,
+    int strips, uint64_t total)
+{
+    constexpr int kThreads = kRouteWaves * kWave;
+    constexpr int ROWS = kRouteWaves * RPW;   // query blocks per strip
+    constexpr int NRB = ROWS / 16;            // 16-row MFMA blocks of the strip
+    constexpr int KD = DH < 128 ? DH : 128;   // key dimensions staged per pass
+    constexpr int PASSES = DH / KD;
+    constexpr int kQRow = DH + 4;             // bf16 per padded LDS row (rows 8 bytes apart in bank)
+    constexpr int kKRow = KD + 4;
+    constexpr int kSRow = kChunkKeys + 4;     // keys per padded staging row
+    constexpr int kQBytes = ROWS * kQRow * 2, kKBytes = kChunkKeys * kKRow * 2, kSBytes = ROWS * kSRow * 4;
+    constexpr int kPhase1 = kQBytes + kKBytes + kSBytes;
+    constexpr int kPhase2 = kRouteWaves * kSelectWords * 4;
+    constexpr int kF4 = kChunkKeys * KD / 4 / kThreads; // float4 of the key chunk per thread and pass
+    static_assert(kF4 >= 1, "tile shapes");
+    __shared__ __align__(16) unsigned char lds_raw[kPhase1 > kPhase2 ? kPhase1 : kPhase2];
+    uint16_t *lds_q = reinterpret_cast<uint16_t *>(lds_raw);
+    uint16_t *lds_k = reinterpret_cast<uint16_t *>(lds_raw + kQBytes);
+    uint32_t *lds_s = reinterpret_cast<uint32_t *>(lds_raw + kQBytes + kKBytes);
+
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    const int r16 = lane & 15, quad = lane >> 4;
+
+    const uint64_t per = gridDim.x / 8, xcd = blockIdx.x % 8, g = blockIdx.x / 8;
+    const uint64_t span = (total + 7) / 8, first = xcd * span;
+    const uint64_t last = first + span < total ? first + span : total;
+    for (uint64_t item = first + g; item < last; item += per) { // the same trip count for the whole workgroup
+        const uint64_t bh = item / (uint64_t)strips;
+        const int i0 = (int)(item % (uint64_t)strips) * ROWS; // first query block of the strip
+        const float *qrow = qp + (bh * nb) * DH;
+        const float *krow = kp + (bh * nb) * DH;
+
+        __syncthreads(); // the previous item's selection areas are free
+        // the strip's query means, bf16, rows past nb zero
+        for (int e = tid; e < ROWS * DH / 4; e += kThreads) {
+            const int r = e / (DH / 4), c4 = e % (DH / 4);
+            const float4 a = i0 + r < nb ? reinterpret_cast<const float4 *>(qrow + (size_t)(i0 + r) * DH)[c4]
+                                         : make_float4(0.f, 0.f, 0.f, 0.f);
+            uint2 pa;
+            pa.x = pack_bf16x2(a.x, a.y), pa.y = pack_bf16x2(a.z, a.w);
+            *reinterpret_cast<uint2 *>(&lds_q[r * kQRow + 4 * c4]) = pa;
+        }
+
+        // A runtime loop over the chunks (unrolled, the compiler would hold the
+        // addresses of every chunk's loads at once); each chunk's keys enter
+        // the last register slot and the earlier ones move down a slot, so
+        // after RV chunks slot r holds chunk r.
+        uint32_t key[RPW][RV][4];
+#pragma unroll 1
+        for (int c = 0; c < RV; ++c) {
+            f32x4 acc[NRB];
+#pragma unroll
+            for (int rb = 0; rb < NRB; ++rb)
+                acc[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int p = 0; p < PASSES; ++p) {
+                float4 v[kF4];
+#pragma unroll
+                for (int m = 0; m < kF4; ++m) {
+                    const int e = tid + kThreads * m;
+                    const int kr = e / (KD / 4), c4 = e % (KD / 4);
+                    const int j = kChunkKeys * c + kr;
+                    v[m] = j < nb ? reinterpret_cast<const float4 *>(krow + (size_t)j * DH + p * KD)[c4]
+                                  : make_float4(0.f, 0.f, 0.f, 0.f);
+                }
+                __syncthreads(); // every wave is done with the previous pass's key tile
+#pragma unroll
+                for (int m = 0; m < kF4; ++m) {
+                    const int e = tid + kThreads * m;
+                    const int kr = e / (KD / 4), c4 = e % (KD / 4);
+                    uint2 pc;
+                    pc.x = pack_bf16x2(v[m].x, v[m].y), pc.y = pack_bf16x2(v[m].z, v[m].w);
+                    *reinterpret_cast<uint2 *>(&lds_k[kr * kKRow + 4 * c4]) = pc;
+                }
+                __syncthreads();
+#pragma unroll
+                for (int s = 0; s < KD / 16; ++s) {
+                    const int kof = 16 * s + 4 * quad;
+                    const s16x4 bv = *reinterpret_cast<const s16x4 *>(&lds_k[(16 * wave + r16) * kKRow + kof]);
+#pragma unroll
+                    for (int rb = 0; rb < NRB; ++rb) {
+                        const s16x4 a = *reinterpret_cast<const s16x4 *>(
+                            &lds_q[(16 * rb + r16) * kQRow + p * KD + kof]);
+                        acc[rb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, bv, acc[rb], 0, 0, 0);
+                    }
+                }
+            }
+            // query block 16 rb + 4 quad + e, key block 256 c + 16 wave + r16
+#pragma unroll
+            for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    lds_s[(16 * rb + 4 * quad + e) * kSRow + 16 * wave + r16] = score_key(acc[rb][e]);
+            __syncthreads();
+#pragma unroll
+            for (int j = 0; j < RPW; ++j) {
+                const uint4 t = reinterpret_cast<const uint4 *>(&lds_s[(RPW * wave + j) * kSRow])[lane];
+#pragma unroll
+                for (int r = 0; r + 1 < RV; ++r)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        key[j][r][e] = key[j][r + 1][e];
+                key[j][RV - 1][0] = t.x, key[j][RV - 1][1] = t.y, key[j][RV - 1][2] = t.z, key[j][RV - 1][3] = t.w;
+            }
+            // the staging rows are written again only after the next chunk's barriers
+        }
+        __syncthreads(); // phase 1's LDS is dead: the selection areas overlay it
+        uint32_t *sel = reinterpret_cast<uint32_t *>(lds_raw) + wave * kSelectWords;
+#pragma unroll
+        for (int j = 0; j < RPW; ++j) {
+            const int i = i0 + RPW * wave + j;
+            if (i < nb) // wave-uniform
+                select_top_keys<RV>(key[j], nb, keep, lane, sel, kept + (bh * nb + (uint64_t)i) * keep);
+        }
+    }
+}
+
+template <int DH, int RV>
+void launch_route_fused_dh_rv(const float *qp, const float *kp, int32_t *kept, int nb, int keep, int H, int B,
+                              hipStream_t stream)
+{
+    constexpr int RPW = RV <= 8 ? 2 : 1;
+    constexpr int ROWS = kRouteWaves * RPW;
+    const int strips = (nb + ROWS - 1) / ROWS;
+    const uint64_t total = (uint64_t)B * (uint64_t)H * (uint64_t)strips;
+    // at most 8 * 4096 workgroups (each then walks its items); a multiple of 8
+    const uint64_t grid = ((total + 7) / 8 * 8) < 32768u ? (total + 7) / 8 * 8 : 32768u;
+    hipLaunchKernelGGL((subblock_route_fused_kernel<DH, RV, RPW>), dim3((unsigned)grid), dim3(kRouteWaves * kWave), 0,
+                       stream, qp, kp, kept, nb, keep, strips, total);
+}
+
+template <int DH>
+void launch_route_fused_dh(const float *qp, const float *kp, int32_t *kept, int nb, int keep, int H, int B,
+                           hipStream_t stream)
+{
+    if (nb <= 256) launch_route_fused_dh_rv<DH, 1>(qp, kp, kept, nb, keep, H, B, stream);
+    else if (nb <= 512) launch_route_fused_dh_rv<DH, 2>(qp, kp, kept, nb, keep, H, B, stream);
+    else if (nb <= 1024) launch_route_fused_dh_rv<DH, 4>(qp, kp, kept, nb, keep, H, B, stream);
+    else if (nb <= 2048) launch_route_fused_dh_rv<DH, 8>(qp, kp, kept, nb, keep, H, B, stream);
+    else launch_route_fused_dh_rv<DH, 16>(qp, kp, kept, nb, keep, H, B, stream);
 }
 
 template <int RV>
@@ -763,6 +970,20 @@ hipError_t launch_subblock_route(const float *q_pooled, const float *k_pooled, f
                                  hipStream_t stream)
 {
     const int n = (int)nb, l = (int)ld, h = (int)H, b = (int)B;
+    if (!scores) { // kept blocks only: one fused kernel, no score matrix
+        if (keep == 0)
+            return hipSuccess;
+        const int kp = (int)keep;
+        switch (Dh) {
+        case 16: launch_route_fused_dh<16>(q_pooled, k_pooled, kept, n, kp, h, b, stream); break;
+        case 32: launch_route_fused_dh<32>(q_pooled, k_pooled, kept, n, kp, h, b, stream); break;
+        case 64: launch_route_fused_dh<64>(q_pooled, k_pooled, kept, n, kp, h, b, stream); break;
+        case 128: launch_route_fused_dh<128>(q_pooled, k_pooled, kept, n, kp, h, b, stream); break;
+        case 256: launch_route_fused_dh<256>(q_pooled, k_pooled, kept, n, kp, h, b, stream); break;
+        default: return hipErrorInvalidValue;
+        }
+        return hipGetLastError();
+    }
     switch (Dh) {
     case 16: launch_scores_dh<16>(q_pooled, k_pooled, scores, n, l, h, b, stream); break;
     case 32: launch_scores_dh<32>(q_pooled, k_pooled, scores, n, l, h, b, stream); break;
