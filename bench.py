@@ -75,6 +75,8 @@ KERNEL_SOURCES = {
     "topk": "subblock.hip",
     "route_fused": "subblock.hip",
     "copy": "copy.hip",
+    **{p: "patterns.hip" for p in ("p_read", "p_write", "p_swiglu", "p_residual", "p_adaln", "p_residual_adaln",
+                                   "p_head_major")},
 }
 # Kernels of the next rows, measured after the chain (see main()).
 NEXT_OPS = ("residual_adaln", "qk_layout", "qk_pool_layout", "change", "change_final", "qk_pool", "pool", "pool_hm",
@@ -165,6 +167,9 @@ def parse_args(argv=None):
     p.add_argument("--summarize-rocprof", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
                    help="write profiles/ summaries from rocprofv3 CSV output of a kernel-trace run and of "
                         "FETCH_SIZE and WRITE_SIZE counter runs of this benchmark, then exit")
+    p.add_argument("--summarize-stalls", nargs=2, metavar=("TRACE_DIR", "STALL_DIR"),
+                   help="write the profiles/ summary of the shader-sequencer stall counter run (wave time waiting, "
+                        "issuing VALU, VMEM latency) next to the kernel trace, then exit")
     p.add_argument("--summarize-sq", nargs=2, metavar=("TRACE_DIR", "SQ_DIR"),
                    help="write the profiles/ summary of the shader-sequencer counter run (instruction mix, LDS "
                         "waits, VALU issue rate, MFMA work) next to the kernel trace, then exit")
@@ -177,6 +182,8 @@ def main(argv=None) -> int:
         return summarize_rocprof(*args.summarize_rocprof, workload=args.workload)
     if args.summarize_sq:
         return summarize_sq(*args.summarize_sq, workload=args.workload)
+    if args.summarize_stalls:
+        return summarize_stalls(*args.summarize_stalls, workload=args.workload)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures the chain on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
@@ -1242,6 +1249,79 @@ def summarize_sq(trace_dir: str, sq_dir: str, workload: str = "full5s", out_dir:
     lines += [""] + extra + [f"- kernel source sha256 ({name} and device_common.hpp): {digest}"
                              for name, digest in sorted(sources.items())]
     out = os.path.join(out_dir or os.path.join(ROOT, "profiles"), f"kernels_{workload}_sq_counters.md")
+    with open(out, "w", encoding="utf-8") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print(f"wrote {out}")
+    return 0
+
+
+STALL_COUNTERS = ("SQ_WAVES", "SQ_WAVE_CYCLES", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_VALU",
+                  "SQ_INST_LEVEL_VMEM", "SQ_INSTS_VMEM", "SQ_INSTS_SMEM")
+
+STALL_COMMANDS = """\
+cd /tmp && export TMPDIR=/tmp
+rocprofv3 --kernel-trace --stats --output-format csv -d $OUT/prof_trace -o trace -- \\
+    python $REPO/bench.py --workload {wl} --steps 10 --warmup 2 --no-cpu-baseline
+rocprofv3 --pmc {counters} --output-format csv -d $OUT/prof_stall -o stall -- \\
+    python $REPO/bench.py --workload {wl} --steps 2 --warmup 1 --no-cpu-baseline --no-graph
+cd $REPO && python bench.py --workload {wl} --summarize-stalls $OUT/prof_trace $OUT/prof_stall"""
+
+
+def summarize_stalls(trace_dir: str, stall_dir: str, workload: str = "full5s", out_dir: str | None = None) -> int:
+    """Where each kernel's waves spend their time (full-size launches, averaged per dispatch).
+
+    SQ_WAVE_CYCLES, SQ_WAIT_ANY, SQ_WAIT_INST_ANY and SQ_ACTIVE_INST_VALU count quad-cycles summed over
+    waves: their ratios are shares of wave residency spent waiting on a dependency (a memory counter
+    or a barrier), waiting to be issued, and issuing VALU work.  SQ_INST_LEVEL_VMEM accumulates the
+    vector-memory instructions in flight every cycle, so over SQ_INSTS_VMEM it is their average latency.
+    """
+    import synthetic_inputs as si
+
+    wl = si.WORKLOADS[workload]
+    avg_us = _full_size_durations(trace_dir)
+    per = {}
+    for r in _csv_rows(stall_dir, "counter_collection.csv"):
+        op = _kernel_op(r["Kernel_Name"])
+        if op is None or r["Counter_Name"] not in STALL_COUNTERS:
+            continue
+        d = per.setdefault(op, {}).setdefault(int(r["Grid_Size"]), {}).setdefault(r["Dispatch_Id"], {})
+        d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    lines = [f"# Where the waves' time goes: {wl.description}", "",
+             "One rocprofv3 counter run of the benchmark with the eight SQ counters below, next to the "
+             "kernel-trace run that gives each kernel's average duration. Full-size launches only, averaged "
+             "per dispatch. Shares are of SQ_WAVE_CYCLES (wave residency, quad-cycles): `waiting` = "
+             "SQ_WAIT_ANY (a wave held by a dependency: s_waitcnt on memory or LDS, or a barrier), `issue "
+             "wait` = SQ_WAIT_INST_ANY (ready but not issued), `VALU` = SQ_ACTIVE_INST_VALU. VMEM latency = "
+             "SQ_INST_LEVEL_VMEM / SQ_INSTS_VMEM (cycles a vector-memory instruction is in flight, on "
+             "average). Wave life = 4 x SQ_WAVE_CYCLES / SQ_WAVES cycles.", "",
+             f"Counters: {' '.join(STALL_COUNTERS)}", "",
+             "Commands (REPO = the repository root, OUT = an output directory for the raw rocprofv3 files):", "",
+             "```", STALL_COMMANDS.format(wl=workload, counters=" ".join(STALL_COUNTERS)), "```", "",
+             "| kernel | waves | wave life (cycles) | waiting % | issue wait % | VALU % | VMEM / wave | "
+             "VMEM latency (cycles) | SMEM / wave | avg us |",
+             "|---|---|---|---|---|---|---|---|---|---|"]
+    for op in (*OPS, *NEXT_OPS, *PATTERN_BOUNDS, "copy"):
+        if op not in per:
+            continue
+        grids = per[op]
+        ds = list(grids[max(grids)].values())
+        mean = {c: sum(d.get(c, 0.0) for d in ds) / len(ds) for c in STALL_COUNTERS}
+        waves, cyc = mean["SQ_WAVES"], mean["SQ_WAVE_CYCLES"]
+        if waves <= 0 or cyc <= 0:
+            continue
+        lat = mean["SQ_INST_LEVEL_VMEM"] / mean["SQ_INSTS_VMEM"] if mean["SQ_INSTS_VMEM"] else 0.0
+        us = avg_us.get(op)
+        lines.append(f"| {op} | {waves:.0f} | {4 * cyc / waves:.0f} | {100 * mean['SQ_WAIT_ANY'] / cyc:.1f} "
+                     f"| {100 * mean['SQ_WAIT_INST_ANY'] / cyc:.1f} | {100 * mean['SQ_ACTIVE_INST_VALU'] / cyc:.1f} "
+                     f"| {mean['SQ_INSTS_VMEM'] / waves:.1f} | {lat:.0f} | {mean['SQ_INSTS_SMEM'] / waves:.1f} "
+                     f"| {f'{us:.2f}' if us else '-'} |")
+    sources = {}
+    for op in per:
+        if op in KERNEL_SOURCES:
+            sources.setdefault(KERNEL_SOURCES[op], source_digest(op))
+    lines += [""] + [f"- kernel source sha256 ({name} and device_common.hpp): {digest}"
+                     for name, digest in sorted(sources.items())]
+    out = os.path.join(out_dir or os.path.join(ROOT, "profiles"), f"kernels_{workload}_stalls.md")
     with open(out, "w", encoding="utf-8") as fh:
         fh.write("\n".join(lines) + "\n")
     print(f"wrote {out}")
