@@ -413,17 +413,30 @@ __global__ __launch_bounds__(512) void subblock_scores_persistent_kernel(const f
 // ---------------------------------------------------------------- selection
 
 // Order-preserving map of an fp32 score to an unsigned key; -0 and +0 map to
-// the same key so that they tie, as equal scores do.
+// the same key so that they tie, as equal scores do.  Positive scores (and
+// +0) take u + 2^31, negative ones 2^32 - u, which sends -0 to +0's key and
+// every other negative below it in reverse order of magnitude.  No score maps
+// to 0, which marks the slots past the last key block.
 __device__ __forceinline__ uint32_t score_key(float f)
 {
-    uint32_t u = __float_as_uint(f);
-    u = (u == 0x80000000u) ? 0u : u;
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    const uint32_t u = __float_as_uint(f);
+    return (int32_t)u < 0 ? 0u - u : u ^ 0x80000000u;
 }
 
 __device__ __forceinline__ int lanes_below(uint64_t mask)
 {
     return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+// Sum of x over lanes lane .. 63.
+__device__ __forceinline__ uint32_t suffix_sum(uint32_t x, int lane)
+{
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        const uint32_t o = __shfl_down(x, off, kWave);
+        x += (lane + off < kWave) ? o : 0u;
+    }
+    return x;
 }
 
 // Radix-select state: keys matching `prefix` under `mask` are still
@@ -432,19 +445,42 @@ struct RadixState {
     uint32_t prefix, mask, need, in_bin;
 };
 
-// Picks the next 8-bit digit from a 256-bin histogram (lane l reads digits
-// 4l .. 4l+3): the largest digit whose keys, with those of all larger digits,
-// reach `need`.
+constexpr int kTopBits = 10;                   // the first digit: a key's top ten bits
+constexpr int kTopBins = 1 << kTopBits;
+constexpr int kMaxSurvivors = 512;
+constexpr int kSelectWords = kTopBins + kMaxSurvivors; // LDS words one selecting wave uses
+
+// Picks the first digit from its 1024-bin histogram: the largest digit whose
+// keys, with those of all larger digits, reach `need`.  Lane l sums bins
+// 16 l .. 16 l + 15; a suffix sum over the lanes finds the lane holding the
+// digit, then sixteen lanes take one bin each of that lane's range.
+__device__ __forceinline__ void choose_top_digit(const uint32_t *hist, int lane, RadixState &st)
+{
+    const uint4 *h4 = reinterpret_cast<const uint4 *>(hist) + 4 * lane;
+    const uint4 a = h4[0], b = h4[1], c = h4[2], d = h4[3];
+    const uint32_t cnt = (a.x + a.y + a.z + a.w) + (b.x + b.y + b.z + b.w) + (c.x + c.y + c.z + c.w) +
+                         (d.x + d.y + d.z + d.w);
+    const uint32_t suffix = suffix_sum(cnt, lane);
+    const uint32_t above = suffix - cnt;
+    const int L = __builtin_ctzll(__ballot(above < st.need && st.need <= suffix)); // exactly one lane
+    const uint32_t above_l = (uint32_t)__builtin_amdgcn_readlane(above, L);
+    uint32_t h = hist[(16 * L + lane) & (kTopBins - 1)];
+    h = lane < 16 ? h : 0u;
+    const uint32_t greater = above_l + suffix_sum(h, lane) - h; // keys of the larger digits
+    const int D = __builtin_ctzll(__ballot(greater < st.need && st.need <= greater + h));
+    st.prefix = (uint32_t)(16 * L + D) << (32 - kTopBits);
+    st.mask = ~0u << (32 - kTopBits);
+    st.need -= (uint32_t)__builtin_amdgcn_readlane(greater, D);
+    st.in_bin = (uint32_t)__builtin_amdgcn_readlane(h, D);
+}
+
+// The same for an 8-bit digit at `shift` from a 256-bin histogram (lane l
+// reads digits 4l .. 4l+3).
 __device__ __forceinline__ void choose_digit(const uint32_t *hist, int lane, int shift, RadixState &st)
 {
     const uint4 h4 = reinterpret_cast<const uint4 *>(hist)[lane];
     const uint32_t c = h4.x + h4.y + h4.z + h4.w;
-    uint32_t suffix = c; // keys of digits >= 4l
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-        const uint32_t o = __shfl_down(suffix, off, kWave);
-        suffix += (lane + off < kWave) ? o : 0u;
-    }
+    const uint32_t suffix = suffix_sum(c, lane); // keys of digits >= 4l
     const uint32_t above = suffix - c;
     const bool mine = above < st.need && st.need <= suffix; // exactly one lane
     uint32_t digit = 4u * lane, greater = above, count = h4.x;
@@ -466,24 +502,6 @@ __device__ __forceinline__ void choose_digit(const uint32_t *hist, int lane, int
     st.in_bin = (uint32_t)__builtin_amdgcn_readlane(count, src);
 }
 
-// Exclusive prefix sum over the wave of per-lane counts in 0 .. 7, and the
-// total, from one ballot per bit.
-__device__ __forceinline__ uint32_t lane_offset(uint32_t c, uint32_t &total)
-{
-    uint32_t excl = 0u;
-    total = 0u;
-#pragma unroll
-    for (int bit = 0; bit < 3; ++bit) {
-        const uint64_t m = __ballot((c >> bit) & 1u);
-        excl += (uint32_t)lanes_below(m) << bit;
-        total += (uint32_t)__builtin_popcountll(m) << bit;
-    }
-    return excl;
-}
-
-constexpr int kMaxSurvivors = 256;
-constexpr int kSelectWords = 2 * (256 + kWave); // LDS words one selecting wave uses: histogram, survivors
-
 // Orders the LDS accesses of one wave across its lanes: a wavefront's LDS
 // operations execute in order, so fences at wavefront scope that keep the
 // compiler from moving memory operations across the point are enough (no
@@ -496,188 +514,133 @@ __device__ __forceinline__ void wave_sync()
 }
 
 // The keep largest of one query block's keys, written as ascending key-block
-// indices to out[0 .. keep-1]; executed by one whole wave.  Lane l holds the
-// keys of blocks 256 r + 4 l + e (r < RV, e < 4) in key[r][e]; blocks at or
-// past nb are not candidates.  `lds` is the wave's own kSelectWords words,
-// 16-byte aligned: a 256-bin histogram with one trash slot per lane after it,
-// then the survivor list with one trash slot per lane after it.
-// A radix select over four 8-bit digits, most significant first, finds the
-// keep-th largest key T and how many keys equal to T are kept (LDS histogram
-// of the keys still matching the chosen prefix, then a suffix scan across
-// lanes).  After two digits the few keys that still match are compacted into
-// LDS and the last two digits count only those.  The kept blocks -- every key
-// above T and the lowest-indexed keys equal to T -- are written in ascending
-// order, each lane's offset taken from ballots.  Counting never branches: a
-// key that does not count adds to its lane's own trash slot after the 256
-// bins (and a survivor past the bound to a trash slot after the list), so the
-// waves issue no exec-mask bookkeeping per key; when the first digit's
-// likeliest crowded bin pair holds most keys, that pair is counted by ballots
-// instead.
-template <int RV>
-__device__ __forceinline__ void select_top_keys(const uint32_t (&key)[RV][4], int nb, int keep, int lane,
-                                                uint32_t *lds, int32_t *__restrict__ out)
+// indices to out[0 .. keep-1]; executed by one whole wave, 1 <= keep <= nb.
+// Lane l holds the key of block 64 s + l in key[s] (s < S, 64 S >= nb), and 0
+// in the slots of blocks at or past nb: below every score's key and past
+// every real block's index, so those slots are never among the kept ones and
+// need no test.  `lds` is the wave's own kSelectWords words, 16-byte aligned:
+// a 1024-bin histogram, then room for kMaxSurvivors keys.
+// A radix select finds the keep-th largest key T, most significant digit
+// first: a histogram of the top ten bits (LDS atomics, one per key) fixes the
+// first digit, the keys sharing it are compacted into LDS (each slot's
+// matching lanes found by one ballot), and 8-bit digits over those few fix
+// the rest -- stopping as soon as every key left in the bin is kept, so that
+// keys >= the prefix are exactly the kept ones.  Only when T splits a run of
+// equal keys do ties need ranks (lowest index first).  Kept blocks are
+// written slot by slot: a ballot of the slot's kept lanes gives each lane its
+// place, so the list comes out ascending with no sort.
+template <int S>
+__device__ __forceinline__ void select_keep(const uint32_t (&key)[S], int nb, int keep, int lane, uint32_t *lds,
+                                            int32_t *__restrict__ out)
 {
-    uint32_t *hist = lds;                   // 256 digits, then one trash slot per lane
-    uint32_t *survivors = lds + 256 + kWave; // kMaxSurvivors, then one trash slot per lane
-    const int limit = nb - 4 * lane; // key (r, e) is a real block when 256 r + e < limit
-    auto valid = [&](int r, int e) { return 256 * r + e < limit; };
-
+    uint32_t *hist = lds;
+    uint32_t *survivors = lds + kTopBins;
     RadixState st = {0u, 0u, (uint32_t)keep, 0u};
-    // Every key adds to a bin without branching: keys that do not count go to
-    // the lane's own trash slot.
-    auto count_registers = [&](int shift) {
+
 #pragma unroll
-        for (int r = 0; r < RV; ++r)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const bool counts = valid(r, e) && (key[r][e] & st.mask) == st.prefix;
-                atomicAdd(&hist[counts ? (key[r][e] >> shift) & 0xffu : 256u + lane], 1u);
-            }
-    };
-    // First digit: every valid key counts.  The first digit is the sign and
-    // the top of the exponent, so a row's keys can crowd into a few bins, and
-    // LDS atomics on one address serialise.  The candidate crowded bin is the
-    // first key's, paired with its mirror 255 - it (the key of -x is the
-    // bitwise inverse of the key of x, so that bin holds the same magnitudes
-    // with the other sign).  When the pair holds more than half of the first
-    // 256 keys (a wave-uniform test), the keys in it are counted with one
-    // ballot per bin and key slot and added once, and only the others go to
-    // the atomics.  Otherwise the ballots would cost more than the conflicts
-    // they remove, and every key adds to its bin.  The counts, and so the
-    // selection, are the same either way.
-    reinterpret_cast<uint4 *>(hist)[lane] = make_uint4(0u, 0u, 0u, 0u);
+    for (int i = 0; i < kTopBins / (4 * kWave); ++i)
+        reinterpret_cast<uint4 *>(hist)[lane + kWave * i] = make_uint4(0u, 0u, 0u, 0u);
     wave_sync();
-    {
-        const uint32_t hot = (uint32_t)__builtin_amdgcn_readfirstlane((int)(key[0][0] >> 24)); // lane 0's key 0 is real
-        const uint32_t mirror = 255u - hot;
-        uint32_t in_pair = 0u, sampled = 0u;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const uint32_t d = key[0][e] >> 24;
-            in_pair += (uint32_t)__builtin_popcountll(__ballot(valid(0, e) && (d == hot || d == mirror)));
-            sampled += (uint32_t)__builtin_popcountll(__ballot(valid(0, e)));
-        }
-        if (2u * in_pair > sampled) {
-            uint32_t hot_count = 0u, mirror_count = 0u;
-#pragma unroll
-            for (int r = 0; r < RV; ++r)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const uint32_t d = key[r][e] >> 24;
-                    const bool v = valid(r, e);
-                    const bool h = v && d == hot, m = v && d == mirror;
-                    hot_count += (uint32_t)__builtin_popcountll(__ballot(h));
-                    mirror_count += (uint32_t)__builtin_popcountll(__ballot(m));
-                    atomicAdd(&hist[(v && !h && !m) ? d : 256u + lane], 1u);
-                }
-            if (lane == 0) {
-                atomicAdd(&hist[hot], hot_count);
-                atomicAdd(&hist[mirror], mirror_count);
-            }
-        } else {
-#pragma unroll
-            for (int r = 0; r < RV; ++r)
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    atomicAdd(&hist[valid(r, e) ? key[r][e] >> 24 : 256u + lane], 1u);
-        }
-    }
+    for (int s = 0; s < S; ++s)
+        if (kWave * s < nb) // wave-uniform
+            atomicAdd(&hist[key[s] >> (32 - kTopBits)], 1u);
     wave_sync();
-    choose_digit(hist, lane, 24, st);
+    choose_top_digit(hist, lane, st);
     wave_sync();
-    reinterpret_cast<uint4 *>(hist)[lane] = make_uint4(0u, 0u, 0u, 0u);
-    wave_sync();
-    count_registers(16);
-    wave_sync();
-    choose_digit(hist, lane, 16, st);
-    wave_sync();
-    const bool compact = st.in_bin <= (uint32_t)kMaxSurvivors; // wave-uniform
-    uint32_t n_surv = 0u;
-    if (compact) {
-#pragma unroll
-        for (int r = 0; r < RV; ++r)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const bool m = valid(r, e) && (key[r][e] & st.mask) == st.prefix;
-                const uint64_t mm = __ballot(m);
-                const uint32_t at = n_surv + (uint32_t)lanes_below(mm);
-                // exactly in_bin keys match; the bound only guards the store
-                survivors[(m && at < (uint32_t)kMaxSurvivors) ? at : kMaxSurvivors + lane] = key[r][e];
-                n_surv += (uint32_t)__builtin_popcountll(mm);
-            }
-    }
-#pragma unroll 1
-    for (int pass = 2; pass < 4; ++pass) {
-        const int shift = 24 - 8 * pass;
-        reinterpret_cast<uint4 *>(hist)[lane] = make_uint4(0u, 0u, 0u, 0u);
-        wave_sync();
+
+    if (st.need < st.in_bin) {
+        // the bin holds keys that are not kept: resolve the remaining bits
+        const bool compact = st.in_bin <= (uint32_t)kMaxSurvivors; // wave-uniform
+        uint32_t n_surv = 0u;
         if (compact) {
-            for (uint32_t c = lane; c < n_surv; c += kWave) {
-                const uint32_t k = survivors[c];
-                if ((k & st.mask) == st.prefix)
-                    atomicAdd(&hist[(k >> shift) & 0xffu], 1u);
-            }
-        } else {
-            count_registers(shift);
+#pragma unroll
+            for (int s = 0; s < S; ++s)
+                if (kWave * s < nb) {
+                    const bool m = (key[s] & st.mask) == st.prefix;
+                    const uint64_t mm = __ballot(m);
+                    if (mm) { // wave-uniform
+                        // exactly in_bin keys match, so every place is below the bound
+                        if (m)
+                            survivors[__builtin_amdgcn_mbcnt_hi((uint32_t)(mm >> 32),
+                                                                __builtin_amdgcn_mbcnt_lo((uint32_t)mm, n_surv))] =
+                                key[s];
+                        n_surv += (uint32_t)__builtin_popcountll(mm);
+                    }
+                }
+            wave_sync();
         }
-        wave_sync();
-        choose_digit(hist, lane, shift, st);
-        wave_sync();
+#pragma unroll 1
+        for (int shift = 32 - kTopBits - 8; st.need < st.in_bin; shift = shift > 8 ? shift - 8 : 0) {
+            reinterpret_cast<uint4 *>(hist)[lane] = make_uint4(0u, 0u, 0u, 0u);
+            wave_sync();
+            if (compact) {
+                for (uint32_t c = lane; c < n_surv; c += kWave) {
+                    const uint32_t k = survivors[c];
+                    if ((k & st.mask) == st.prefix)
+                        atomicAdd(&hist[(k >> shift) & 0xffu], 1u);
+                }
+            } else {
+#pragma unroll
+                for (int s = 0; s < S; ++s)
+                    if (kWave * s < nb && (key[s] & st.mask) == st.prefix)
+                        atomicAdd(&hist[(key[s] >> shift) & 0xffu], 1u);
+            }
+            wave_sync();
+            choose_digit(hist, lane, shift, st);
+            wave_sync();
+            if (shift == 0)
+                break; // every bit fixed: st.prefix is the keep-th largest key
+        }
     }
 
-    // st.prefix is now the keep-th largest key T; st.in_bin keys equal T and
-    // st.need of them are kept.  Exactly keep blocks are selected; the bound
-    // on `at` only guards the stores.
+    // Kept: every key above T = st.prefix and, of the in_bin keys equal to
+    // it, the st.need of lowest index -- when st.need == st.in_bin simply
+    // every key >= st.prefix (the bits below the mask are zero in it).  A
+    // slot whose kept keys would run past keep (never, as exactly keep are
+    // kept) writes nothing: the test is on wave-uniform counts.
     const uint32_t T = st.prefix;
-    const bool all_ties = st.need == st.in_bin; // wave-uniform
-    uint32_t written = 0u, ties = 0u;
-#pragma unroll
-    for (int r = 0; r < RV; ++r) {
-        bool sel[4];
-        uint32_t c = 0u;
-        if (all_ties) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                sel[e] = valid(r, e) && key[r][e] >= T;
-                c += sel[e] ? 1u : 0u;
-            }
-        } else {
-            bool eq[4];
-            uint32_t c_eq = 0u, eq_total;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                eq[e] = valid(r, e) && key[r][e] == T;
-                c_eq += eq[e] ? 1u : 0u;
-            }
-            uint32_t rank = ties + lane_offset(c_eq, eq_total); // tie rank of this lane's first tie
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                sel[e] = (valid(r, e) && key[r][e] > T) || (eq[e] && rank < st.need);
-                rank += eq[e] ? 1u : 0u;
-                c += sel[e] ? 1u : 0u;
-            }
-            ties += eq_total;
+    int32_t block; // lane's block index in the current slot, advanced per slot
+    asm volatile("v_mov_b32 %0, %1" : "=v"(block) : "v"(lane));
+    char *out_bytes = reinterpret_cast<char *>(out);
+    uint32_t written = 0u;
+    auto emit = [&](bool sel) {
+        const uint64_t ms = __ballot(sel);
+        const uint32_t n = (uint32_t)__builtin_popcountll(ms);
+        if (written + n <= (uint32_t)keep && sel) {
+            const uint32_t at = __builtin_amdgcn_mbcnt_hi((uint32_t)(ms >> 32),
+                                                          __builtin_amdgcn_mbcnt_lo((uint32_t)ms, written));
+            *reinterpret_cast<int32_t *>(out_bytes + (at << 2)) = block;
         }
-        uint32_t total;
-        uint32_t at = written + lane_offset(c, total);
+        written += n;
+        block += kWave;
+    };
+    if (st.need == st.in_bin) { // wave-uniform
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-            if (sel[e]) {
-                if (at < (uint32_t)keep)
-                    out[at] = 256 * r + 4 * lane + e;
-                ++at;
+        for (int s = 0; s < S; ++s)
+            if (kWave * s < nb)
+                emit(key[s] >= T);
+    } else {
+        uint32_t ties = 0u;
+#pragma unroll
+        for (int s = 0; s < S; ++s)
+            if (kWave * s < nb) {
+                const bool eq = key[s] == T;
+                const uint64_t me = __ballot(eq);
+                emit(key[s] > T || (eq && ties + (uint32_t)lanes_below(me) < st.need));
+                ties += (uint32_t)__builtin_popcountll(me);
             }
-        written += total;
     }
 }
 
 // One wave (one workgroup) per query block; grid (nb, H, B).  Lane l loads
-// key blocks 256 r + 4 l .. 256 r + 4 l + 3 with one 16-byte load per r and
-// keeps their keys in registers, then selects (select_top_keys).  Up to 2048
-// blocks the kernel is held to 80 VGPRs (six waves per SIMD; the compiler
-// would take 79-87): 0-8% faster at 1953 blocks on three kinds of inputs.
-template <int RV>
-__global__ __launch_bounds__(kWave, RV <= 8 ? 6 : 3) void subblock_topk_kernel(const float *__restrict__ scores,
+// the scores of key blocks l, l + 64, ... (S of them) and keeps their keys in
+// registers, then selects (select_keep).  The launcher picks the smallest S
+// with 64 S >= nb, so for S > 4 the first S / 2 slots are whole and load
+// without a bound; the others load the last block in place of blocks past it
+// (every load is issued before any is used) and then set those keys to 0.
+template <int S>
+__global__ __launch_bounds__(kWave) void subblock_topk_kernel(const float *__restrict__ scores,
                                                               int32_t *__restrict__ kept, int nb, int ld, int keep,
                                                               int H)
 {
@@ -685,19 +648,19 @@ __global__ __launch_bounds__(kWave, RV <= 8 ? 6 : 3) void subblock_topk_kernel(c
     const int lane = threadIdx.x;
     const size_t row = ((size_t)blockIdx.z * H + blockIdx.y) * nb + blockIdx.x;
     const float *s = scores + row * ld;
+    constexpr int kWhole = S > 4 ? S / 2 : 0;
 
-    uint32_t key[RV][4];
+    float v[S];
 #pragma unroll
-    for (int r = 0; r < RV; ++r) {
-        const int j0 = 256 * r + 4 * lane;
-        f32x4 v = {0.f, 0.f, 0.f, 0.f};
-        if (j0 < nb) // the row is 16-byte aligned and ld >= nb rounded up to 4
-            v = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(s + j0));
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            key[r][e] = score_key(v[e]);
+    for (int q = 0; q < S; ++q) {
+        const int j = kWave * q + lane;
+        v[q] = __builtin_nontemporal_load(s + (q < kWhole ? j : min(j, nb - 1)));
     }
-    select_top_keys<RV>(key, nb, keep, lane, lds, kept + row * keep);
+    uint32_t key[S];
+#pragma unroll
+    for (int q = 0; q < S; ++q)
+        key[q] = (q < kWhole || kWave * q + lane < nb) ? score_key(v[q]) : 0u;
+    select_keep<S>(key, nb, keep, lane, lds, kept + row * keep);
 }
 
 // ---------------------------------------------------------------- fused route
@@ -717,9 +680,10 @@ __global__ __launch_bounds__(kWave, RV <= 8 ? 6 : 3) void subblock_topk_kernel(c
 // the same MFMA 16x16x16 sequence over the dimensions as the score kernels,
 // so every score is the same bits.  The order-preserving keys of the chunk's
 // scores are staged in LDS, and each wave reads its own query blocks' 256
-// keys into the register slot of the chunk: lane l ends up with key blocks
-// 256 r + 4 l + e, the layout select_top_keys takes.  Phase 2 reuses the LDS
-// as one selection area per wave and the waves select independently.
+// keys into the register slots of the chunk: lane l ends up with key block
+// 64 s + l in slot s, the layout select_keep takes (0 past the last block).
+// Phase 2 reuses the LDS as one selection area per wave and the waves select
+// independently.
 //
 // RV = ceil(nb / 256) register slots per query block; RPW = 2 query blocks
 // per wave while RV <= 8 (up to 64 key registers of the 128 a wave has when
@@ -786,7 +750,7 @@ __global__ __launch_bounds__(kRouteWaves * kWave) void subblock_route_fused_kern
         // addresses of every chunk's loads at once); each chunk's keys enter
         // the last register slot and the earlier ones move down a slot, so
         // after RV chunks slot r holds chunk r.
-        uint32_t key[RPW][RV][4];
+        uint32_t key[RPW][4 * RV];
 #pragma unroll 1
         for (int c = 0; c < RV; ++c) {
             f32x4 acc[NRB];
@@ -831,17 +795,17 @@ __global__ __launch_bounds__(kRouteWaves * kWave) void subblock_route_fused_kern
             for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    lds_s[(16 * rb + 4 * quad + e) * kSRow + 16 * wave + r16] = score_key(acc[rb][e]);
+                    lds_s[(16 * rb + 4 * quad + e) * kSRow + 16 * wave + r16] =
+                        kChunkKeys * c + 16 * wave + r16 < nb ? score_key(acc[rb][e]) : 0u;
             __syncthreads();
 #pragma unroll
             for (int j = 0; j < RPW; ++j) {
-                const uint4 t = reinterpret_cast<const uint4 *>(&lds_s[(RPW * wave + j) * kSRow])[lane];
 #pragma unroll
-                for (int r = 0; r + 1 < RV; ++r)
+                for (int q = 0; q + 4 < 4 * RV; ++q)
+                    key[j][q] = key[j][q + 4];
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        key[j][r][e] = key[j][r + 1][e];
-                key[j][RV - 1][0] = t.x, key[j][RV - 1][1] = t.y, key[j][RV - 1][2] = t.z, key[j][RV - 1][3] = t.w;
+                for (int e = 0; e < 4; ++e)
+                    key[j][4 * RV - 4 + e] = lds_s[(RPW * wave + j) * kSRow + kWave * e + lane];
             }
             // the staging rows are written again only after the next chunk's barriers
         }
@@ -851,7 +815,7 @@ __global__ __launch_bounds__(kRouteWaves * kWave) void subblock_route_fused_kern
         for (int j = 0; j < RPW; ++j) {
             const int i = i0 + RPW * wave + j;
             if (i < nb) // wave-uniform
-                select_top_keys<RV>(key[j], nb, keep, lane, sel, kept + (bh * nb + (uint64_t)i) * keep);
+                select_keep<4 * RV>(key[j], nb, keep, lane, sel, kept + (bh * nb + (uint64_t)i) * keep);
         }
     }
 }
@@ -881,10 +845,10 @@ void launch_route_fused_dh(const float *qp, const float *kp, int32_t *kept, int 
     else launch_route_fused_dh_rv<DH, 16>(qp, kp, kept, nb, keep, H, B, stream);
 }
 
-template <int RV>
-void launch_topk_rv(const float *scores, int32_t *kept, int nb, int ld, int keep, int H, int B, hipStream_t stream)
+template <int S>
+void launch_topk_s(const float *scores, int32_t *kept, int nb, int ld, int keep, int H, int B, hipStream_t stream)
 {
-    hipLaunchKernelGGL(subblock_topk_kernel<RV>, dim3((unsigned)nb, (unsigned)H, (unsigned)B), dim3(kWave), 0, stream,
+    hipLaunchKernelGGL(subblock_topk_kernel<S>, dim3((unsigned)nb, (unsigned)H, (unsigned)B), dim3(kWave), 0, stream,
                        scores, kept, nb, ld, keep, H);
 }
 
@@ -997,11 +961,11 @@ hipError_t launch_subblock_route(const float *q_pooled, const float *k_pooled, f
     if (keep == 0)
         return hipGetLastError();
     const int kp = (int)keep;
-    if (n <= 256) launch_topk_rv<1>(scores, kept, n, l, kp, h, b, stream);
-    else if (n <= 512) launch_topk_rv<2>(scores, kept, n, l, kp, h, b, stream);
-    else if (n <= 1024) launch_topk_rv<4>(scores, kept, n, l, kp, h, b, stream);
-    else if (n <= 2048) launch_topk_rv<8>(scores, kept, n, l, kp, h, b, stream);
-    else launch_topk_rv<16>(scores, kept, n, l, kp, h, b, stream);
+    if (n <= 256) launch_topk_s<4>(scores, kept, n, l, kp, h, b, stream);
+    else if (n <= 512) launch_topk_s<8>(scores, kept, n, l, kp, h, b, stream);
+    else if (n <= 1024) launch_topk_s<16>(scores, kept, n, l, kp, h, b, stream);
+    else if (n <= 2048) launch_topk_s<32>(scores, kept, n, l, kp, h, b, stream);
+    else launch_topk_s<64>(scores, kept, n, l, kp, h, b, stream);
     return hipGetLastError();
 }
 
