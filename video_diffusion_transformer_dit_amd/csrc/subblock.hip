@@ -513,6 +513,15 @@ __device__ __forceinline__ void wave_sync()
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// A wave-uniform value the compiler cannot see through: each loop over the
+// slots tests `64 s < nb` against its own copy, so the tests are not merged
+// across loops into per-slot flags held for the whole selection.
+__device__ __forceinline__ int fresh_uniform(int x)
+{
+    asm volatile("" : "+s"(x));
+    return x;
+}
+
 // The keep largest of one query block's keys, written as ascending key-block
 // indices to out[0 .. keep-1]; executed by one whole wave, 1 <= keep <= nb.
 // Lane l holds the key of block 64 s + l in key[s] (s < S, 64 S >= nb), and 0
@@ -541,9 +550,10 @@ __device__ __forceinline__ void select_keep(const uint32_t (&key)[S], int nb, in
     for (int i = 0; i < kTopBins / (4 * kWave); ++i)
         reinterpret_cast<uint4 *>(hist)[lane + kWave * i] = make_uint4(0u, 0u, 0u, 0u);
     wave_sync();
+    int n = fresh_uniform(nb);
 #pragma unroll
     for (int s = 0; s < S; ++s)
-        if (kWave * s < nb) // wave-uniform
+        if (kWave * s < n) // wave-uniform
             atomicAdd(&hist[key[s] >> (32 - kTopBits)], 1u);
     wave_sync();
     choose_top_digit(hist, lane, st);
@@ -554,9 +564,10 @@ __device__ __forceinline__ void select_keep(const uint32_t (&key)[S], int nb, in
         const bool compact = st.in_bin <= (uint32_t)kMaxSurvivors; // wave-uniform
         uint32_t n_surv = 0u;
         if (compact) {
+            n = fresh_uniform(nb);
 #pragma unroll
             for (int s = 0; s < S; ++s)
-                if (kWave * s < nb) {
+                if (kWave * s < n) {
                     const bool m = (key[s] & st.mask) == st.prefix;
                     const uint64_t mm = __ballot(m);
                     if (mm) { // wave-uniform
@@ -581,9 +592,10 @@ __device__ __forceinline__ void select_keep(const uint32_t (&key)[S], int nb, in
                         atomicAdd(&hist[(k >> shift) & 0xffu], 1u);
                 }
             } else {
+                n = fresh_uniform(nb);
 #pragma unroll
                 for (int s = 0; s < S; ++s)
-                    if (kWave * s < nb && (key[s] & st.mask) == st.prefix)
+                    if (kWave * s < n && (key[s] & st.mask) == st.prefix)
                         atomicAdd(&hist[(key[s] >> shift) & 0xffu], 1u);
             }
             wave_sync();
@@ -606,25 +618,26 @@ __device__ __forceinline__ void select_keep(const uint32_t (&key)[S], int nb, in
     uint32_t written = 0u;
     auto emit = [&](bool sel) {
         const uint64_t ms = __ballot(sel);
-        const uint32_t n = (uint32_t)__builtin_popcountll(ms);
-        if (written + n <= (uint32_t)keep && sel) {
+        const uint32_t cnt = (uint32_t)__builtin_popcountll(ms);
+        if (written + cnt <= (uint32_t)keep && sel) {
             const uint32_t at = __builtin_amdgcn_mbcnt_hi((uint32_t)(ms >> 32),
                                                           __builtin_amdgcn_mbcnt_lo((uint32_t)ms, written));
             *reinterpret_cast<int32_t *>(out_bytes + (at << 2)) = block;
         }
-        written += n;
+        written += cnt;
         block += kWave;
     };
+    n = fresh_uniform(nb);
     if (st.need == st.in_bin) { // wave-uniform
 #pragma unroll
         for (int s = 0; s < S; ++s)
-            if (kWave * s < nb)
+            if (kWave * s < n)
                 emit(key[s] >= T);
     } else {
         uint32_t ties = 0u;
 #pragma unroll
         for (int s = 0; s < S; ++s)
-            if (kWave * s < nb) {
+            if (kWave * s < n) {
                 const bool eq = key[s] == T;
                 const uint64_t me = __ballot(eq);
                 emit(key[s] > T || (eq && ties + (uint32_t)lanes_below(me) < st.need));
