@@ -551,10 +551,12 @@ __device__ __forceinline__ void select_keep(const uint32_t (&key)[S], int nb, in
         reinterpret_cast<uint4 *>(hist)[lane + kWave * i] = make_uint4(0u, 0u, 0u, 0u);
     wave_sync();
     int n = fresh_uniform(nb);
+    uint32_t one; // held in a register (the compiler would set it again before every atomic)
+    asm volatile("v_mov_b32 %0, 1" : "=v"(one));
 #pragma unroll
     for (int s = 0; s < S; ++s)
         if (kWave * s < n) // wave-uniform
-            atomicAdd(&hist[key[s] >> (32 - kTopBits)], 1u);
+            atomicAdd(&hist[key[s] >> (32 - kTopBits)], one);
     wave_sync();
     choose_top_digit(hist, lane, st);
     wave_sync();
