@@ -428,15 +428,35 @@ __device__ __forceinline__ int lanes_below(uint64_t mask)
     return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
-// Sum of x over lanes lane .. 63.
-__device__ __forceinline__ uint32_t suffix_sum(uint32_t x, int lane)
+// x from the lane `ctrl` names (DPP), 0 where the source lane is out of
+// range or the row / bank masks leave the lane out.
+template <int CTRL, int ROW_MASK = 0xf, int BANK_MASK = 0xf>
+__device__ __forceinline__ uint32_t dpp_or_zero(uint32_t x)
 {
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-        const uint32_t o = __shfl_down(x, off, kWave);
-        x += (lane + off < kWave) ? o : 0u;
-    }
-    return x;
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, ROW_MASK, BANK_MASK, true);
+}
+
+// Sum of x over lanes 0 .. lane: within each row of 16 lanes by row shifts
+// (1, 2, 3, then 4 and 8 on the upper banks), then across rows by broadcasting
+// lane 15 into row 1 and 3 and lane 31 into rows 2 and 3 (the GCN DPP scan).
+__device__ __forceinline__ uint32_t prefix_sum(uint32_t x)
+{
+    uint32_t t = x + dpp_or_zero<0x111>(x); // row_shr:1
+    t += dpp_or_zero<0x112>(x);             // row_shr:2
+    t += dpp_or_zero<0x113>(x);             // row_shr:3
+    t += dpp_or_zero<0x114, 0xf, 0xe>(t);   // row_shr:4, banks 1-3
+    t += dpp_or_zero<0x118, 0xf, 0xc>(t);   // row_shr:8, banks 2-3
+    t += dpp_or_zero<0x142, 0xa, 0xf>(t);   // row_bcast:15 into rows 1, 3
+    t += dpp_or_zero<0x143, 0xc, 0xf>(t);   // row_bcast:31 into rows 2, 3
+    return t;
+}
+
+// Sum of x over lanes lane .. 63: the wave total less the sum below the lane.
+__device__ __forceinline__ uint32_t suffix_sum(uint32_t x)
+{
+    const uint32_t incl = prefix_sum(x);
+    const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)incl, kWave - 1);
+    return total - incl + x;
 }
 
 // Radix-select state: keys matching `prefix` under `mask` are still
@@ -460,13 +480,13 @@ __device__ __forceinline__ void choose_top_digit(const uint32_t *hist, int lane,
     const uint4 a = h4[0], b = h4[1], c = h4[2], d = h4[3];
     const uint32_t cnt = (a.x + a.y + a.z + a.w) + (b.x + b.y + b.z + b.w) + (c.x + c.y + c.z + c.w) +
                          (d.x + d.y + d.z + d.w);
-    const uint32_t suffix = suffix_sum(cnt, lane);
+    const uint32_t suffix = suffix_sum(cnt);
     const uint32_t above = suffix - cnt;
     const int L = __builtin_ctzll(__ballot(above < st.need && st.need <= suffix)); // exactly one lane
     const uint32_t above_l = (uint32_t)__builtin_amdgcn_readlane(above, L);
     uint32_t h = hist[(16 * L + lane) & (kTopBins - 1)];
     h = lane < 16 ? h : 0u;
-    const uint32_t greater = above_l + suffix_sum(h, lane) - h; // keys of the larger digits
+    const uint32_t greater = above_l + suffix_sum(h) - h; // keys of the larger digits
     const int D = __builtin_ctzll(__ballot(greater < st.need && st.need <= greater + h));
     st.prefix = (uint32_t)(16 * L + D) << (32 - kTopBits);
     st.mask = ~0u << (32 - kTopBits);
@@ -480,7 +500,7 @@ __device__ __forceinline__ void choose_digit(const uint32_t *hist, int lane, int
 {
     const uint4 h4 = reinterpret_cast<const uint4 *>(hist)[lane];
     const uint32_t c = h4.x + h4.y + h4.z + h4.w;
-    const uint32_t suffix = suffix_sum(c, lane); // keys of digits >= 4l
+    const uint32_t suffix = suffix_sum(c); // keys of digits >= 4l
     const uint32_t above = suffix - c;
     const bool mine = above < st.need && st.need <= suffix; // exactly one lane
     uint32_t digit = 4u * lane, greater = above, count = h4.x;
@@ -524,7 +544,8 @@ __device__ __forceinline__ int fresh_uniform(int x)
 
 // The keep largest of one query block's keys, written as ascending key-block
 // indices to out[0 .. keep-1]; executed by one whole wave, 1 <= keep <= nb.
-// Lane l holds the key of block 64 s + l in key[s] (s < S, 64 S >= nb), and 0
+// Lane l holds the key of block 64 s + l in key[s] (s < S, 64 S >= nb, and
+// 64 S / 2 < nb when S > 4, so the first half of the slots is whole), and 0
 // in the slots of blocks at or past nb: below every score's key and past
 // every real block's index, so those slots are never among the kept ones and
 // need no test.  `lds` is the wave's own kSelectWords words, 16-byte aligned:
@@ -545,6 +566,7 @@ __device__ __forceinline__ void select_keep(const uint32_t (&key)[S], int nb, in
     uint32_t *hist = lds;
     uint32_t *survivors = lds + kTopBins;
     RadixState st = {0u, 0u, (uint32_t)keep, 0u};
+    constexpr int kWhole = S > 4 ? S / 2 : 0; // slots known to be whole: no test
 
 #pragma unroll
     for (int i = 0; i < kTopBins / (4 * kWave); ++i)
@@ -555,7 +577,7 @@ __device__ __forceinline__ void select_keep(const uint32_t (&key)[S], int nb, in
     asm volatile("v_mov_b32 %0, 1" : "=v"(one));
 #pragma unroll
     for (int s = 0; s < S; ++s)
-        if (kWave * s < n) // wave-uniform
+        if (s < kWhole || kWave * s < n) // wave-uniform
             atomicAdd(&hist[key[s] >> (32 - kTopBits)], one);
     wave_sync();
     choose_top_digit(hist, lane, st);
@@ -567,17 +589,19 @@ __device__ __forceinline__ void select_keep(const uint32_t (&key)[S], int nb, in
         uint32_t n_surv = 0u;
         if (compact) {
             n = fresh_uniform(nb);
+            char *surv_bytes = reinterpret_cast<char *>(survivors);
 #pragma unroll
             for (int s = 0; s < S; ++s)
-                if (kWave * s < n) {
+                if (s < kWhole || kWave * s < n) {
                     const bool m = (key[s] & st.mask) == st.prefix;
                     const uint64_t mm = __ballot(m);
                     if (mm) { // wave-uniform
-                        // exactly in_bin keys match, so every place is below the bound
+                        // exactly in_bin keys match, so every place is below the bound (the
+                        // mask only keeps the address inside the list whatever happens)
                         if (m)
-                            survivors[__builtin_amdgcn_mbcnt_hi((uint32_t)(mm >> 32),
-                                                                __builtin_amdgcn_mbcnt_lo((uint32_t)mm, n_surv))] =
-                                key[s];
+                            *reinterpret_cast<uint32_t *>(
+                                surv_bytes + ((((uint32_t)lanes_below(mm) << 2) + (n_surv << 2)) &
+                                              (uint32_t)(4 * kMaxSurvivors - 1))) = key[s];
                         n_surv += (uint32_t)__builtin_popcountll(mm);
                     }
                 }
@@ -597,7 +621,7 @@ __device__ __forceinline__ void select_keep(const uint32_t (&key)[S], int nb, in
                 n = fresh_uniform(nb);
 #pragma unroll
                 for (int s = 0; s < S; ++s)
-                    if (kWave * s < n && (key[s] & st.mask) == st.prefix)
+                    if ((s < kWhole || kWave * s < n) && (key[s] & st.mask) == st.prefix)
                         atomicAdd(&hist[(key[s] >> shift) & 0xffu], 1u);
             }
             wave_sync();
@@ -621,11 +645,8 @@ __device__ __forceinline__ void select_keep(const uint32_t (&key)[S], int nb, in
     auto emit = [&](bool sel) {
         const uint64_t ms = __ballot(sel);
         const uint32_t cnt = (uint32_t)__builtin_popcountll(ms);
-        if (written + cnt <= (uint32_t)keep && sel) {
-            const uint32_t at = __builtin_amdgcn_mbcnt_hi((uint32_t)(ms >> 32),
-                                                          __builtin_amdgcn_mbcnt_lo((uint32_t)ms, written));
-            *reinterpret_cast<int32_t *>(out_bytes + (at << 2)) = block;
-        }
+        if (written + cnt <= (uint32_t)keep && sel)
+            *reinterpret_cast<int32_t *>(out_bytes + (((uint32_t)lanes_below(ms) << 2) + (written << 2))) = block;
         written += cnt;
         block += kWave;
     };
@@ -633,13 +654,13 @@ __device__ __forceinline__ void select_keep(const uint32_t (&key)[S], int nb, in
     if (st.need == st.in_bin) { // wave-uniform
 #pragma unroll
         for (int s = 0; s < S; ++s)
-            if (kWave * s < n)
+            if (s < kWhole || kWave * s < n)
                 emit(key[s] >= T);
     } else {
         uint32_t ties = 0u;
 #pragma unroll
         for (int s = 0; s < S; ++s)
-            if (kWave * s < n) {
+            if (s < kWhole || kWave * s < n) {
                 const bool eq = key[s] == T;
                 const uint64_t me = __ballot(eq);
                 emit(key[s] > T || (eq && ties + (uint32_t)lanes_below(me) < st.need));
@@ -650,26 +671,33 @@ __device__ __forceinline__ void select_keep(const uint32_t (&key)[S], int nb, in
 
 // One wave (one workgroup) per query block; grid (nb, H, B).  Lane l loads
 // the scores of key blocks l, l + 64, ... (S of them) and keeps their keys in
-// registers, then selects (select_keep).  The launcher picks the smallest S
-// with 64 S >= nb, so for S > 4 the first S / 2 slots are whole and load
-// without a bound; the others load the last block in place of blocks past it
-// (every load is issued before any is used) and then set those keys to 0.
+// registers, then selects (select_keep).  The loads go through a buffer
+// descriptor over the row's nb scores: lane offset and slot offset are fixed
+// (no address arithmetic per slot), every load is issued before any is used,
+// and blocks past nb read 0 from the range check and are then given key 0.
+// The launcher picks the smallest S with 64 S >= nb, so for S > 4 the first
+// S / 2 slots are whole and need no test.
 template <int S>
 __global__ __launch_bounds__(kWave) void subblock_topk_kernel(const float *__restrict__ scores,
                                                               int32_t *__restrict__ kept, int nb, int ld, int keep,
                                                               int H)
 {
     __shared__ __align__(16) uint32_t lds[kSelectWords];
+    constexpr int kRawFormat = 0x00020000; // descriptor dword 3: 32-bit data format, no swizzle or stride
+    constexpr int kWhole = S > 4 ? S / 2 : 0;
+    constexpr int kSlotsPerOffset = 4096 / (4 * kWave); // slots the 12-bit instruction offset reaches
     const int lane = threadIdx.x;
     const size_t row = ((size_t)blockIdx.z * H + blockIdx.y) * nb + blockIdx.x;
-    const float *s = scores + row * ld;
-    constexpr int kWhole = S > 4 ? S / 2 : 0;
+    const __amdgpu_buffer_rsrc_t rd =
+        __builtin_amdgcn_make_buffer_rsrc((void *)(scores + row * ld), 0, nb * 4, kRawFormat);
 
     float v[S];
 #pragma unroll
     for (int q = 0; q < S; ++q) {
-        const int j = kWave * q + lane;
-        v[q] = __builtin_nontemporal_load(s + (q < kWhole ? j : min(j, nb - 1)));
+        // lane offset + a multiple of 4 KiB in the register, the rest in the instruction
+        const int base = 4 * lane + 4096 * (q / kSlotsPerOffset);
+        v[q] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                             rd, base + 4 * kWave * (q % kSlotsPerOffset), 0, 2 /* nt */));
     }
     uint32_t key[S];
 #pragma unroll
