@@ -468,7 +468,8 @@ struct RadixState {
 constexpr int kTopBits = 10;                   // the first digit: a key's top ten bits
 constexpr int kTopBins = 1 << kTopBits;
 constexpr int kMaxSurvivors = 512;
-constexpr int kSelectWords = kTopBins + kMaxSurvivors; // LDS words one selecting wave uses
+constexpr int kSelectWords = kTopBins; // LDS words one selecting wave uses (survivors overlay the histogram)
+static_assert(256 + kMaxSurvivors <= kTopBins, "survivors sit past the 256 bins the later digits use");
 
 // Picks the first digit from its 1024-bin histogram: the largest digit whose
 // keys, with those of all larger digits, reach `need`.  Lane l sums bins
@@ -549,7 +550,9 @@ __device__ __forceinline__ int fresh_uniform(int x)
 // in the slots of blocks at or past nb: below every score's key and past
 // every real block's index, so those slots are never among the kept ones and
 // need no test.  `lds` is the wave's own kSelectWords words, 16-byte aligned:
-// a 1024-bin histogram, then room for kMaxSurvivors keys.
+// the 1024-bin histogram of the first digit; once that digit is chosen,
+// words 256 .. 256 + kMaxSurvivors - 1 take the survivors and words 0 .. 255
+// the 256-bin histograms of the later digits.
 // A radix select finds the keep-th largest key T, most significant digit
 // first: a histogram of the top ten bits (LDS atomics, one per key) fixes the
 // first digit, the keys sharing it are compacted into LDS (each slot's
@@ -564,7 +567,7 @@ __device__ __forceinline__ void select_keep(const uint32_t (&key)[S], int nb, in
                                             int32_t *__restrict__ out)
 {
     uint32_t *hist = lds;
-    uint32_t *survivors = lds + kTopBins;
+    uint32_t *survivors = lds + 256;
     RadixState st = {0u, 0u, (uint32_t)keep, 0u};
     constexpr int kWhole = S > 4 ? S / 2 : 0; // slots known to be whole: no test
 
