@@ -248,6 +248,29 @@ def test_route_fused_equals_scores_then_topk(shape):
     check_kept_lists(to_host(kf), nb, dit.dit_subblock_keep(nb, 0.8))
 
 
+# The top-k and the fused route pick their register slots per nb (S = 4, 8,
+# 16, 32 or 64 slots of 64 blocks) and skip the nb test on the first half of
+# the slots, which is whole for every nb a bucket serves; these are the
+# bucket edges, where the last slot is either full or holds a single block.
+@pytest.mark.parametrize("nb", [256, 257, 512, 513, 1024, 1025, 2048, 2049, 4096])
+def test_route_slot_bucket_edges(nb):
+    B, H, Dh = 1, 2, 32
+    qp, kp = route_inputs((B, H, nb, Dh), seed=500 + nb)
+    s_ref = oracle.subblock_scores(qp.double().numpy(), kp.double().numpy())
+    e = score_bound(qp.double().numpy(), kp.double().numpy())
+    qd, kd = qp.to(DEV), kp.to(DEV)
+    for keep in sorted({1, nb // 4, nb - 1, nb}):
+        kept, scores = dit.dit_subblock_route(qd, kd, keep=keep)
+        kf = fused_kept(qd, kd, keep=keep)
+        torch.cuda.synchronize()
+        s_gpu = to_host(scores)[..., :nb].astype(np.float64)
+        kh = to_host(kept)
+        check_kept_lists(kh, nb, keep)
+        check_valid_against_oracle(kh, s_ref, e)
+        check_top_set_of_own_scores(kh, s_gpu)
+        assert torch.equal(kf, kept), f"nb {nb}, keep {keep}: fused route differs from scores + top-k"
+
+
 def test_route_deterministic_and_buffers_reused():
     shape = (1, 3, 300, 128)
     qp, kp = route_inputs(shape, seed=41)
