@@ -731,18 +731,20 @@ __global__ __launch_bounds__(kWave) void subblock_topk_kernel(const float *__res
 // Phase 2 reuses the LDS as one selection area per wave and the waves select
 // independently.
 //
-// RV = ceil(nb / 256) register slots per query block; RPW = 2 query blocks
-// per wave while RV <= 8 (up to 64 key registers of the 128 a wave has when
-// 16 share a CU), else 1.  Workgroups walk (sample, head, strip) items; the
+// RV = ceil(nb / 256) chunks, so 4 RV key slots per query block; RPW = 2
+// query blocks per wave while RV <= 8 (up to 64 key registers of the 128 a
+// wave has when 16 share a CU), else 1.  Workgroups walk (sample, head, strip) items; the
 // XCD of workgroup g (g % 8, dispatch is round-robin) takes the (g % 8)-th
 // contiguous eighth of the items, so the 32 workgroups an XCD runs at once
 // share one head's key means in its L2.
 //
 // What bounds it (1344x768 5 s, 1953 blocks, 32 heads): each strip re-reads
 // its head's key means, 16 bytes of L2 traffic per score against the score
-// kernel's 4 (128 x 128 tiles), and the keys of a strip fill the register
-// file, so one workgroup runs per CU and its load, multiply and select phases
-// do not overlap with another's.
+// kernel's 4 (128 x 128 tiles): 2 GB in all, which L2 serves at about 9 TB/s
+// (a copy of the kernel that only streams the chunks takes ~230 us).  The
+// keys of a strip fill the register file, so the strip cannot grow, one
+// workgroup runs per CU, and its load, multiply and select phases do not
+// overlap with another's.
 constexpr int kRouteWaves = 16;
 constexpr int kChunkKeys = 256;
 
@@ -793,9 +795,9 @@ __global__ __launch_bounds__(kRouteWaves * kWave) void subblock_route_fused_kern
         }
 
         // A runtime loop over the chunks (unrolled, the compiler would hold the
-        // addresses of every chunk's loads at once); each chunk's keys enter
-        // the last register slot and the earlier ones move down a slot, so
-        // after RV chunks slot r holds chunk r.
+        // addresses of every chunk's loads at once, and spill); each chunk's
+        // keys enter the last four register slots and the earlier ones move
+        // down four, so after RV chunks slots 4 r .. 4 r + 3 hold chunk r.
         uint32_t key[RPW][4 * RV];
 #pragma unroll 1
         for (int c = 0; c < RV; ++c) {
