@@ -480,7 +480,8 @@ def main(argv=None) -> int:
 
     # SubBlock routing front-end on the chain's q', k' at sparsity 0.75: block
     # means (both input layouts), block scores alone (keep = 0 runs only the
-    # score kernel), then scores plus the kept blocks.
+    # score kernel), then scores plus the kept blocks (top-k = the difference,
+    # both timed in the same context).
     def timed(fn):
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
         for i in range(args.warmup + args.steps):
@@ -512,8 +513,35 @@ def main(argv=None) -> int:
     ko_as_hm = ko.view(wl.B, wl.H, wl.N, wl.Dh)
     pool_hm_ms = timed(lambda: dit.dit_subblock_pool(qo_as_hm, ko_as_hm, head_major=True, q_pooled=qp_s,
                                                      k_pooled=kp_s, stream=stream))
-    scores_ms = timed(lambda: dit.dit_subblock_route(qp_s, kp_s, keep=0, scores=sc, kept=kept0, stream=stream))
-    route_ms = timed(lambda: dit.dit_subblock_route(qp_s, kp_s, keep=keep, scores=sc, kept=kept, stream=stream))
+    # Scores alone (keep = 0 runs only the score kernel) and the full route,
+    # each timed right after a full route: the score kernel's time depends on
+    # what ran before it (after a top-k has read the whole score matrix it is
+    # not the same as back to back), so top-k = route - scores compares like
+    # with like.  Per step: the route (timed), scores alone (timed), the route
+    # (untimed, so that the next timed route also follows one).
+    def route_call():
+        dit.dit_subblock_route(qp_s, kp_s, keep=keep, scores=sc, kept=kept, stream=stream)
+
+    def scores_call():
+        dit.dit_subblock_route(qp_s, kp_s, keep=0, scores=sc, kept=kept0, stream=stream)
+
+    rev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    route_call()
+    for i in range(args.warmup + args.steps):
+        e = rev[i - args.warmup] if i >= args.warmup else None
+        if e:
+            e[0].record(stream)
+        route_call()
+        if e:
+            e[1].record(stream)
+            e[2].record(stream)
+        scores_call()
+        if e:
+            e[3].record(stream)
+        route_call()
+    torch.cuda.synchronize()
+    route_ms = sum(e[0].elapsed_time(e[1]) for e in rev) / args.steps
+    scores_ms = sum(e[2].elapsed_time(e[3]) for e in rev) / args.steps
     # the same kept lists with the scores kept on chip (one fused kernel, no score matrix)
     kept_f = torch.empty_like(kept)
     fused_route_ms = timed(lambda: dit.dit_subblock_route(qp_s, kp_s, keep=keep, kept=kept_f, write_scores=False,
