@@ -76,7 +76,7 @@ KERNEL_SOURCES = {
     "route_fused": "subblock.hip",
     "copy": "copy.hip",
     **{p: "patterns.hip" for p in ("p_read", "p_write", "p_swiglu", "p_residual", "p_adaln", "p_residual_adaln",
-                                   "p_head_major")},
+                                   "p_head_major", "p_score_tiles", "p_topk_rows")},
 }
 # Kernels of the next rows, measured after the chain (see main()).
 NEXT_OPS = ("residual_adaln", "qk_layout", "qk_pool_layout", "change", "change_final", "qk_pool", "pool", "pool_hm",
@@ -119,6 +119,8 @@ def op_bytes(wl, next_rows: bool = False) -> dict:
             "p_adaln": R * 4 * D,
             "p_residual_adaln": R * 8 * D,
             "p_head_major": R * 4 * H * Dh,
+            "p_score_tiles": pooled + B * H * nb * nb * 4,   # the score kernel's bytes (head dim 128)
+            "p_topk_rows": B * H * nb * nb * 4 + B * H * nb * (-(-nb // 4)) * 4,  # top-k's bytes at keep = nb / 4
         })
     return out
 
@@ -542,6 +544,37 @@ def main(argv=None) -> int:
     torch.cuda.synchronize()
     route_ms = sum(e[0].elapsed_time(e[1]) for e in rev) / args.steps
     scores_ms = sum(e[2].elapsed_time(e[3]) for e in rev) / args.steps
+
+    # The two kernels' traffic with no arithmetic, each where its kernel runs:
+    # the score tiles (DIT_STREAM_SCORE_TILES, head dim 128 only) right after a
+    # full route, the top-k rows (DIT_STREAM_TOPK_ROWS, ceil(nb / 4) words per
+    # row: the kept count at this sparsity) right after the score tiles have
+    # written the matrix, and a route after both, so that every score kernel
+    # launch still follows a full pass over the matrix.
+    has_pattern = wl.Dh == 128 and keep == -(-nb // 4)
+    score_pattern_ms = topk_pattern_ms = None
+    if has_pattern:
+        kept_p = torch.empty((wl.B * wl.H * nb * keep,), dtype=torch.int32, device=dev)
+        pev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+        route_call()
+        for i in range(args.warmup + args.steps):
+            e = pev[i - args.warmup] if i >= args.warmup else None
+            if e:
+                e[0].record(stream)
+            dit.dit_stream_pattern(dit.DIT_STREAM_SCORE_TILES, wl.B * wl.H * nb, 4 * ld, in0=qp_s, in1=kp_s, out0=sc,
+                                   heads=nb, stream=stream)
+            if e:
+                e[1].record(stream)
+                e[2].record(stream)
+            dit.dit_stream_pattern(dit.DIT_STREAM_TOPK_ROWS, wl.B * wl.H * nb, 4 * ld, in0=sc, out0=kept_p, heads=nb,
+                                   stream=stream)
+            if e:
+                e[3].record(stream)
+            route_call()
+        torch.cuda.synchronize()
+        score_pattern_ms = sum(e[0].elapsed_time(e[1]) for e in pev) / args.steps
+        topk_pattern_ms = sum(e[2].elapsed_time(e[3]) for e in pev) / args.steps
+        del kept_p
     # the same kept lists with the scores kept on chip (one fused kernel, no score matrix)
     kept_f = torch.empty_like(kept)
     fused_route_ms = timed(lambda: dit.dit_subblock_route(qp_s, kp_s, keep=keep, kept=kept_f, write_scores=False,
@@ -616,6 +649,21 @@ def main(argv=None) -> int:
     # kernel's own launch shape (dit_stream_pattern), on buffers of the same
     # sizes; the chain's outputs are left intact for the oracle check below.
     ceilings = pattern_ceilings(dit, wl, ins, ops, fused_ms, layout_ms, timed, dev)
+    if score_pattern_ms:
+        ceilings["scores_shape"] = {
+            "avg_ms": round(score_pattern_ms, 5), "bytes": scores_bytes,
+            "GB_s": round(scores_bytes / (score_pattern_ms * 1e-3) / 1e9, 1),
+            "pct_of_peak": round(100.0 * scores_bytes / (score_pattern_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
+            "kernel_over_pattern": round(scores_ms / score_pattern_ms, 4),
+            "timing": "each call right after a full route, as the score kernel's"}
+    if topk_pattern_ms:
+        ceilings["topk_shape"] = {
+            "avg_ms": round(topk_pattern_ms, 5), "bytes": topk_bytes,
+            "GB_s": round(topk_bytes / (topk_pattern_ms * 1e-3) / 1e9, 1),
+            "pct_of_peak": round(100.0 * topk_bytes / (topk_pattern_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
+            "kernel_over_pattern": round(topk_ms / topk_pattern_ms, 4),
+            "timing": "each call right after the score tiles have written the matrix, as top-k follows the score "
+                      "kernel inside the route"}
 
     mix_ms = 2 * ops["adaln"]["avg_ms"] + ops["qk"]["avg_ms"] + 2 * ops["residual"]["avg_ms"] + ops["swiglu"]["avg_ms"]
     mix_bytes = 2 * nbytes["adaln"] + nbytes["qk"] + 2 * nbytes["residual"] + nbytes["swiglu"]
@@ -986,6 +1034,8 @@ KERNEL_OPS = (
     (r"pattern_row_wave_kernel<\d+, false,", "p_adaln"),
     (r"pattern_row_wave_kernel<\d+, true,", "p_residual_adaln"),
     (r"pattern_head_major_kernel", "p_head_major"),
+    (r"pattern_score_tiles_kernel", "p_score_tiles"),
+    (r"pattern_topk_rows_kernel", "p_topk_rows"),
     (r"gated_residual_adaln_kernel", "residual_adaln"),
     (r"adaln_modulate_kernel", "adaln"),
     (r"gated_residual_kernel", "residual"),
@@ -1168,7 +1218,8 @@ def summarize_rocprof(trace_dir: str, fetch_dir: str, write_dir: str, workload: 
 # pattern -> (kernel it bounds, launches of the pattern per kernel launch)
 PATTERN_BOUNDS = {"p_read": (None, 1), "p_write": (None, 1), "p_swiglu": ("swiglu", 1),
                   "p_residual": ("residual", 1), "p_adaln": ("adaln", 1), "p_residual_adaln": ("residual_adaln", 1),
-                  "p_head_major": ("qk_layout", 2)}
+                  "p_head_major": ("qk_layout", 2), "p_score_tiles": ("scores", 1),
+                  "p_topk_rows": ("topk", 1)}
 
 
 def write_ceilings_summary(stats: dict, nbytes: dict, wl, workload: str, commands: str, out_dir: str):
@@ -1179,7 +1230,8 @@ def write_ceilings_summary(stats: dict, nbytes: dict, wl, workload: str, command
              "(kernels_<workload>_trace.md), full-size launches only. `kernel / pattern` is the kernel's average "
              "duration over its pattern's (the head-major copy moves one of q and k per launch, so QK with "
              "head-major output is set against two of its launches; that kernel also reads q, k out of a fused "
-             "QKV buffer).", "",
+             "QKV buffer). The SubBlock patterns run where their kernels run: the score tiles right after a full "
+             "route, the top-k rows right after the score tiles have written the matrix.", "",
              "Commands (REPO = the repository root, OUT = an output directory for the raw rocprofv3 files):", "",
              "```", commands, "```", "",
              "| pattern | kernel | calls | avg us | bytes | GB/s | % of 8 TB/s | kernel avg us | kernel / pattern |",

@@ -460,6 +460,28 @@ dit_status dit_copy16(const void *src, void *dst, int64_t bytes, void *stream);
  *                            out0 [heads][rows][row_bytes/heads] (token-major
  *                            to head-major copy); row_bytes/16 a multiple of
  *                            heads; rows * ceil(row_bytes / 4096) < 2^24
+ *   DIT_STREAM_SCORE_TILES   the block-score traffic of dit_subblock_route at
+ *                            head dim 128, in that kernel's launch shape and
+ *                            tile order: here `heads` is the number of blocks
+ *                            n and rows = P * n (P planes).  Reads in0 and in1
+ *                            [rows][128] fp32 (query and key means; each query
+ *                            tile when it changes, every key tile), writes the
+ *                            n x n leading block of each plane of out0
+ *                            [rows][row_bytes] (columns up to n rounded up to
+ *                            4; row_bytes >= 16 * ceil(n / 4)).  With all-zero
+ *                            means the 32-bit word at (row r, column c) is
+ *                            (r * 65536 + c) mod 2^32; otherwise it is that
+ *                            XOR a fold of the words loaded.  P * ceil(n /
+ *                            128)^2 < 2^31
+ *   DIT_STREAM_TOPK_ROWS     the top-k traffic of dit_subblock_route, in that
+ *                            kernel's launch shape (one wave per row): `heads`
+ *                            is n and rows = P * n (P <= 65535, n <= 4096).
+ *                            Reads the first n fp32 words of each row of in0
+ *                            [rows][row_bytes] (row_bytes >= 4 * n) and writes
+ *                            out0 [rows][keep] int32 with keep = ceil(n / 4),
+ *                            the kept count at sparsity 0.75.  With an all-zero
+ *                            in0, word j of row r is (r * 65536 + j) mod 2^32;
+ *                            otherwise that XOR a fold of the words loaded
  * Limits: rows < 2^24; row_bytes <= 2^25; SPLIT_ROWS and TWO_IN as for
  * dit_swiglu and dit_gated_residual on the same rows and widths.  Pointers
  * 16-byte aligned; no output may overlap an input (DIT_ERR_ARG); unused
@@ -472,6 +494,8 @@ dit_status dit_copy16(const void *src, void *dst, int64_t bytes, void *stream);
 #define DIT_STREAM_ROW_WAVE 4
 #define DIT_STREAM_ROW_WAVE_2X2 5
 #define DIT_STREAM_HEAD_MAJOR 6
+#define DIT_STREAM_SCORE_TILES 7
+#define DIT_STREAM_TOPK_ROWS 8
 dit_status dit_stream_pattern(int32_t kind, const void *in0, const void *in1,
                               void *out0, void *out1, int64_t rows,
                               int64_t row_bytes, int64_t heads, void *stream);

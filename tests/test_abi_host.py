@@ -376,13 +376,14 @@ def test_copy_validation(lib):
 
 def test_stream_pattern_validation(lib):
     from video_diffusion_transformer_dit_amd import (DIT_STREAM_HEAD_MAJOR, DIT_STREAM_READ, DIT_STREAM_ROW_WAVE,
-                                                     DIT_STREAM_ROW_WAVE_2X2, DIT_STREAM_SPLIT_ROWS,
-                                                     DIT_STREAM_TWO_IN, DIT_STREAM_WRITE)
+                                                     DIT_STREAM_ROW_WAVE_2X2, DIT_STREAM_SCORE_TILES,
+                                                     DIT_STREAM_SPLIT_ROWS, DIT_STREAM_TOPK_ROWS, DIT_STREAM_TWO_IN,
+                                                     DIT_STREAM_WRITE)
 
     def f(kind=DIT_STREAM_TWO_IN, a=P, b=Q, o=R, o2=S, rows=4, width=8192, heads=0):
         return lib.dit_stream_pattern(kind, a, b, o, o2, rows, width, heads, None)
 
-    assert f(kind=7) == DIT_ERR_ARG and f(kind=-1) == DIT_ERR_ARG
+    assert f(kind=9) == DIT_ERR_ARG and f(kind=-1) == DIT_ERR_ARG
     assert f(rows=-1) == DIT_ERR_ARG and f(rows=1 << 24) == DIT_ERR_ARG
     assert f(width=8) == DIT_ERR_SHAPE and f(width=8200) == DIT_ERR_SHAPE and f(width=0) == DIT_ERR_SHAPE
     assert f(kind=DIT_STREAM_ROW_WAVE, width=16400) == DIT_ERR_SHAPE  # wave-per-row rows up to 16 KiB
@@ -399,6 +400,32 @@ def test_stream_pattern_validation(lib):
     assert f(kind=DIT_STREAM_ROW_WAVE_2X2, o2=R + 64) == DIT_ERR_ARG  # the two outputs overlap
     assert f(kind=DIT_STREAM_READ, o=P + 4 * 8192 - 16) == DIT_ERR_ARG  # sink inside the input
     assert f(rows=0, a=0, b=0, o=0, o2=0) == DIT_OK
+
+    def st(**kw):  # block-score tiles: heads = n blocks, rows = planes * n
+        args = dict(kind=DIT_STREAM_SCORE_TILES, rows=8, width=16, heads=4, o2=0)
+        args.update(kw)
+        return f(**args)
+
+    assert st(heads=0) == DIT_ERR_SHAPE
+    assert st(rows=10) == DIT_ERR_SHAPE  # not a whole number of planes
+    assert st(heads=8, width=16) == DIT_ERR_SHAPE  # 8 columns need 32 bytes per row
+    assert st(rows=1 << 23, heads=1 << 23, width=1 << 25) == DIT_ERR_ARG  # 2^32 tiles
+    assert st(b=0) == DIT_ERR_NULL  # both means are read
+    assert st(o=P + 8 * 512 - 16) == DIT_ERR_ARG  # output inside the [rows][128] fp32 query means
+    assert st(rows=0, a=0, b=0, o=0) == DIT_OK
+
+    def tk(**kw):  # top-k rows: heads = n blocks, rows = planes * n, keep = ceil(n / 4) words out per row
+        args = dict(kind=DIT_STREAM_TOPK_ROWS, rows=8, width=16, heads=4, b=0, o2=0)
+        args.update(kw)
+        return f(**args)
+
+    assert tk(heads=0) == DIT_ERR_SHAPE and tk(heads=4097, rows=4097, width=16400) == DIT_ERR_SHAPE
+    assert tk(rows=10) == DIT_ERR_SHAPE  # not a whole number of planes
+    assert tk(heads=8, width=16) == DIT_ERR_SHAPE  # 8 scores need 32 bytes per row
+    assert tk(rows=65536 * 2, heads=2) == DIT_ERR_ARG  # 65536 planes: past the grid's y limit
+    assert tk(a=0) == DIT_ERR_NULL
+    assert tk(o=P + 8 * 16 - 16) == DIT_ERR_ARG  # kept words inside the scores
+    assert tk(rows=0, a=0, o=0) == DIT_OK
 
 
 def test_binding_rejects_host_tensors():

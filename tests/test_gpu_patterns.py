@@ -85,3 +85,61 @@ def test_read_and_write():
     dit.dit_stream_pattern(dit.DIT_STREAM_READ, rows, row_bytes, in0=zeros, out0=sink)
     torch.cuda.synchronize()
     assert torch.equal(sink, torch.full((4,), 5, dtype=torch.int32, device=DEV))
+
+
+@pytest.mark.parametrize("planes,n,ld", [(1, 1, 4), (2, 5, 8), (3, 127, 128), (2, 128, 132), (2, 129, 132),
+                                         (1, 300, 304), (2, 1953, 1984), (32, 1953, 1984)])
+def test_score_tiles(planes, n, ld):
+    """Every word of each plane's n x n block (columns up to n rounded up to 4) is written with its tag when the
+    means are zero; the rest of each row keeps its fill; non-zero means change the words (the loads are live)."""
+    rows, row_bytes = planes * n, 4 * ld
+    print(f"[score_tiles] planes={planes} n={n} ld={ld}", flush=True)
+    qm = torch.zeros((rows, 128), dtype=torch.float32, device=DEV)
+    km = torch.zeros_like(qm)
+    out = torch.full((rows, ld), -7, dtype=torch.int32, device=DEV)
+    dit.dit_stream_pattern(dit.DIT_STREAM_SCORE_TILES, rows, row_bytes, in0=qm, in1=km, out0=out, heads=n)
+    torch.cuda.synchronize()
+    cols = -(-n // 4) * 4
+    r = torch.arange(rows, device=DEV, dtype=torch.int64).unsqueeze(1)
+    c = torch.arange(cols, device=DEV, dtype=torch.int64).unsqueeze(0)
+    tags = (r * 65536 + c) & 0xFFFFFFFF
+    assert torch.equal(out[:, :cols].to(torch.int64) & 0xFFFFFFFF, tags)
+    assert bool((out[:, cols:] == -7).all())
+    del tags
+    g = torch.Generator(device=DEV).manual_seed(8)
+    qm.copy_(torch.randn(qm.shape, generator=g, device=DEV))
+    km.copy_(torch.randn(km.shape, generator=g, device=DEV))
+    before = out.clone()
+    dit.dit_stream_pattern(dit.DIT_STREAM_SCORE_TILES, rows, row_bytes, in0=qm, in1=km, out0=out, heads=n)
+    torch.cuda.synchronize()
+    assert not torch.equal(out[:, :cols], before[:, :cols])
+    assert bool((out[:, cols:] == -7).all())
+
+
+@pytest.mark.parametrize("planes,n,ld", [(1, 1, 4), (2, 5, 8), (3, 200, 200), (2, 256, 260), (2, 257, 260),
+                                         (1, 1000, 1000), (2, 1953, 1984), (32, 1953, 1984), (1, 4096, 4096)])
+def test_topk_rows(planes, n, ld):
+    """Each row's ceil(n / 4) kept words carry their tags when the scores are zero (and nothing past them is
+    written); non-zero scores in the first n words change them, words past n in the row do not."""
+    rows, keep = planes * n, -(-n // 4)
+    print(f"[topk_rows] planes={planes} n={n} ld={ld}", flush=True)
+    scores = torch.zeros((rows, ld), dtype=torch.float32, device=DEV)
+    out = torch.full((rows * keep + 64,), -7, dtype=torch.int32, device=DEV)
+    dit.dit_stream_pattern(dit.DIT_STREAM_TOPK_ROWS, rows, 4 * ld, in0=scores, out0=out, heads=n)
+    torch.cuda.synchronize()
+    r = torch.arange(rows, device=DEV, dtype=torch.int64).unsqueeze(1)
+    j = torch.arange(keep, device=DEV, dtype=torch.int64).unsqueeze(0)
+    tags = ((r * 65536 + j) & 0xFFFFFFFF).reshape(-1)
+    got = out[:rows * keep].to(torch.int64) & 0xFFFFFFFF
+    assert torch.equal(got, tags)
+    assert bool((out[rows * keep:] == -7).all())
+    if ld > n:  # words past n are outside the loads' range: a change there changes nothing
+        scores[:, n:] = 3.0
+        dit.dit_stream_pattern(dit.DIT_STREAM_TOPK_ROWS, rows, 4 * ld, in0=scores, out0=out, heads=n)
+        torch.cuda.synchronize()
+        assert torch.equal(out[:rows * keep].to(torch.int64) & 0xFFFFFFFF, tags)
+    g = torch.Generator(device=DEV).manual_seed(9)
+    scores[:, :n] = torch.randn((rows, n), generator=g, device=DEV)
+    dit.dit_stream_pattern(dit.DIT_STREAM_TOPK_ROWS, rows, 4 * ld, in0=scores, out0=out, heads=n)
+    torch.cuda.synchronize()
+    assert not torch.equal(out[:rows * keep].to(torch.int64) & 0xFFFFFFFF, tags)

@@ -477,7 +477,7 @@ def dit_copy16(src, dst, stream=None):
 
 
 DIT_STREAM_READ, DIT_STREAM_WRITE, DIT_STREAM_SPLIT_ROWS, DIT_STREAM_TWO_IN, DIT_STREAM_ROW_WAVE, \
-    DIT_STREAM_ROW_WAVE_2X2, DIT_STREAM_HEAD_MAJOR = range(7)
+    DIT_STREAM_ROW_WAVE_2X2, DIT_STREAM_HEAD_MAJOR, DIT_STREAM_SCORE_TILES, DIT_STREAM_TOPK_ROWS = range(9)
 
 
 def dit_stream_pattern(kind: int, rows: int, row_bytes: int, in0=None, in1=None, out0=None, out1=None, heads: int = 0,
@@ -485,11 +485,14 @@ def dit_stream_pattern(kind: int, rows: int, row_bytes: int, in0=None, in1=None,
     """Access-pattern stream (measurement only): the traffic of one of the chain's kernels with no arithmetic.
 
     Tensors are contiguous device tensors of any dtype holding at least the bytes the pattern touches
-    (see dit_ops.h); unused ones may be None.
+    (see dit_ops.h); unused ones may be None.  For DIT_STREAM_SCORE_TILES and DIT_STREAM_TOPK_ROWS `heads` is the block count n.
     """
     split = kind == DIT_STREAM_SPLIT_ROWS
-    need = {"in0": rows * row_bytes * (2 if split else 1), "in1": rows * row_bytes,
+    means = rows * 512 if kind == DIT_STREAM_SCORE_TILES else None  # [rows][128] fp32 query / key means
+    need = {"in0": means or rows * row_bytes * (2 if split else 1), "in1": means or rows * row_bytes,
             "out0": 16 if kind == DIT_STREAM_READ else rows * row_bytes, "out1": rows * row_bytes}
+    if kind == DIT_STREAM_TOPK_ROWS and heads > 0:
+        need["out0"] = rows * (-(-heads // 4)) * 4  # [rows][ceil(n / 4)] int32
     ptrs, devs = {}, []
     for name, t in (("in0", in0), ("in1", in1), ("out0", out0), ("out1", out1)):
         if t is None:

@@ -484,13 +484,14 @@ dit_status dit_packed_positions(int32_t *pos, int64_t T, int64_t Hg, int64_t Wg,
 static_assert(DIT_STREAM_READ == dit::kPatternRead && DIT_STREAM_WRITE == dit::kPatternWrite &&
                   DIT_STREAM_SPLIT_ROWS == dit::kPatternSplitRows && DIT_STREAM_TWO_IN == dit::kPatternTwoIn &&
                   DIT_STREAM_ROW_WAVE == dit::kPatternRowWave && DIT_STREAM_ROW_WAVE_2X2 == dit::kPatternRowWave2x2 &&
-                  DIT_STREAM_HEAD_MAJOR == dit::kPatternHeadMajor,
+                  DIT_STREAM_HEAD_MAJOR == dit::kPatternHeadMajor && DIT_STREAM_SCORE_TILES == dit::kPatternScoreTiles &&
+                  DIT_STREAM_TOPK_ROWS == dit::kPatternTopkRows,
               "pattern kinds");
 
 dit_status dit_stream_pattern(int32_t kind, const void *in0, const void *in1, void *out0, void *out1, int64_t rows,
                               int64_t row_bytes, int64_t heads, void *stream)
 {
-    if (kind < DIT_STREAM_READ || kind > DIT_STREAM_HEAD_MAJOR || rows < 0 || rows > kMaxRows || row_bytes < 0 ||
+    if (kind < DIT_STREAM_READ || kind > DIT_STREAM_TOPK_ROWS || rows < 0 || rows > kMaxRows || row_bytes < 0 ||
         heads < 0)
         return DIT_ERR_ARG;
     if (row_bytes < 16 || row_bytes % 16 != 0 || row_bytes > 2 * kMaxWidth)
@@ -505,19 +506,34 @@ dit_status dit_stream_pattern(int32_t kind, const void *in0, const void *in1, vo
         if (rows * ((row_bytes / 16 + 255) / 256) > kMaxRows)
             return DIT_ERR_ARG;
     }
+    const bool score_tiles = kind == DIT_STREAM_SCORE_TILES;
+    if (score_tiles) {
+        if (heads < 1 || rows % heads != 0 || row_bytes < 16 * ((heads + 3) / 4))
+            return DIT_ERR_SHAPE;
+        const int64_t tiles = (heads + 127) / 128;
+        if ((rows / heads) * tiles * tiles >= (int64_t)1 << 31)
+            return DIT_ERR_ARG;
+    }
+    const bool topk_rows = kind == DIT_STREAM_TOPK_ROWS;
+    if (topk_rows) {
+        if (heads < 1 || heads > 4096 || rows % heads != 0 || row_bytes < 4 * heads)
+            return DIT_ERR_SHAPE;
+        if (rows / heads > 65535)
+            return DIT_ERR_ARG;
+    }
     if ((kind == DIT_STREAM_SPLIT_ROWS && !dit::swiglu_fits(rows, row_bytes / 2)) ||
         (kind == DIT_STREAM_TWO_IN && !dit::gated_residual_fits(rows, row_bytes / 2)))
         return DIT_ERR_ARG;
     if (rows == 0)
         return DIT_OK;
-    const bool two_in = kind == DIT_STREAM_TWO_IN || kind == DIT_STREAM_ROW_WAVE_2X2;
+    const bool two_in = kind == DIT_STREAM_TWO_IN || kind == DIT_STREAM_ROW_WAVE_2X2 || score_tiles;
     if ((kind != DIT_STREAM_WRITE && !in0) || (two_in && !in1) || !out0 || (kind == DIT_STREAM_ROW_WAVE_2X2 && !out1))
         return DIT_ERR_NULL;
     if (!aligned(in0, 16) || !aligned(in1, 16) || !aligned(out0, 16) || !aligned(out1, 16))
         return DIT_ERR_ALIGN;
     const int64_t n = rows * row_bytes;
-    const int64_t nin = kind == DIT_STREAM_SPLIT_ROWS ? 2 * n : n;
-    const int64_t nout = kind == DIT_STREAM_READ ? 16 : n;
+    const int64_t nin = kind == DIT_STREAM_SPLIT_ROWS ? 2 * n : score_tiles ? rows * 512 : n;
+    const int64_t nout = kind == DIT_STREAM_READ ? 16 : topk_rows ? rows * ((heads + 3) / 4) * 4 : n;
     const void *ins[2] = {kind == DIT_STREAM_WRITE ? nullptr : in0, two_in ? in1 : nullptr};
     void *outs[2] = {out0, kind == DIT_STREAM_ROW_WAVE_2X2 ? out1 : nullptr};
     for (void *o : outs) {

@@ -92,6 +92,8 @@ enum : int {
     kPatternRowWave = 4,
     kPatternRowWave2x2 = 5,
     kPatternHeadMajor = 6,
+    kPatternScoreTiles = 7,
+    kPatternTopkRows = 8,
 };
 hipError_t launch_stream_pattern(int kind, const void *in0, const void *in1, void *out0, void *out1, int64_t rows,
                                  int64_t row_bytes, int64_t heads, hipStream_t stream);

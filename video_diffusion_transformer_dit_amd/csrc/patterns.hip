@@ -22,6 +22,17 @@
 //   HEAD_MAJOR     [rows][heads][W/heads] -> [heads][rows][W/heads]: a
 //                  token-major to head-major copy, one vector per thread,
 //                  grid (row, 4 KiB part) as the token-major QK kernel
+//   SCORE_TILES    the SubBlock block-score kernel's traffic at head dim 128:
+//                  its persistent 512-thread workgroups (one per CU), its
+//                  order of (plane, query tile, key tile) items, the query
+//                  tile loaded when it changes and the next key tile
+//                  prefetched, and each 128 x 128 tile of fp32 words stored
+//                  as 512-byte row segments; no products, no LDS staging
+//   TOPK_ROWS      the SubBlock top-k kernel's traffic: one wave per row of
+//                  n scores read with its buffer loads (n / 64 rounded up to
+//                  4, 8, 16, 32 or 64 per lane), then ceil(n / 4) words of the
+//                  row's kept list written (the kept count at sparsity 0.75);
+//                  no selection
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -132,6 +143,113 @@ __global__ __launch_bounds__(256) void pattern_head_major_kernel(const u32x4 *__
     }
 }
 
+// SCORE_TILES: P planes of n x n fp32 words (row stride ld4 vectors), the
+// block-score kernel's item order and loads.  A stored word is its tag
+// (plane row * 65536 + column, mod 2^32) XOR the fold of the words this thread
+// loaded for the tile, so all-zero means give the bare tags.  The LDS array
+// is never touched; it holds occupancy at the kernel's one workgroup per CU.
+constexpr int kScoreTile = 128, kScoreDh = 128, kScoreLds = 135168;
+
+__global__ __launch_bounds__(512) void pattern_score_tiles_kernel(const u32x4 *__restrict__ qm,
+                                                                  const u32x4 *__restrict__ km,
+                                                                  u32x4 *__restrict__ out, int n, int ld4, int tiles,
+                                                                  unsigned total)
+{
+    constexpr int kThreads = 512, kF4PerRow = kScoreDh / 4;
+    constexpr int kLoads = kScoreTile * kF4PerRow / kThreads;
+    constexpr int kStores = kScoreTile * kScoreTile / 4 / kThreads;
+    __shared__ uint32_t lds_hold[kScoreLds / 4];
+    asm volatile("" : : "v"(lds_hold) : "memory"); // the array's address escapes: the allocation stays
+
+    const unsigned per = gridDim.x / 8, xcd = blockIdx.x % 8, j = blockIdx.x / 8;
+    const unsigned span = (total + 7) / 8;
+    const unsigned first = xcd * span, last = min(total, first + span);
+    const unsigned run = (span + per - 1) / per;
+    const unsigned begin = min(last, first + j * run), end = min(last, begin + run);
+    const unsigned per_plane = (unsigned)(tiles * tiles);
+
+    u32x4 kr[kLoads];
+    auto load_k = [&](unsigned it) {
+        const size_t p = it / per_plane;
+        const int tj = (int)(it % per_plane) % tiles;
+        const u32x4 *kb = km + (p * n + (size_t)tj * kScoreTile) * kF4PerRow;
+        const int k_rows = min(kScoreTile, n - tj * kScoreTile);
+#pragma unroll
+        for (int m = 0; m < kLoads; ++m) {
+            const int e = threadIdx.x + kThreads * m;
+            kr[m] = e / kF4PerRow < k_rows ? kb[e] : u32x4{0u, 0u, 0u, 0u};
+        }
+    };
+    if (begin < end)
+        load_k(begin);
+    size_t held_p = ~(size_t)0;
+    int held_ti = -1;
+    uint32_t qfold = 0u;
+    for (unsigned item = begin; item < end; ++item) {
+        const size_t p = item / per_plane;
+        const int tile = (int)(item % per_plane), ti = tile / tiles, tj = tile % tiles;
+        const int q_rows = min(kScoreTile, n - ti * kScoreTile), k_rows = min(kScoreTile, n - tj * kScoreTile);
+        if (p != held_p || ti != held_ti) { // workgroup-uniform
+            const u32x4 *qa = qm + (p * n + (size_t)ti * kScoreTile) * kF4PerRow;
+            qfold = 0u;
+#pragma unroll
+            for (int m = 0; m < kLoads; ++m) {
+                const int e = threadIdx.x + kThreads * m;
+                const u32x4 a = e / kF4PerRow < q_rows ? qa[e] : u32x4{0u, 0u, 0u, 0u};
+                qfold ^= a[0] ^ a[1] ^ a[2] ^ a[3];
+            }
+            held_p = p, held_ti = ti;
+        }
+        uint32_t x = qfold;
+#pragma unroll
+        for (int m = 0; m < kLoads; ++m)
+            x ^= kr[m][0] ^ kr[m][1] ^ kr[m][2] ^ kr[m][3];
+        __syncthreads(); // the kernel's barrier before the key tile is replaced
+        if (item + 1 < end)
+            load_k(item + 1);
+        const uint32_t row_tag = (uint32_t)(p * n + (size_t)ti * kScoreTile) * 65536u;
+        u32x4 *o = out + (p * n + (size_t)ti * kScoreTile) * ld4 + (size_t)tj * (kScoreTile / 4);
+#pragma unroll
+        for (int m = 0; m < kStores; ++m) {
+            const int idx = threadIdx.x + kThreads * m;
+            const int row = idx / (kScoreTile / 4), c4 = idx % (kScoreTile / 4);
+            if (row < q_rows && 4 * c4 < k_rows) {
+                const uint32_t t = row_tag + (uint32_t)row * 65536u + (uint32_t)(tj * kScoreTile + 4 * c4);
+                store_stream(o + (size_t)row * ld4 + c4, u32x4{t ^ x, (t + 1u) ^ x, (t + 2u) ^ x, (t + 3u) ^ x});
+            }
+        }
+    }
+}
+
+// TOPK_ROWS: row r of in [rows][ld] (n words read), ceil(n / 4) words written
+// to out [rows][keep]: word j = (r * 65536 + j) XOR the fold of the words the
+// lane loaded, so an all-zero input gives the bare tags.  The loads are the
+// top-k kernel's (out-of-range words read as 0 by the buffer's range check,
+// the same 4 KiB split of the offset); the LDS array holds its occupancy.
+template <int S>
+__global__ __launch_bounds__(kWave) void pattern_topk_rows_kernel(const float *__restrict__ in, uint32_t *__restrict__ out,
+                                                                  int n, int ld, int keep)
+{
+    constexpr int kRawFormat = 0x00020000;
+    constexpr int kSlotsPerOffset = 4096 / (4 * kWave);
+    __shared__ uint32_t lds_hold[1024];
+    asm volatile("" : : "v"(lds_hold) : "memory"); // the array's address escapes: the allocation stays
+    const int lane = threadIdx.x;
+    const size_t row = (size_t)blockIdx.y * n + blockIdx.x;
+    const __amdgpu_buffer_rsrc_t rd = __builtin_amdgcn_make_buffer_rsrc((void *)(in + row * ld), 0, n * 4, kRawFormat);
+    uint32_t fold = 0u;
+#pragma unroll
+    for (int q = 0; q < S; ++q) {
+        const int base = 4 * lane + 4096 * (q / kSlotsPerOffset);
+        fold ^= __builtin_bit_cast(uint32_t, __builtin_amdgcn_raw_buffer_load_b32(
+                                                 rd, base + 4 * kWave * (q % kSlotsPerOffset), 0, 2 /* nt */));
+    }
+    uint32_t *o = out + row * keep;
+    const uint32_t tag = (uint32_t)row * 65536u;
+    for (int j = lane; j < keep; j += kWave)
+        o[j] = (tag + (uint32_t)j) ^ fold;
+}
+
 unsigned capped(uint64_t tiles) { return tiles < kGridCap ? (unsigned)tiles : kGridCap; }
 
 template <bool TWO>
@@ -200,6 +318,36 @@ hipError_t launch_stream_pattern(int kind, const void *in0, const void *in1, voi
         const int H = (int)heads, VPH = (int)(C / heads);
         hipLaunchKernelGGL(pattern_head_major_kernel, dim3((unsigned)rows, (unsigned)((C + 255) / 256)), dim3(256), 0,
                            stream, a, o, (int)rows, H, VPH);
+        break;
+    }
+    case kPatternScoreTiles: {
+        // rows = P * n, heads = n: the grid the block-score kernel takes at
+        // head dim 128, one workgroup per CU (a multiple of 8), no more than
+        // there are tiles
+        const int n = (int)heads, tiles = (n + kScoreTile - 1) / kScoreTile;
+        const unsigned total = (unsigned)((uint64_t)(rows / heads) * (uint64_t)tiles * (uint64_t)tiles);
+        int dev = 0, cus = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 8) {
+            (void)hipGetLastError();
+            cus = 256;
+        }
+        const unsigned resident = (unsigned)cus / 8 * 8, need = (total + 7) / 8 * 8;
+        hipLaunchKernelGGL(pattern_score_tiles_kernel, dim3(resident < need ? resident : need), dim3(512), 0, stream,
+                           a, b, o, n, (int)C, tiles, total);
+        break;
+    }
+    case kPatternTopkRows: {
+        // rows = P * n, heads = n; the top-k kernel's grid (n, P) of single waves
+        const int n = (int)heads, ld = (int)(row_bytes / 4), keep = (n + 3) / 4;
+        const dim3 grid((unsigned)n, (unsigned)(rows / heads));
+        const float *in = static_cast<const float *>(in0);
+        auto *out = static_cast<uint32_t *>(out0);
+        if (n <= 256) hipLaunchKernelGGL(pattern_topk_rows_kernel<4>, grid, dim3(kWave), 0, stream, in, out, n, ld, keep);
+        else if (n <= 512) hipLaunchKernelGGL(pattern_topk_rows_kernel<8>, grid, dim3(kWave), 0, stream, in, out, n, ld, keep);
+        else if (n <= 1024) hipLaunchKernelGGL(pattern_topk_rows_kernel<16>, grid, dim3(kWave), 0, stream, in, out, n, ld, keep);
+        else if (n <= 2048) hipLaunchKernelGGL(pattern_topk_rows_kernel<32>, grid, dim3(kWave), 0, stream, in, out, n, ld, keep);
+        else hipLaunchKernelGGL(pattern_topk_rows_kernel<64>, grid, dim3(kWave), 0, stream, in, out, n, ld, keep);
         break;
     }
     default: return hipErrorInvalidValue;
