@@ -791,10 +791,10 @@ def pattern_ceilings(dit, wl, ins, ops, fused_ms: float, layout_ms: float, timed
                          R * 6 * F, ops["swiglu"]["avg_ms"]),
         "residual_shape": (lambda: sp(dit.DIT_STREAM_TWO_IN, R, 2 * D, in0=a, in1=b, out0=o1), R * 6 * D,
                            ops["residual"]["avg_ms"]),
-        "adaln_shape": (lambda: sp(dit.DIT_STREAM_ROW_WAVE, R, 2 * D, in0=ins["x_mod"], out0=o1), R * 4 * D,
+        "adaln_shape": (lambda: sp(dit.DIT_STREAM_ROW_GROUP, R, 2 * D, in0=ins["x_mod"], out0=o1), R * 4 * D,
                         ops["adaln"]["avg_ms"]),
         "fused_residual_adaln_shape": (
-            lambda: sp(dit.DIT_STREAM_ROW_WAVE_2X2, R, 2 * D, in0=a, in1=b, out0=o1, out1=o2), R * 8 * D, fused_ms),
+            lambda: sp(dit.DIT_STREAM_ROW_GROUP_2X2, R, 2 * D, in0=a, in1=b, out0=o1, out1=o2), R * 8 * D, fused_ms),
         "qk_token_major_copy": (lambda: (dit.dit_copy16(q, qo), dit.dit_copy16(k, ko)), R * 8 * HD,
                                 ops["qk"]["avg_ms"]),
         "qk_head_major_copy": (lambda: (sp(dit.DIT_STREAM_HEAD_MAJOR, R, 2 * HD, in0=q, out0=qo, heads=H),
@@ -1031,8 +1031,8 @@ KERNEL_OPS = (
     (r"pattern_write_kernel", "p_write"),
     (r"pattern_split_rows_kernel", "p_swiglu"),
     (r"pattern_two_in_kernel", "p_residual"),
-    (r"pattern_row_wave_kernel<\d+, false,", "p_adaln"),
-    (r"pattern_row_wave_kernel<\d+, true,", "p_residual_adaln"),
+    (r"pattern_row_group_kernel<false,", "p_adaln"),
+    (r"pattern_row_group_kernel<true,", "p_residual_adaln"),
     (r"pattern_head_major_kernel", "p_head_major"),
     (r"pattern_score_tiles_kernel", "p_score_tiles"),
     (r"pattern_topk_rows_kernel", "p_topk_rows"),

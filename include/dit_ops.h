@@ -70,7 +70,7 @@ typedef enum {
     DIT_ERR_SCRATCH = 6 /* sizes beyond a static scratch buffer's capacity */
 } dit_status;
 
-#define DIT_ABI_VERSION 3
+#define DIT_ABI_VERSION 4
 
 /* Human-readable name of a status code; never NULL. */
 const char *dit_status_str(int status);
@@ -451,11 +451,13 @@ dit_status dit_copy16(const void *src, void *dst, int64_t bytes, void *stream);
  *   DIT_STREAM_SPLIT_ROWS    in0 [rows][2*row_bytes] -> out0 [rows][row_bytes],
  *                            out = first half XOR second half (SwiGLU's shape)
  *   DIT_STREAM_TWO_IN        out0 = in0 XOR in1 (the gated residual's shape)
- *   DIT_STREAM_ROW_WAVE      out0 = in0, one wave per row with every load
- *                            before any store (AdaLN's shape); row_bytes <=
- *                            16384
- *   DIT_STREAM_ROW_WAVE_2X2  out0 = in0 and out1 = in1 with ROW_WAVE's mapping
- *                            (the fused residual -> AdaLN's shape)
+ *   DIT_STREAM_ROW_GROUP     out0 = in0 with AdaLN's mapping: two rows per
+ *                            workgroup, each thread two 16-byte vectors of
+ *                            each row, every load before any store;
+ *                            row_bytes <= 16384
+ *   DIT_STREAM_ROW_GROUP_2X2 out0 = in0 and out1 = in1 with ROW_GROUP's
+ *                            mapping, out0 stored before out1 (the fused
+ *                            residual -> AdaLN's shape)
  *   DIT_STREAM_HEAD_MAJOR    in0 [rows][heads][row_bytes/heads] ->
  *                            out0 [heads][rows][row_bytes/heads] (token-major
  *                            to head-major copy); row_bytes/16 a multiple of
@@ -491,8 +493,8 @@ dit_status dit_copy16(const void *src, void *dst, int64_t bytes, void *stream);
 #define DIT_STREAM_WRITE 1
 #define DIT_STREAM_SPLIT_ROWS 2
 #define DIT_STREAM_TWO_IN 3
-#define DIT_STREAM_ROW_WAVE 4
-#define DIT_STREAM_ROW_WAVE_2X2 5
+#define DIT_STREAM_ROW_GROUP 4 /* stream kinds 4 and 5 take this mapping from ABI version 4 */
+#define DIT_STREAM_ROW_GROUP_2X2 5
 #define DIT_STREAM_HEAD_MAJOR 6
 #define DIT_STREAM_SCORE_TILES 7
 #define DIT_STREAM_TOPK_ROWS 8

@@ -375,8 +375,8 @@ def test_copy_validation(lib):
 
 
 def test_stream_pattern_validation(lib):
-    from video_diffusion_transformer_dit_amd import (DIT_STREAM_HEAD_MAJOR, DIT_STREAM_READ, DIT_STREAM_ROW_WAVE,
-                                                     DIT_STREAM_ROW_WAVE_2X2, DIT_STREAM_SCORE_TILES,
+    from video_diffusion_transformer_dit_amd import (DIT_STREAM_HEAD_MAJOR, DIT_STREAM_READ, DIT_STREAM_ROW_GROUP,
+                                                     DIT_STREAM_ROW_GROUP_2X2, DIT_STREAM_SCORE_TILES,
                                                      DIT_STREAM_SPLIT_ROWS, DIT_STREAM_TOPK_ROWS, DIT_STREAM_TWO_IN,
                                                      DIT_STREAM_WRITE)
 
@@ -386,18 +386,18 @@ def test_stream_pattern_validation(lib):
     assert f(kind=9) == DIT_ERR_ARG and f(kind=-1) == DIT_ERR_ARG
     assert f(rows=-1) == DIT_ERR_ARG and f(rows=1 << 24) == DIT_ERR_ARG
     assert f(width=8) == DIT_ERR_SHAPE and f(width=8200) == DIT_ERR_SHAPE and f(width=0) == DIT_ERR_SHAPE
-    assert f(kind=DIT_STREAM_ROW_WAVE, width=16400) == DIT_ERR_SHAPE  # wave-per-row rows up to 16 KiB
+    assert f(kind=DIT_STREAM_ROW_GROUP, width=16400) == DIT_ERR_SHAPE  # row-group rows up to 16 KiB
     assert f(kind=DIT_STREAM_HEAD_MAJOR, heads=0) == DIT_ERR_SHAPE
     assert f(kind=DIT_STREAM_HEAD_MAJOR, width=8192, heads=3) == DIT_ERR_SHAPE  # 512 vectors over 3 heads
     assert f(kind=DIT_STREAM_HEAD_MAJOR, rows=(1 << 23), width=8192, heads=32) == DIT_ERR_ARG  # 2^24 workgroups
     assert f(kind=DIT_STREAM_SPLIT_ROWS, rows=(1 << 24) - 1, width=1 << 25) == DIT_ERR_ARG  # tile counter
     assert f(kind=DIT_STREAM_TWO_IN, rows=(1 << 24) - 1, width=1 << 25) == DIT_ERR_ARG
     assert f(b=0) == DIT_ERR_NULL and f(o=0) == DIT_ERR_NULL
-    assert f(kind=DIT_STREAM_ROW_WAVE_2X2, o2=0) == DIT_ERR_NULL
+    assert f(kind=DIT_STREAM_ROW_GROUP_2X2, o2=0) == DIT_ERR_NULL
     assert f(kind=DIT_STREAM_WRITE, a=0, b=0, o2=0, o=P + 8) == DIT_ERR_ALIGN
     assert f(o=Q + 16) == DIT_ERR_ARG  # output inside in1
     assert f(kind=DIT_STREAM_SPLIT_ROWS, o=P + 4 * 8192 + 16) == DIT_ERR_ARG  # inside the doubled input rows
-    assert f(kind=DIT_STREAM_ROW_WAVE_2X2, o2=R + 64) == DIT_ERR_ARG  # the two outputs overlap
+    assert f(kind=DIT_STREAM_ROW_GROUP_2X2, o2=R + 64) == DIT_ERR_ARG  # the two outputs overlap
     assert f(kind=DIT_STREAM_READ, o=P + 4 * 8192 - 16) == DIT_ERR_ARG  # sink inside the input
     assert f(rows=0, a=0, b=0, o=0, o2=0) == DIT_OK
 

@@ -48,14 +48,14 @@ def test_split_rows_and_two_in(rows, row_bytes):
 
 
 @pytest.mark.parametrize("rows,row_bytes", SHAPES)
-def test_row_wave_copies(rows, row_bytes):
+def test_row_group_copies(rows, row_bytes):
     x, y = words(rows, row_bytes, 4), words(rows, row_bytes, 5)
     ox, oy = torch.zeros_like(x), torch.zeros_like(y)
-    dit.dit_stream_pattern(dit.DIT_STREAM_ROW_WAVE, rows, row_bytes, in0=x, out0=ox)
+    dit.dit_stream_pattern(dit.DIT_STREAM_ROW_GROUP, rows, row_bytes, in0=x, out0=ox)
     torch.cuda.synchronize()
     assert torch.equal(ox, x)
     ox.zero_()
-    dit.dit_stream_pattern(dit.DIT_STREAM_ROW_WAVE_2X2, rows, row_bytes, in0=x, in1=y, out0=ox, out1=oy)
+    dit.dit_stream_pattern(dit.DIT_STREAM_ROW_GROUP_2X2, rows, row_bytes, in0=x, in1=y, out0=ox, out1=oy)
     torch.cuda.synchronize()
     assert torch.equal(ox, x) and torch.equal(oy, y)
 

@@ -35,8 +35,8 @@ from ._binding import (  # noqa: F401
     DIT_QK_TOKEN_MAJOR,
     DIT_STREAM_HEAD_MAJOR,
     DIT_STREAM_READ,
-    DIT_STREAM_ROW_WAVE,
-    DIT_STREAM_ROW_WAVE_2X2,
+    DIT_STREAM_ROW_GROUP,
+    DIT_STREAM_ROW_GROUP_2X2,
     DIT_STREAM_SCORE_TILES,
     DIT_STREAM_TOPK_ROWS,
     DIT_STREAM_SPLIT_ROWS,

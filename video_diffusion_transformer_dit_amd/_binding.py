@@ -476,8 +476,8 @@ def dit_copy16(src, dst, stream=None):
     return dst
 
 
-DIT_STREAM_READ, DIT_STREAM_WRITE, DIT_STREAM_SPLIT_ROWS, DIT_STREAM_TWO_IN, DIT_STREAM_ROW_WAVE, \
-    DIT_STREAM_ROW_WAVE_2X2, DIT_STREAM_HEAD_MAJOR, DIT_STREAM_SCORE_TILES, DIT_STREAM_TOPK_ROWS = range(9)
+DIT_STREAM_READ, DIT_STREAM_WRITE, DIT_STREAM_SPLIT_ROWS, DIT_STREAM_TWO_IN, DIT_STREAM_ROW_GROUP, \
+    DIT_STREAM_ROW_GROUP_2X2, DIT_STREAM_HEAD_MAJOR, DIT_STREAM_SCORE_TILES, DIT_STREAM_TOPK_ROWS = range(9)
 
 
 def dit_stream_pattern(kind: int, rows: int, row_bytes: int, in0=None, in1=None, out0=None, out1=None, heads: int = 0,

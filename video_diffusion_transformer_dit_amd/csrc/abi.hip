@@ -28,7 +28,7 @@ namespace {
 // workgroup per row spans up to 256 work-items) and every row index fits in
 // 32 bits.
 constexpr int64_t kMaxRows = (int64_t(1) << 24) - 1;
-constexpr int64_t kMaxAdaLNWidth = 8192; // row held in registers: 128 fp32 per lane
+constexpr int64_t kMaxAdaLNWidth = 8192; // rows of up to 1024 vectors: 512 threads per workgroup
 constexpr int64_t kMaxWidth = int64_t(1) << 24;
 constexpr int64_t kMaxHeadRow = 65536; // H * Dh
 
@@ -483,7 +483,7 @@ dit_status dit_packed_positions(int32_t *pos, int64_t T, int64_t Hg, int64_t Wg,
 
 static_assert(DIT_STREAM_READ == dit::kPatternRead && DIT_STREAM_WRITE == dit::kPatternWrite &&
                   DIT_STREAM_SPLIT_ROWS == dit::kPatternSplitRows && DIT_STREAM_TWO_IN == dit::kPatternTwoIn &&
-                  DIT_STREAM_ROW_WAVE == dit::kPatternRowWave && DIT_STREAM_ROW_WAVE_2X2 == dit::kPatternRowWave2x2 &&
+                  DIT_STREAM_ROW_GROUP == dit::kPatternRowGroup && DIT_STREAM_ROW_GROUP_2X2 == dit::kPatternRowGroup2x2 &&
                   DIT_STREAM_HEAD_MAJOR == dit::kPatternHeadMajor && DIT_STREAM_SCORE_TILES == dit::kPatternScoreTiles &&
                   DIT_STREAM_TOPK_ROWS == dit::kPatternTopkRows,
               "pattern kinds");
@@ -496,7 +496,7 @@ dit_status dit_stream_pattern(int32_t kind, const void *in0, const void *in1, vo
         return DIT_ERR_ARG;
     if (row_bytes < 16 || row_bytes % 16 != 0 || row_bytes > 2 * kMaxWidth)
         return DIT_ERR_SHAPE;
-    if (kind == DIT_STREAM_ROW_WAVE || kind == DIT_STREAM_ROW_WAVE_2X2) {
+    if (kind == DIT_STREAM_ROW_GROUP || kind == DIT_STREAM_ROW_GROUP_2X2) {
         if (row_bytes > 2 * kMaxAdaLNWidth)
             return DIT_ERR_SHAPE;
     }
@@ -526,8 +526,8 @@ dit_status dit_stream_pattern(int32_t kind, const void *in0, const void *in1, vo
         return DIT_ERR_ARG;
     if (rows == 0)
         return DIT_OK;
-    const bool two_in = kind == DIT_STREAM_TWO_IN || kind == DIT_STREAM_ROW_WAVE_2X2 || score_tiles;
-    if ((kind != DIT_STREAM_WRITE && !in0) || (two_in && !in1) || !out0 || (kind == DIT_STREAM_ROW_WAVE_2X2 && !out1))
+    const bool two_in = kind == DIT_STREAM_TWO_IN || kind == DIT_STREAM_ROW_GROUP_2X2 || score_tiles;
+    if ((kind != DIT_STREAM_WRITE && !in0) || (two_in && !in1) || !out0 || (kind == DIT_STREAM_ROW_GROUP_2X2 && !out1))
         return DIT_ERR_NULL;
     if (!aligned(in0, 16) || !aligned(in1, 16) || !aligned(out0, 16) || !aligned(out1, 16))
         return DIT_ERR_ALIGN;
@@ -535,7 +535,7 @@ dit_status dit_stream_pattern(int32_t kind, const void *in0, const void *in1, vo
     const int64_t nin = kind == DIT_STREAM_SPLIT_ROWS ? 2 * n : score_tiles ? rows * 512 : n;
     const int64_t nout = kind == DIT_STREAM_READ ? 16 : topk_rows ? rows * ((heads + 3) / 4) * 4 : n;
     const void *ins[2] = {kind == DIT_STREAM_WRITE ? nullptr : in0, two_in ? in1 : nullptr};
-    void *outs[2] = {out0, kind == DIT_STREAM_ROW_WAVE_2X2 ? out1 : nullptr};
+    void *outs[2] = {out0, kind == DIT_STREAM_ROW_GROUP_2X2 ? out1 : nullptr};
     for (void *o : outs) {
         if (!o)
             continue;

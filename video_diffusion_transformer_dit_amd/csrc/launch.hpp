@@ -89,8 +89,8 @@ enum : int {
     kPatternWrite = 1,
     kPatternSplitRows = 2,
     kPatternTwoIn = 3,
-    kPatternRowWave = 4,
-    kPatternRowWave2x2 = 5,
+    kPatternRowGroup = 4,
+    kPatternRowGroup2x2 = 5,
     kPatternHeadMajor = 6,
     kPatternScoreTiles = 7,
     kPatternTopkRows = 8,

@@ -35,6 +35,7 @@
 //                  no selection
 #include "device_common.hpp"
 #include "launch.hpp"
+#include "row_group.hpp"
 
 namespace dit {
 namespace {
@@ -92,41 +93,52 @@ __global__ __launch_bounds__(512) void pattern_two_in_kernel(const u32x4 *__rest
     }
 }
 
-// FULL: the row is exactly 64 * VPL vectors, so no load is conditional (as in
-// AdaLN's kernels: conditional loads into an array make the compiler wait for
-// each load before the next).
-template <int VPL, bool TWO, bool FULL>
-__global__ __launch_bounds__(256) void pattern_row_wave_kernel(const u32x4 *__restrict__ x,
-                                                               const u32x4 *__restrict__ y, u32x4 *__restrict__ ox,
-                                                               u32x4 *__restrict__ oy, int rows, int C)
+// The loads and stores of adaln.hip (TWO = false) and residual_adaln.hip
+// (TWO = true) with nothing computed in between.
+template <bool TWO, bool FULL>
+__global__ __launch_bounds__(kGroupMaxThreads) void pattern_row_group_kernel(const u32x4 *__restrict__ x,
+                                                                             const u32x4 *__restrict__ y,
+                                                                             u32x4 *__restrict__ ox,
+                                                                             u32x4 *__restrict__ oy, int rows, int C)
 {
-    const int lane = threadIdx.x & (kWave - 1);
-    const int row = blockIdx.x * 4 + threadIdx.x / kWave;
-    if (row >= rows) // wave-uniform
-        return;
-    const size_t base = (size_t)row * C;
-    u32x4 a[VPL], b[VPL];
+    const int T = blockDim.x, tid = threadIdx.x;
+    const int r0 = blockIdx.x * kGroupRows;
+    const int nr = min(rows - r0, kGroupRows);
+    int c[kGroupVecs];
+    bool ok[kGroupVecs];
 #pragma unroll
-    for (int k = 0; k < VPL; ++k) {
-        const int c = lane + kWave * k;
-        a[k] = b[k] = u32x4{0u, 0u, 0u, 0u};
-        if (FULL || c < C) {
-            a[k] = load_stream(x + base + c);
-            if (TWO)
-                b[k] = load_stream(y + base + c);
-        }
+    for (int k = 0; k < kGroupVecs; ++k) {
+        c[k] = tid + T * k;
+        ok[k] = FULL || c[k] < C;
     }
-    // the kernels this stands for store only after the whole row is in (their
-    // row statistics need it): keep the scheduler from moving stores earlier
+    const __amdgpu_buffer_rsrc_t rx = group_rows_rsrc(x + (size_t)r0 * C, nr, C);
+    const __amdgpu_buffer_rsrc_t ry = group_rows_rsrc((TWO ? y : x) + (size_t)r0 * C, nr, C);
+    u32x4 a[kGroupRows][kGroupVecs], b[kGroupRows][kGroupVecs];
+#pragma unroll
+    for (int j = 0; j < kGroupRows; ++j)
+#pragma unroll
+        for (int k = 0; k < kGroupVecs; ++k) {
+            const int off = ok[k] ? (j * C + c[k]) * 16 : kOutOfRange;
+            a[j][k] = group_load(rx, off);
+            if (TWO)
+                b[j][k] = group_load(ry, off);
+        }
+    // the kernels this stands for store only after their rows are in: keep
+    // the scheduler from moving stores earlier
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int k = 0; k < VPL; ++k) {
-        const int c = lane + kWave * k;
-        if (FULL || c < C) {
-            store_stream(ox + base + c, a[k]);
-            if (TWO)
-                store_stream(oy + base + c, b[k]);
-        }
+    for (int j = 0; j < kGroupRows; ++j)
+#pragma unroll
+        for (int k = 0; k < kGroupVecs; ++k)
+            if ((FULL || ok[k]) && j < nr)
+                store_stream(ox + (size_t)(r0 + j) * C + c[k], a[j][k]);
+    if (TWO) {
+#pragma unroll
+        for (int j = 0; j < kGroupRows; ++j)
+#pragma unroll
+            for (int k = 0; k < kGroupVecs; ++k)
+                if ((FULL || ok[k]) && j < nr)
+                    store_stream(oy + (size_t)(r0 + j) * C + c[k], b[j][k]);
     }
 }
 
@@ -253,24 +265,14 @@ __global__ __launch_bounds__(kWave) void pattern_topk_rows_kernel(const float *_
 unsigned capped(uint64_t tiles) { return tiles < kGridCap ? (unsigned)tiles : kGridCap; }
 
 template <bool TWO>
-hipError_t launch_row_wave(const u32x4 *x, const u32x4 *y, u32x4 *ox, u32x4 *oy, int rows, int C, hipStream_t stream)
+hipError_t launch_row_group(const u32x4 *x, const u32x4 *y, u32x4 *ox, u32x4 *oy, int rows, int C, hipStream_t stream)
 {
-    const dim3 grid((unsigned)((rows + 3) / 4)), block(256);
-#define DIT_ROW_WAVE(V)                                                                                              \
-    do {                                                                                                             \
-        if (C == kWave * (V))                                                                                        \
-            hipLaunchKernelGGL((pattern_row_wave_kernel<V, TWO, true>), grid, block, 0, stream, x, y, ox, oy, rows,   \
-                               C);                                                                                   \
-        else                                                                                                         \
-            hipLaunchKernelGGL((pattern_row_wave_kernel<V, TWO, false>), grid, block, 0, stream, x, y, ox, oy, rows,  \
-                               C);                                                                                   \
-    } while (0)
-    if (C <= kWave) DIT_ROW_WAVE(1);
-    else if (C <= 2 * kWave) DIT_ROW_WAVE(2);
-    else if (C <= 4 * kWave) DIT_ROW_WAVE(4);
-    else if (C <= 8 * kWave) DIT_ROW_WAVE(8);
-    else DIT_ROW_WAVE(16);
-#undef DIT_ROW_WAVE
+    const RowGroupShape shape = row_group_shape(C);
+    const dim3 grid((unsigned)((rows + kGroupRows - 1) / kGroupRows)), block((unsigned)shape.threads);
+    if (shape.full)
+        hipLaunchKernelGGL((pattern_row_group_kernel<TWO, true>), grid, block, 0, stream, x, y, ox, oy, rows, C);
+    else
+        hipLaunchKernelGGL((pattern_row_group_kernel<TWO, false>), grid, block, 0, stream, x, y, ox, oy, rows, C);
     return hipGetLastError();
 }
 
@@ -312,8 +314,8 @@ hipError_t launch_stream_pattern(int kind, const void *in0, const void *in1, voi
                            (unsigned)tiles);
         break;
     }
-    case kPatternRowWave: return launch_row_wave<false>(a, a, o, o, (int)rows, (int)C, stream);
-    case kPatternRowWave2x2: return launch_row_wave<true>(a, b, o, o2, (int)rows, (int)C, stream);
+    case kPatternRowGroup: return launch_row_group<false>(a, a, o, o, (int)rows, (int)C, stream);
+    case kPatternRowGroup2x2: return launch_row_group<true>(a, b, o, o2, (int)rows, (int)C, stream);
     case kPatternHeadMajor: {
         const int H = (int)heads, VPH = (int)(C / heads);
         hipLaunchKernelGGL(pattern_head_major_kernel, dim3((unsigned)rows, (unsigned)((C + 255) / 256)), dim3(256), 0,
