@@ -594,6 +594,9 @@ def main(argv=None) -> int:
     score_flops = 2 * score_elems * wl.Dh
     topk_ms = route_ms - scores_ms
     fused_route_bytes = pooled_bytes + wl.B * wl.H * nb * keep * 4
+    # the fused route's strips: 32 query blocks (16 past 2048 blocks), each reading its head's key means
+    strip_blocks = 32 if nb <= 2048 else 16
+    l2_key_bytes = wl.B * wl.H * (-(-nb // strip_blocks)) * nb * wl.Dh * 4
     subblock = {
         "sparsity": sparsity, "blocks": nb, "keep": keep,
         "pool": rate(pool_bytes, pool_ms, "pool"),
@@ -608,6 +611,11 @@ def main(argv=None) -> int:
         "route_fused": {**rate(fused_route_bytes, fused_route_ms, "route_fused"),
                         "op": "dit_subblock_route with scores = NULL (scores and selection in one kernel)",
                         "TFLOP_s": round(score_flops / (fused_route_ms * 1e-3) / 1e12, 1),
+                        "bound": "L2 reads of the key means: each strip of query blocks reads its head's fp32 key "
+                                 "means again (strip_blocks per strip), then selects from registers",
+                        "strip_blocks": strip_blocks,
+                        "l2_key_read_bytes": l2_key_bytes,
+                        "l2_key_read_GB_s": round(l2_key_bytes / (fused_route_ms * 1e-3) / 1e9, 1),
                         "two_kernel_ms": round(route_ms, 5)},
         "total_ms": round(pool_ms + route_ms, 5),
         "total_after_fused_qk_ms": round(qk_pool_ms - ops["qk"]["avg_ms"] + route_ms, 5),
