@@ -105,10 +105,11 @@ def test_gated_residual_validation(lib):
     assert f(P, Q, R, Q + 32, 1, 3, 4096, None) == DIT_ERR_ARG  # partial overlap with y
     assert f(P, Q, R, R, 1, 3, 4096, None) == DIT_ERR_ARG  # output over the gate
     assert f(0, 0, 0, 0, 0, 3, 4096, None) == DIT_OK
-    # rows x ceil(D / 4096) tiles must fit the 32-bit tile counter: refused as an argument, before any launch
-    wide = 1 << 24  # 4096 segments per row
-    assert f(P, 0, R, S, 1, (2 ** 32 - 2 ** 23) // 4096, wide, None) == DIT_ERR_NULL  # exactly at the limit
-    assert f(P, Q, R, S, 1, (2 ** 32 - 2 ** 23) // 4096 + 1, wide, None) == DIT_ERR_ARG
+    # rows x ceil(D / 512) tiles (64 vectors each) must fit the 32-bit tile counter with the 2^23 - 1
+    # workgroup grid: refused as an argument, before any launch
+    wide = 1 << 24  # 32768 segments per row
+    assert f(P, 0, R, S, 1, (2 ** 32 - 2 ** 23) // 32768, wide, None) == DIT_ERR_NULL  # exactly at the limit
+    assert f(P, Q, R, S, 1, (2 ** 32 - 2 ** 23) // 32768 + 1, wide, None) == DIT_ERR_ARG
     assert f(P, Q, R, S, 1, (1 << 24) - 1, wide, None) == DIT_ERR_ARG
 
 
@@ -145,10 +146,11 @@ def test_swiglu_validation(lib):
     assert f(P, Q + 2, 4, 16384, None) == DIT_ERR_ALIGN
     assert f(P, P + 4 * 16384, 4, 16384, None) == DIT_ERR_ARG  # output inside the input
     assert f(0, 0, 0, 16384, None) == DIT_OK
-    # M x ceil(F / 2048) tiles must fit the 32-bit tile counter: refused as an argument, before any launch
-    wide = 1 << 24  # 8192 segments per row
-    assert f(0, Q, (2 ** 32 - 2 ** 24) // 8192, wide, None) == DIT_ERR_NULL  # exactly at the limit
-    assert f(P, Q, (2 ** 32 - 2 ** 24) // 8192 + 1, wide, None) == DIT_ERR_ARG
+    # M x ceil(F / 512) tiles (64 vectors each) must fit the 32-bit tile counter with the 2^24 - 1
+    # workgroup grid: refused as an argument, before any launch
+    wide = 1 << 24  # 32768 segments per row
+    assert f(0, Q, (2 ** 32 - 2 ** 24) // 32768, wide, None) == DIT_ERR_NULL  # exactly at the limit
+    assert f(P, Q, (2 ** 32 - 2 ** 24) // 32768 + 1, wide, None) == DIT_ERR_ARG
     assert f(P, Q, (1 << 24) - 1, wide, None) == DIT_ERR_ARG
 
 

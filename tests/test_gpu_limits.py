@@ -111,7 +111,7 @@ def test_row_limit_positions_and_qk():
 
 
 def test_swiglu_past_the_grid_cap():
-    M, F = (1 << 23) + 8, 2056  # 257 vectors per output row: 2 segments, 2^24 + 16 tiles
+    M, F = (1 << 23) + 8, 2056  # 257 vectors per output row: 5 segments of 64, 5 * (2^23 + 8) tiles
     need = M * 3 * F * 2
     free, _ = torch.cuda.mem_get_info()
     if free < need + (16 << 30):
@@ -125,8 +125,9 @@ def test_swiglu_past_the_grid_cap():
         inp[r0:r1].copy_((torch.randn((r1 - r0, 2 * F), generator=g, device=DEV) * 2.0).to(torch.bfloat16))
     out = dit.dit_swiglu(inp)
     torch.cuda.synchronize()
-    # tiles from 2^24 - 1 on are each a second tile of a workgroup: rows from (2^24 - 1) // 2 on
-    idx = sampled(M, around=(((1 << 24) - 1) // 2,))
+    # tiles from 2^24 - 1 on are a second tile of a workgroup (rows from (2^24 - 1) // 5 on), from
+    # 2 * (2^24 - 1) on a third
+    idx = sampled(M, around=(((1 << 24) - 1) // 5, 2 * ((1 << 24) - 1) // 5))
     assert_close(rows_of(out, idx, F), oracle.swiglu(bits(rows_of(inp, idx, 2 * F))), "swiglu past the cap")
     del inp, out
 

@@ -4,21 +4,24 @@
 // keeps the launch shape of the kernel it stands for, so "X% of its pattern"
 // compares a kernel with the same loads and stores minus its arithmetic.
 //   READ           one 16-byte non-temporal load per thread, 256-thread
-//                  workgroups over consecutive 4 KiB tiles (copy16's shape
-//                  without the stores); the loaded words are folded into one
-//                  value that is stored only if it equals `sink_key`, so the
-//                  loads cannot be dropped and nearly nothing is written
+//                  workgroups over consecutive 4 KiB tiles (a one-way
+//                  stream: the fastest workgroup size for it, see below); the
+//                  loaded words are folded into one value that is stored
+//                  only if it equals `sink_key`, so the loads cannot be
+//                  dropped and nearly nothing is written
 //   WRITE          one 16-byte non-temporal store per thread, same tiling
 //   SPLIT_ROWS     [rows][2W] -> [rows][W] bytes, out = a ^ b of the two
-//                  halves: SwiGLU's tiling (256 threads per 4 KiB output
+//                  halves: SwiGLU's tiling (64 threads per 1 KiB output
 //                  segment, 1-D grid over (row, segment))
 //   TWO_IN         two [rows][W] inputs -> one output (a ^ b): the gated
-//                  residual's tiling (512 threads per 8 KiB segment)
-//   ROW_WAVE       [rows][W] -> [rows][W]: AdaLN's mapping (one wave per row,
-//                  four rows per 256-thread workgroup, each lane's vectors
-//                  lane, lane + 64, ..., every load issued before any store)
-//   ROW_WAVE_2X2   two [rows][W] inputs -> two outputs with ROW_WAVE's
-//                  mapping: the fused residual -> AdaLN's traffic
+//                  residual's tiling (64 threads per 1 KiB segment)
+//   ROW_GROUP      [rows][W] -> [rows][W]: AdaLN's mapping (row_group.hpp:
+//                  two rows per workgroup, thread t holding vectors t and
+//                  t + T of each, loaded through the workgroup's buffer
+//                  descriptor, every load issued before any store)
+//   ROW_GROUP_2X2  two [rows][W] inputs -> two outputs with ROW_GROUP's
+//                  mapping, the first output stored before the second: the
+//                  fused residual -> AdaLN's traffic
 //   HEAD_MAJOR     [rows][heads][W/heads] -> [heads][rows][W/heads]: a
 //                  token-major to head-major copy, one vector per thread,
 //                  grid (row, 4 KiB part) as the token-major QK kernel
@@ -40,15 +43,23 @@
 namespace dit {
 namespace {
 
-constexpr unsigned kGridCap = (1u << 24) - 1; // < 2^32 work-items per dispatch at 256 threads
+constexpr unsigned kGridCap = (1u << 24) - 1; // < 2^32 work-items per dispatch
+// Workgroup size of the streaming kernels these shapes stand for (dit_copy16,
+// SwiGLU, the gated residual): one wave per workgroup.
+constexpr int kStreamThreads = 64;
+// The one-way streams keep 256-thread workgroups: with one wave a workgroup
+// moves only 1 KiB, and an 8 GB read then ran at the rate workgroups are
+// dispatched (1.69 ms against 1.16 ms with 256 threads at 1344x768 5 s).
+constexpr int kOneWayThreads = 256;
 
 __device__ __forceinline__ u32x4 xor4(u32x4 a, u32x4 b) { return a ^ b; }
 
-__global__ __launch_bounds__(256) void pattern_read_kernel(const u32x4 *__restrict__ src, int64_t nvec,
+__global__ __launch_bounds__(kOneWayThreads) void pattern_read_kernel(const u32x4 *__restrict__ src, int64_t nvec,
                                                            u32x4 *__restrict__ sink, uint32_t sink_key)
 {
     uint32_t acc = 0u;
-    for (int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x; c < nvec; c += (int64_t)gridDim.x * 256) {
+    for (int64_t c = (int64_t)blockIdx.x * kOneWayThreads + threadIdx.x; c < nvec;
+         c += (int64_t)gridDim.x * kOneWayThreads) {
         const u32x4 v = load_stream(src + c);
         acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
     }
@@ -56,22 +67,23 @@ __global__ __launch_bounds__(256) void pattern_read_kernel(const u32x4 *__restri
         sink[0] = u32x4{acc, acc, acc, acc};
 }
 
-__global__ __launch_bounds__(256) void pattern_write_kernel(u32x4 *__restrict__ dst, int64_t nvec)
+__global__ __launch_bounds__(kOneWayThreads) void pattern_write_kernel(u32x4 *__restrict__ dst, int64_t nvec)
 {
-    for (int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x; c < nvec; c += (int64_t)gridDim.x * 256) {
+    for (int64_t c = (int64_t)blockIdx.x * kOneWayThreads + threadIdx.x; c < nvec;
+         c += (int64_t)gridDim.x * kOneWayThreads) {
         const uint32_t w = (uint32_t)c;
         store_stream(dst + c, u32x4{w, w, w, w});
     }
 }
 
 // C = 16-byte vectors per output row.
-__global__ __launch_bounds__(256) void pattern_split_rows_kernel(const u32x4 *__restrict__ in,
+__global__ __launch_bounds__(kStreamThreads) void pattern_split_rows_kernel(const u32x4 *__restrict__ in,
                                                                  u32x4 *__restrict__ out, int C, unsigned segs,
                                                                  unsigned tiles)
 {
     for (unsigned tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
         const unsigned row = tile / segs;
-        const int c = (int)(tile - row * segs) * 256 + threadIdx.x;
+        const int c = (int)(tile - row * segs) * kStreamThreads + threadIdx.x;
         if (c < C) {
             const u32x4 *a = in + (size_t)row * 2 * C;
             store_stream(out + (size_t)row * C + c, xor4(load_stream(a + c), load_stream(a + C + c)));
@@ -79,13 +91,13 @@ __global__ __launch_bounds__(256) void pattern_split_rows_kernel(const u32x4 *__
     }
 }
 
-__global__ __launch_bounds__(512) void pattern_two_in_kernel(const u32x4 *__restrict__ x, const u32x4 *__restrict__ y,
+__global__ __launch_bounds__(kStreamThreads) void pattern_two_in_kernel(const u32x4 *__restrict__ x, const u32x4 *__restrict__ y,
                                                              u32x4 *__restrict__ out, int C, unsigned segs,
                                                              unsigned tiles)
 {
     for (unsigned tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
         const unsigned row = tile / segs;
-        const int c = (int)(tile - row * segs) * 512 + threadIdx.x;
+        const int c = (int)(tile - row * segs) * kStreamThreads + threadIdx.x;
         if (c < C) {
             const size_t at = (size_t)row * C + c;
             store_stream(out + at, xor4(load_stream(x + at), load_stream(y + at)));
@@ -289,28 +301,28 @@ hipError_t launch_stream_pattern(int kind, const void *in0, const void *in1, voi
     switch (kind) {
     case kPatternRead: {
         const int64_t nvec = rows * C;
-        hipLaunchKernelGGL(pattern_read_kernel, dim3(capped((uint64_t)(nvec + 255) / 256)), dim3(256), 0, stream, a,
-                           nvec, o, 0x9e3779b9u);
+        hipLaunchKernelGGL(pattern_read_kernel, dim3(capped((uint64_t)(nvec + kOneWayThreads - 1) / kOneWayThreads)),
+                           dim3(kOneWayThreads), 0, stream, a, nvec, o, 0x9e3779b9u);
         break;
     }
     case kPatternWrite: {
         const int64_t nvec = rows * C;
-        hipLaunchKernelGGL(pattern_write_kernel, dim3(capped((uint64_t)(nvec + 255) / 256)), dim3(256), 0, stream, o,
-                           nvec);
+        hipLaunchKernelGGL(pattern_write_kernel, dim3(capped((uint64_t)(nvec + kOneWayThreads - 1) / kOneWayThreads)),
+                           dim3(kOneWayThreads), 0, stream, o, nvec);
         break;
     }
     case kPatternSplitRows: {
-        const unsigned segs = (unsigned)((C + 255) / 256);
+        const unsigned segs = (unsigned)((C + kStreamThreads - 1) / kStreamThreads);
         const uint64_t tiles = (uint64_t)rows * segs;
-        hipLaunchKernelGGL(pattern_split_rows_kernel, dim3(capped(tiles)), dim3(256), 0, stream, a, o, (int)C, segs,
-                           (unsigned)tiles);
+        hipLaunchKernelGGL(pattern_split_rows_kernel, dim3(capped(tiles)), dim3(kStreamThreads), 0, stream, a, o,
+                           (int)C, segs, (unsigned)tiles);
         break;
     }
     case kPatternTwoIn: {
-        const unsigned segs = (unsigned)((C + 511) / 512);
+        const unsigned segs = (unsigned)((C + kStreamThreads - 1) / kStreamThreads);
         const uint64_t tiles = (uint64_t)rows * segs;
-        const unsigned grid = tiles < (1u << 23) - 1 ? (unsigned)tiles : (1u << 23) - 1;
-        hipLaunchKernelGGL(pattern_two_in_kernel, dim3(grid), dim3(512), 0, stream, a, b, o, (int)C, segs,
+        const unsigned grid = tiles < (1u << 23) - 1 ? (unsigned)tiles : (1u << 23) - 1; // the residual's cap
+        hipLaunchKernelGGL(pattern_two_in_kernel, dim3(grid), dim3(kStreamThreads), 0, stream, a, b, o, (int)C, segs,
                            (unsigned)tiles);
         break;
     }
