@@ -70,7 +70,7 @@ typedef enum {
     DIT_ERR_SCRATCH = 6 /* sizes beyond a static scratch buffer's capacity */
 } dit_status;
 
-#define DIT_ABI_VERSION 4
+#define DIT_ABI_VERSION 5
 
 /* Human-readable name of a status code; never NULL. */
 const char *dit_status_str(int status);
@@ -460,8 +460,12 @@ dit_status dit_copy16(const void *src, void *dst, int64_t bytes, void *stream);
  *                            residual -> AdaLN's shape)
  *   DIT_STREAM_HEAD_MAJOR    in0 [rows][heads][row_bytes/heads] ->
  *                            out0 [heads][rows][row_bytes/heads] (token-major
- *                            to head-major copy); row_bytes/16 a multiple of
- *                            heads; rows * ceil(row_bytes / 4096) < 2^24
+ *                            to head-major copy) in the head-major QK
+ *                            kernel's shape: four tokens per workgroup,
+ *                            staged so each store writes one head's four
+ *                            tokens; row_bytes/16 a multiple of heads and
+ *                            row_bytes/heads/16 a divisor of 256;
+ *                            rows * ceil(row_bytes / 4096) < 2^24
  *   DIT_STREAM_SCORE_TILES   the block-score traffic of dit_subblock_route at
  *                            head dim 128, in that kernel's launch shape and
  *                            tile order: here `heads` is the number of blocks

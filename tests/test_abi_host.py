@@ -391,6 +391,7 @@ def test_stream_pattern_validation(lib):
     assert f(kind=DIT_STREAM_ROW_GROUP, width=16400) == DIT_ERR_SHAPE  # row-group rows up to 16 KiB
     assert f(kind=DIT_STREAM_HEAD_MAJOR, heads=0) == DIT_ERR_SHAPE
     assert f(kind=DIT_STREAM_HEAD_MAJOR, width=8192, heads=3) == DIT_ERR_SHAPE  # 512 vectors over 3 heads
+    assert f(kind=DIT_STREAM_HEAD_MAJOR, width=96 * 16, heads=32) == DIT_ERR_SHAPE  # 3 vectors per head
     assert f(kind=DIT_STREAM_HEAD_MAJOR, rows=(1 << 23), width=8192, heads=32) == DIT_ERR_ARG  # 2^24 workgroups
     assert f(kind=DIT_STREAM_SPLIT_ROWS, rows=(1 << 24) - 1, width=1 << 25) == DIT_ERR_ARG  # tile counter
     assert f(kind=DIT_STREAM_TWO_IN, rows=(1 << 24) - 1, width=1 << 25) == DIT_ERR_ARG

@@ -60,7 +60,8 @@ def test_row_group_copies(rows, row_bytes):
     assert torch.equal(ox, x) and torch.equal(oy, y)
 
 
-@pytest.mark.parametrize("rows,heads,head_bytes", [(5, 32, 256), (17, 4, 128), (3, 3, 16), (2, 48, 256)])
+@pytest.mark.parametrize("rows,heads,head_bytes", [(5, 32, 256), (17, 4, 128), (3, 3, 16), (2, 48, 256), (7, 3, 512),
+                                                   (130, 32, 256), (1, 1, 16)])
 def test_head_major_copy(rows, heads, head_bytes):
     row_bytes = heads * head_bytes
     x = words(rows, row_bytes, 6)

@@ -501,7 +501,7 @@ dit_status dit_stream_pattern(int32_t kind, const void *in0, const void *in1, vo
             return DIT_ERR_SHAPE;
     }
     if (kind == DIT_STREAM_HEAD_MAJOR) {
-        if (heads < 1 || (row_bytes / 16) % heads != 0)
+        if (heads < 1 || (row_bytes / 16) % heads != 0 || 256 % ((row_bytes / 16) / heads) != 0)
             return DIT_ERR_SHAPE;
         if (rows * ((row_bytes / 16 + 255) / 256) > kMaxRows)
             return DIT_ERR_ARG;

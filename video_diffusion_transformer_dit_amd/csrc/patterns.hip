@@ -23,8 +23,11 @@
 //                  mapping, the first output stored before the second: the
 //                  fused residual -> AdaLN's traffic
 //   HEAD_MAJOR     [rows][heads][W/heads] -> [heads][rows][W/heads]: a
-//                  token-major to head-major copy, one vector per thread,
-//                  grid (row, 4 KiB part) as the token-major QK kernel
+//                  token-major to head-major copy in the head-major QK
+//                  kernel's shape: grid (group of 4 tokens, 4 KiB part),
+//                  each thread one column of the 4 tokens, staged in LDS so
+//                  that each store instruction writes runs of one head's 4
+//                  tokens
 //   SCORE_TILES    the SubBlock block-score kernel's traffic at head dim 128:
 //                  its persistent 512-thread workgroups (one per CU), its
 //                  order of (plane, query tile, key tile) items, the query
@@ -154,16 +157,40 @@ __global__ __launch_bounds__(kGroupMaxThreads) void pattern_row_group_kernel(con
     }
 }
 
-// VPH = vectors per head, H heads, C = H * VPH vectors per row; grid (rows, parts).
+// VPH = vectors per head (a divisor of 256, so no head straddles two parts),
+// C vectors per row; grid (ceil(rows / kHmTokens), parts).  Loads and stores
+// of qk_rmsnorm_rope3d_head_major_kernel without its arithmetic.
+constexpr int kHmTokens = 4;
 __global__ __launch_bounds__(256) void pattern_head_major_kernel(const u32x4 *__restrict__ in, u32x4 *__restrict__ out,
-                                                                 int rows, int H, int VPH)
+                                                                 int rows, int C, int VPH)
 {
-    const int C = H * VPH;
-    const int c = blockIdx.y * 256 + threadIdx.x;
-    const unsigned row = blockIdx.x;
-    if (c < C) {
-        const int h = c / VPH, s = c - h * VPH;
-        store_stream(out + ((size_t)h * rows + row) * VPH + s, load_stream(in + (size_t)row * C + c));
+    __shared__ u32x4 stage[kHmTokens][256];
+    const int tid = threadIdx.x;
+    const unsigned r0 = blockIdx.x * kHmTokens;
+    const int c = blockIdx.y * 256 + tid;
+    const bool col_ok = c < C;
+    // absent tokens and columns read the group's first row or column and are never stored
+    u32x4 raw[kHmTokens];
+#pragma unroll
+    for (int t = 0; t < kHmTokens; ++t) {
+        const bool ok = col_ok && r0 + t < (unsigned)rows;
+        raw[t] = load_stream(in + (size_t)(ok ? r0 + t : r0) * C + (col_ok ? c : 0));
+    }
+#pragma unroll
+    for (int t = 0; t < kHmTokens; ++t)
+        stage[t][tid] = raw[t];
+    __syncthreads();
+    // vector m of a head's run of kHmTokens * VPH is token m / VPH, slot m % VPH
+    const int run = kHmTokens * VPH;
+#pragma unroll
+    for (int i = 0; i < kHmTokens; ++i) {
+        const int idx = tid + 256 * i;
+        const int hl = idx / run, m = idx % run;
+        const int t = m / VPH, s = m % VPH;
+        const int col = blockIdx.y * 256 + hl * VPH + s;
+        const unsigned r = r0 + t;
+        if (col < C && r < (unsigned)rows)
+            store_stream(out + ((size_t)(col / VPH) * (unsigned)rows + r) * VPH + s, stage[t][hl * VPH + s]);
     }
 }
 
@@ -329,9 +356,10 @@ hipError_t launch_stream_pattern(int kind, const void *in0, const void *in1, voi
     case kPatternRowGroup: return launch_row_group<false>(a, a, o, o, (int)rows, (int)C, stream);
     case kPatternRowGroup2x2: return launch_row_group<true>(a, b, o, o2, (int)rows, (int)C, stream);
     case kPatternHeadMajor: {
-        const int H = (int)heads, VPH = (int)(C / heads);
-        hipLaunchKernelGGL(pattern_head_major_kernel, dim3((unsigned)rows, (unsigned)((C + 255) / 256)), dim3(256), 0,
-                           stream, a, o, (int)rows, H, VPH);
+        const int VPH = (int)(C / heads);
+        hipLaunchKernelGGL(pattern_head_major_kernel,
+                           dim3((unsigned)((rows + kHmTokens - 1) / kHmTokens), (unsigned)((C + 255) / 256)), dim3(256),
+                           0, stream, a, o, (int)rows, (int)C, VPH);
         break;
     }
     case kPatternScoreTiles: {
