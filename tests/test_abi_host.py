@@ -54,6 +54,39 @@ def test_header_and_binding_agree():
     assert names == set(dit.SIGNATURES), names ^ set(dit.SIGNATURES)
 
 
+def declared_signatures():
+    """name -> (parameter ctypes, result ctypes) parsed from the header's declarations."""
+    with open(HEADER, encoding="utf-8") as fh:
+        text = re.sub(r"/\*.*?\*/", " ", fh.read(), flags=re.S)
+
+    def ctype(decl):
+        decl = decl.strip()
+        if "*" in decl:
+            return ctypes.c_char_p if re.match(r"const\s+char\s*\*", decl) else ctypes.c_void_p
+        base = decl.split()[0] if decl.split()[0] != "const" else decl.split()[1]
+        return {"int64_t": ctypes.c_int64, "int32_t": ctypes.c_int32, "int": ctypes.c_int, "float": ctypes.c_float,
+                "double": ctypes.c_double, "dit_status": ctypes.c_int}[base]
+
+    out = {}
+    for m in re.finditer(r"^\s*((?:const\s+)?\w+\s*\*?)\s*(dit_\w+)\s*\(([^;]*?)\)\s*;", text, flags=re.M):
+        ret, name, params = m.groups()
+        params = params.strip()
+        args = [] if params in ("", "void") else [ctype(p) for p in params.split(",")]
+        out[name] = (args, ctype(ret))
+    return out
+
+
+def test_binding_signatures_match_header():
+    # a parameter added to, dropped from or retyped in a declaration without
+    # the same change in the ctypes table would pass wrong arguments silently
+    decl = declared_signatures()
+    assert set(decl) == set(dit.SIGNATURES)
+    for name, (args, res) in dit.SIGNATURES.items():
+        want_args, want_res = decl[name]
+        assert [a.__name__ for a in args] == [a.__name__ for a in want_args], name
+        assert res.__name__ == want_res.__name__, name
+
+
 def test_library_exports_every_declared_symbol(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name
