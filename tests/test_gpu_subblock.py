@@ -206,6 +206,65 @@ def test_route_crowded_first_digit_bit_exact(nb, first_rare):
         assert np.array_equal(to_host(kf), oracle.subblock_topk(s_ref, keep)), f"fused, sparsity {sparsity}"
 
 
+@pytest.mark.parametrize("nb", [5, 300, 1953, 2100])
+@pytest.mark.parametrize("sign,centre", [(1.0, 16.0), (1.0, 16.5), (-1.0, 16.0), (-1.0, 16.5)])
+def test_route_narrow_range_bit_exact(nb, sign, centre):
+    # Every score of a row within half a unit of +-16 or +-16.5: one sign and
+    # one or two binary magnitudes, so the keys agree in most of their top
+    # bits and the selection's first digit must come from the bits below the
+    # ones they share.  On a 1/64 grid, exact in bf16 means and fp32 sums; the
+    # lists must equal the oracle's bit for bit.
+    B, H, Dh = 1, 2, 16
+    rng = np.random.default_rng(3000 + nb + int(4 * centre) + (sign < 0))
+    qp = np.zeros((B, H, nb, Dh))
+    qp[..., 0] = sign
+    qp[..., 1] = rng.integers(-4, 5, size=(B, H, nb)) / 8.0
+    kp = np.zeros((B, H, nb, Dh))
+    kp[..., 0] = centre
+    kp[..., 1] = rng.integers(-8, 9, size=(B, H, nb)) / 8.0
+    kp[..., 2:] = rng.integers(-8, 9, size=(B, H, nb, Dh - 2)) / 8.0  # multiplied by the zero q means
+    s_ref = oracle.subblock_scores(qp, kp)
+    assert np.all(np.abs(np.abs(s_ref) - centre) <= 0.5)
+    qd = torch.from_numpy(qp).float().to(DEV)
+    kd = torch.from_numpy(kp).float().to(DEV)
+    for sparsity in (0.0, 0.5, 0.75, 0.95):
+        keep = oracle.subblock_keep(nb, sparsity)
+        kept, scores = dit.dit_subblock_route(qd, kd, sparsity=sparsity)
+        torch.cuda.synchronize()
+        assert np.array_equal(to_host(scores)[..., :nb].astype(np.float64), s_ref)
+        assert np.array_equal(to_host(kept), oracle.subblock_topk(s_ref, keep)), sparsity
+        kf = fused_kept(qd, kd, sparsity=sparsity)
+        torch.cuda.synchronize()
+        assert np.array_equal(to_host(kf), oracle.subblock_topk(s_ref, keep)), f"fused, sparsity {sparsity}"
+
+
+@pytest.mark.parametrize("nb", [1953, 4096])
+def test_route_shared_component_valid(nb):
+    # Block means with a component shared by every block of a head (as when
+    # a head's queries and keys share a mean direction): the scores crowd
+    # into a narrow band of one sign.  Lists must be valid top-keep sets of
+    # the oracle's scores, and both routes must agree bit for bit.
+    B, H, Dh = 1, 2, 64
+    g = torch.Generator().manual_seed(nb)
+    base = torch.randn((B, H, 1, Dh), generator=g)
+    qp = base + 0.125 * torch.randn((B, H, nb, Dh), generator=g)
+    kp = base + 0.125 * torch.randn((B, H, nb, Dh), generator=g)
+    s_ref = oracle.subblock_scores(qp.double().numpy(), kp.double().numpy())
+    e = score_bound(qp.double().numpy(), kp.double().numpy())
+    qd, kd = qp.to(DEV), kp.to(DEV)
+    for sparsity in (0.75, 0.95):
+        kept, scores = dit.dit_subblock_route(qd, kd, sparsity=sparsity)
+        torch.cuda.synchronize()
+        keep = kept.shape[-1]
+        kh = to_host(kept)
+        check_kept_lists(kh, nb, keep)
+        check_valid_against_oracle(kh, s_ref, e)
+        check_top_set_of_own_scores(kh, to_host(scores)[..., :nb].astype(np.float64))
+        kf = fused_kept(qd, kd, sparsity=sparsity)
+        torch.cuda.synchronize()
+        assert torch.equal(kf, kept), f"sparsity {sparsity}: fused route differs from scores + top-k"
+
+
 def test_route_special_values():
     # all-zero means: every score is +0 or -0, all tie, the lowest indices are kept
     B, H, nb, Dh = 1, 1, 9, 16

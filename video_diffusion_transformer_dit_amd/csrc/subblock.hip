@@ -471,11 +471,38 @@ constexpr int kMaxSurvivors = 512;
 constexpr int kSelectWords = kTopBins; // LDS words one selecting wave uses (survivors overlay the histogram)
 static_assert(256 + kMaxSurvivors <= kTopBins, "survivors sit past the 256 bins the later digits use");
 
-// Picks the first digit from its 1024-bin histogram: the largest digit whose
-// keys, with those of all larger digits, reach `need`.  Lane l sums bins
-// 16 l .. 16 l + 15; a suffix sum over the lanes finds the lane holding the
-// digit, then sixteen lanes take one bin each of that lane's range.
-__device__ __forceinline__ void choose_top_digit(const uint32_t *hist, int lane, RadixState &st)
+// Least and greatest x over the wave: four row shifts leave each row's
+// extreme in its lane 15 (a lane whose source lies outside its row keeps its
+// own value), and the four rows' extremes are combined from those lanes.
+__device__ __forceinline__ uint32_t wave_min(uint32_t x)
+{
+    x = min(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x111, 0xf, 0xf, false)); // row_shr:1
+    x = min(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x112, 0xf, 0xf, false)); // row_shr:2
+    x = min(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x114, 0xf, 0xf, false)); // row_shr:4
+    x = min(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x118, 0xf, 0xf, false)); // row_shr:8
+    const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)x, 15), b = (uint32_t)__builtin_amdgcn_readlane((int)x, 31);
+    const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)x, 47), d = (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
+    return min(min(a, b), min(c, d));
+}
+
+__device__ __forceinline__ uint32_t wave_max(uint32_t x)
+{
+    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x111, 0xf, 0xf, false));
+    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x112, 0xf, 0xf, false));
+    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x114, 0xf, 0xf, false));
+    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x118, 0xf, 0xf, false));
+    const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)x, 15), b = (uint32_t)__builtin_amdgcn_readlane((int)x, 31);
+    const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)x, 47), d = (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
+    return max(max(a, b), max(c, d));
+}
+
+// Picks the first digit, bits shift .. shift + 9 of the keys (all keys share
+// `high`, their bits above those), from its 1024-bin histogram: the largest
+// digit whose keys, with those of all larger digits, reach `need`.  Lane l
+// sums bins 16 l .. 16 l + 15; a suffix sum over the lanes finds the lane
+// holding the digit, then sixteen lanes take one bin each of that lane's range.
+__device__ __forceinline__ void choose_top_digit(const uint32_t *hist, int lane, int shift, uint32_t high,
+                                                 RadixState &st)
 {
     const uint4 *h4 = reinterpret_cast<const uint4 *>(hist) + 4 * lane;
     const uint4 a = h4[0], b = h4[1], c = h4[2], d = h4[3];
@@ -489,8 +516,8 @@ __device__ __forceinline__ void choose_top_digit(const uint32_t *hist, int lane,
     h = lane < 16 ? h : 0u;
     const uint32_t greater = above_l + suffix_sum(h) - h; // keys of the larger digits
     const int D = __builtin_ctzll(__ballot(greater < st.need && st.need <= greater + h));
-    st.prefix = (uint32_t)(16 * L + D) << (32 - kTopBits);
-    st.mask = ~0u << (32 - kTopBits);
+    st.prefix = high | ((uint32_t)(16 * L + D) << shift);
+    st.mask = ~0u << shift;
     st.need -= (uint32_t)__builtin_amdgcn_readlane(greater, D);
     st.in_bin = (uint32_t)__builtin_amdgcn_readlane(h, D);
 }
@@ -554,8 +581,11 @@ __device__ __forceinline__ int fresh_uniform(int x)
 // words 256 .. 256 + kMaxSurvivors - 1 take the survivors and words 0 .. 255
 // the 256-bin histograms of the later digits.
 // A radix select finds the keep-th largest key T, most significant digit
-// first: a histogram of the top ten bits (LDS atomics, one per key) fixes the
-// first digit, the keys sharing it are compacted into LDS (each slot's
+// first.  The bits above the highest one in which the least and the greatest
+// key differ are the same in every key, so the first digit is the ten bits
+// just below them: keys crowded into a narrow range (scores of one sign and
+// magnitude) still spread over the 1024 bins.  A histogram of that digit
+// (LDS atomics, one per key) fixes it, the keys sharing it are compacted into LDS (each slot's
 // matching lanes found by one ballot), and 8-bit digits over those few fix
 // the rest -- stopping as soon as every key left in the bin is kept, so that
 // keys >= the prefix are exactly the kept ones.  Only when T splits a run of
@@ -575,18 +605,36 @@ __device__ __forceinline__ void select_keep(const uint32_t (&key)[S], int nb, in
     for (int i = 0; i < kTopBins / (4 * kWave); ++i)
         reinterpret_cast<uint4 *>(hist)[lane + kWave * i] = make_uint4(0u, 0u, 0u, 0u);
     wave_sync();
+    // The keys' range; key 0 (slots past the last block) wraps to the top
+    // under key - 1 and so is left out of the least.
+    uint32_t lo = ~0u, hi = 0u;
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+        lo = min(lo, key[s] - 1u);
+        hi = max(hi, key[s]);
+    }
+    lo = wave_min(lo) + 1u;
+    hi = wave_max(hi);
+    const uint32_t diff = lo ^ hi;
+    const int varying = diff ? 32 - __builtin_clz(diff) : 0; // low bits in which the keys differ
+    const int shift0 = varying > kTopBits ? varying - kTopBits : 0;
+    const uint32_t high = shift0 + kTopBits >= 32 ? 0u : lo & (~0u << (shift0 + kTopBits));
+
     int n = fresh_uniform(nb);
     uint32_t one; // held in a register (the compiler would set it again before every atomic)
     asm volatile("v_mov_b32 %0, 1" : "=v"(one));
 #pragma unroll
-    for (int s = 0; s < S; ++s)
-        if (s < kWhole || kWave * s < n) // wave-uniform
-            atomicAdd(&hist[key[s] >> (32 - kTopBits)], one);
+    for (int s = 0; s < S; ++s) {
+        if (s < kWhole) // every lane holds a block's key
+            atomicAdd(&hist[(key[s] >> shift0) & (kTopBins - 1)], one);
+        else if (kWave * s < n && key[s] != 0u) // wave-uniform slot test; lanes past the last block left out
+            atomicAdd(&hist[(key[s] >> shift0) & (kTopBins - 1)], one);
+    }
     wave_sync();
-    choose_top_digit(hist, lane, st);
+    choose_top_digit(hist, lane, shift0, high, st);
     wave_sync();
 
-    if (st.need < st.in_bin) {
+    if (st.need < st.in_bin && shift0 > 0) {
         // the bin holds keys that are not kept: resolve the remaining bits
         const bool compact = st.in_bin <= (uint32_t)kMaxSurvivors; // wave-uniform
         uint32_t n_surv = 0u;
@@ -611,7 +659,7 @@ __device__ __forceinline__ void select_keep(const uint32_t (&key)[S], int nb, in
             wave_sync();
         }
 #pragma unroll 1
-        for (int shift = 32 - kTopBits - 8; st.need < st.in_bin; shift = shift > 8 ? shift - 8 : 0) {
+        for (int shift = shift0 > 8 ? shift0 - 8 : 0; st.need < st.in_bin; shift = shift > 8 ? shift - 8 : 0) {
             reinterpret_cast<uint4 *>(hist)[lane] = make_uint4(0u, 0u, 0u, 0u);
             wave_sync();
             if (compact) {
