@@ -238,6 +238,36 @@ def test_route_narrow_range_bit_exact(nb, sign, centre):
         assert np.array_equal(to_host(kf), oracle.subblock_topk(s_ref, keep)), f"fused, sparsity {sparsity}"
 
 
+@pytest.mark.parametrize("nb", [5, 700, 1953, 2100])
+@pytest.mark.parametrize("levels", [1, 2, 8, "one_apart"])
+def test_route_few_distinct_scores_bit_exact(nb, levels):
+    # Rows whose scores take one, two or eight values (or all one value but
+    # for a single larger one): the selection ends on candidates that are all
+    # equal, so the tie rule (lowest index first) decides.  Exact scores; the
+    # lists must equal the oracle's bit for bit.
+    B, H, Dh = 1, 2, 16
+    rng = np.random.default_rng(4000 + nb + (9 if levels == "one_apart" else levels))
+    qp = np.ones((B, H, nb, Dh))
+    kp = np.zeros((B, H, nb, Dh))
+    if levels == "one_apart":
+        kp[..., 0] = 0.5
+        kp[:, :, rng.integers(0, nb), 0] = 0.625
+    else:
+        kp[..., 0] = rng.integers(0, levels, size=(B, H, nb)) / 8.0
+    s_ref = oracle.subblock_scores(qp, kp)
+    qd = torch.from_numpy(qp).float().to(DEV)
+    kd = torch.from_numpy(kp).float().to(DEV)
+    for sparsity in (0.0, 0.5, 0.75, 0.95):
+        keep = oracle.subblock_keep(nb, sparsity)
+        kept, scores = dit.dit_subblock_route(qd, kd, sparsity=sparsity)
+        torch.cuda.synchronize()
+        assert np.array_equal(to_host(scores)[..., :nb].astype(np.float64), s_ref)
+        assert np.array_equal(to_host(kept), oracle.subblock_topk(s_ref, keep)), sparsity
+        kf = fused_kept(qd, kd, sparsity=sparsity)
+        torch.cuda.synchronize()
+        assert np.array_equal(to_host(kf), oracle.subblock_topk(s_ref, keep)), f"fused, sparsity {sparsity}"
+
+
 @pytest.mark.parametrize("nb", [1953, 4096])
 def test_route_shared_component_valid(nb):
     # Block means with a component shared by every block of a head (as when

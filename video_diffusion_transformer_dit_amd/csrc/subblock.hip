@@ -587,8 +587,10 @@ __device__ __forceinline__ int fresh_uniform(int x)
 // magnitude) still spread over the 1024 bins.  A histogram of that digit
 // (LDS atomics, one per key) fixes it, the keys sharing it are compacted into LDS (each slot's
 // matching lanes found by one ballot), and 8-bit digits over those few fix
-// the rest -- stopping as soon as every key left in the bin is kept, so that
-// keys >= the prefix are exactly the kept ones.  Only when T splits a run of
+// the rest, each again taken just below the bits the remaining candidates
+// share -- stopping as soon as every key left in the bin is kept (keys >=
+// the prefix are then exactly the kept ones) or the candidates are all equal.
+// A row whose keys are all equal skips the digits.  Only when T splits a run of
 // equal keys do ties need ranks (lowest index first).  Kept blocks are
 // written slot by slot: a ballot of the slot's kept lanes gives each lane its
 // place, so the list comes out ascending with no sort.
@@ -620,66 +622,98 @@ __device__ __forceinline__ void select_keep(const uint32_t (&key)[S], int nb, in
     const int shift0 = varying > kTopBits ? varying - kTopBits : 0;
     const uint32_t high = shift0 + kTopBits >= 32 ? 0u : lo & (~0u << (shift0 + kTopBits));
 
-    int n = fresh_uniform(nb);
-    uint32_t one; // held in a register (the compiler would set it again before every atomic)
-    asm volatile("v_mov_b32 %0, 1" : "=v"(one));
+    int n;
+    if (lo == hi) { // wave-uniform: every key of the row is the same, all are ties
+        st.prefix = lo, st.mask = ~0u, st.in_bin = (uint32_t)nb;
+    } else {
+        n = fresh_uniform(nb);
+        uint32_t one; // held in a register (the compiler would set it again before every atomic)
+        asm volatile("v_mov_b32 %0, 1" : "=v"(one));
 #pragma unroll
-    for (int s = 0; s < S; ++s) {
-        if (s < kWhole) // every lane holds a block's key
-            atomicAdd(&hist[(key[s] >> shift0) & (kTopBins - 1)], one);
-        else if (kWave * s < n && key[s] != 0u) // wave-uniform slot test; lanes past the last block left out
-            atomicAdd(&hist[(key[s] >> shift0) & (kTopBins - 1)], one);
-    }
-    wave_sync();
-    choose_top_digit(hist, lane, shift0, high, st);
-    wave_sync();
-
-    if (st.need < st.in_bin && shift0 > 0) {
-        // the bin holds keys that are not kept: resolve the remaining bits
-        const bool compact = st.in_bin <= (uint32_t)kMaxSurvivors; // wave-uniform
-        uint32_t n_surv = 0u;
-        if (compact) {
-            n = fresh_uniform(nb);
-            char *surv_bytes = reinterpret_cast<char *>(survivors);
-#pragma unroll
-            for (int s = 0; s < S; ++s)
-                if (s < kWhole || kWave * s < n) {
-                    const bool m = (key[s] & st.mask) == st.prefix;
-                    const uint64_t mm = __ballot(m);
-                    if (mm) { // wave-uniform
-                        // exactly in_bin keys match, so every place is below the bound (the
-                        // mask only keeps the address inside the list whatever happens)
-                        if (m)
-                            *reinterpret_cast<uint32_t *>(
-                                surv_bytes + ((((uint32_t)lanes_below(mm) << 2) + (n_surv << 2)) &
-                                              (uint32_t)(4 * kMaxSurvivors - 1))) = key[s];
-                        n_surv += (uint32_t)__builtin_popcountll(mm);
-                    }
-                }
-            wave_sync();
+        for (int s = 0; s < S; ++s) {
+            if (s < kWhole) // every lane holds a block's key
+                atomicAdd(&hist[(key[s] >> shift0) & (kTopBins - 1)], one);
+            else if (kWave * s < n && key[s] != 0u) // wave-uniform slot test; lanes past the last block left out
+                atomicAdd(&hist[(key[s] >> shift0) & (kTopBins - 1)], one);
         }
-#pragma unroll 1
-        for (int shift = shift0 > 8 ? shift0 - 8 : 0; st.need < st.in_bin; shift = shift > 8 ? shift - 8 : 0) {
-            reinterpret_cast<uint4 *>(hist)[lane] = make_uint4(0u, 0u, 0u, 0u);
-            wave_sync();
+        wave_sync();
+        choose_top_digit(hist, lane, shift0, high, st);
+        wave_sync();
+
+        if (st.need < st.in_bin && shift0 > 0) {
+            // the bin holds keys that are not kept: resolve the remaining bits
+            const bool compact = st.in_bin <= (uint32_t)kMaxSurvivors; // wave-uniform
+            uint32_t n_surv = 0u;
             if (compact) {
-                for (uint32_t c = lane; c < n_surv; c += kWave) {
-                    const uint32_t k = survivors[c];
-                    if ((k & st.mask) == st.prefix)
-                        atomicAdd(&hist[(k >> shift) & 0xffu], 1u);
-                }
-            } else {
                 n = fresh_uniform(nb);
+                char *surv_bytes = reinterpret_cast<char *>(survivors);
 #pragma unroll
                 for (int s = 0; s < S; ++s)
-                    if ((s < kWhole || kWave * s < n) && (key[s] & st.mask) == st.prefix)
-                        atomicAdd(&hist[(key[s] >> shift) & 0xffu], 1u);
+                    if (s < kWhole || kWave * s < n) {
+                        const bool m = (key[s] & st.mask) == st.prefix;
+                        const uint64_t mm = __ballot(m);
+                        if (mm) { // wave-uniform
+                            // exactly in_bin keys match, so every place is below the bound (the
+                            // mask only keeps the address inside the list whatever happens)
+                            if (m)
+                                *reinterpret_cast<uint32_t *>(
+                                    surv_bytes + ((((uint32_t)lanes_below(mm) << 2) + (n_surv << 2)) &
+                                                  (uint32_t)(4 * kMaxSurvivors - 1))) = key[s];
+                            n_surv += (uint32_t)__builtin_popcountll(mm);
+                        }
+                    }
+                wave_sync();
             }
-            wave_sync();
-            choose_digit(hist, lane, shift, st);
-            wave_sync();
-            if (shift == 0)
-                break; // every bit fixed: st.prefix is the keep-th largest key
+#pragma unroll 1
+            for (;;) {
+                // The candidates' range (keys under the prefix): bits they all
+                // share are fixed at once, and the next 8-bit digit is the one
+                // just below them; equal candidates end the search (ties).
+                uint32_t clo = ~0u, chi = 0u;
+                if (compact) {
+                    for (uint32_t c = lane; c < n_surv; c += kWave) {
+                        const uint32_t k = survivors[c];
+                        if ((k & st.mask) == st.prefix)
+                            clo = min(clo, k), chi = max(chi, k);
+                    }
+                } else {
+                    n = fresh_uniform(nb);
+#pragma unroll
+                    for (int s = 0; s < S; ++s)
+                        if ((s < kWhole || kWave * s < n) && (key[s] & st.mask) == st.prefix)
+                            clo = min(clo, key[s]), chi = max(chi, key[s]);
+                }
+                clo = wave_min(clo);
+                chi = wave_max(chi);
+                if (clo == chi) {
+                    st.prefix = clo, st.mask = ~0u;
+                    break; // every candidate is the keep-th largest key
+                }
+                const int vary = 32 - __builtin_clz(clo ^ chi); // below the bits already fixed
+                const int shift = vary > 8 ? vary - 8 : 0;
+                st.prefix = clo & (~0u << vary);
+                st.mask = ~0u << vary;
+                reinterpret_cast<uint4 *>(hist)[lane] = make_uint4(0u, 0u, 0u, 0u);
+                wave_sync();
+                if (compact) {
+                    for (uint32_t c = lane; c < n_surv; c += kWave) {
+                        const uint32_t k = survivors[c];
+                        if ((k & st.mask) == st.prefix)
+                            atomicAdd(&hist[(k >> shift) & 0xffu], 1u);
+                    }
+                } else {
+                    n = fresh_uniform(nb);
+#pragma unroll
+                    for (int s = 0; s < S; ++s)
+                        if ((s < kWhole || kWave * s < n) && (key[s] & st.mask) == st.prefix)
+                            atomicAdd(&hist[(key[s] >> shift) & 0xffu], 1u);
+                }
+                wave_sync();
+                choose_digit(hist, lane, shift, st);
+                wave_sync();
+                if (shift == 0 || st.need == st.in_bin)
+                    break; // every bit fixed, or every key left in the bin is kept
+            }
         }
     }
 
