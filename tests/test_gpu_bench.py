@@ -43,3 +43,7 @@ def test_bench_tiny_reports_every_field():
     assert base["kind"] == "oracle" and base["cores"] >= 1 and base["value"] > 0 and base["sample"]
     assert out["parity_checked"] is True and out["parity_ok"] is True
     assert base["parity_max_err_over_bound"] <= 1.0
+    route = out["next_subblock_routing"]
+    shared = route["shared_component"]
+    assert shared["fused_equals_two_kernel"] is True and shared["route_ms"] > 0 and shared["route_fused_ms"] > 0
+    assert out["next_consistency"]["fused_route_equals_scores_then_topk"] is True

@@ -465,7 +465,7 @@ struct RadixState {
     uint32_t prefix, mask, need, in_bin;
 };
 
-constexpr int kTopBits = 10;                   // the first digit: a key's top ten bits
+constexpr int kTopBits = 10;                   // the first digit: ten bits, just below those all of a row's keys share
 constexpr int kTopBins = 1 << kTopBits;
 constexpr int kMaxSurvivors = 512;
 constexpr int kSelectWords = kTopBins; // LDS words one selecting wave uses (survivors overlay the histogram)
